@@ -1,0 +1,579 @@
+/*
+ * moe_oracle.c -- plain CPU reference for the DeepSeekMoE layer forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library.  The GPU library never
+ * links, loads or calls it, and the two share no source, header or table.
+ *
+ * Sources (DeepSeek-V3 Technical Report, as rewritten on the "papers-reader"
+ * page "DeepSeek-V3 Technical Report"):
+ *   - §2.1.2 DeepSeekMoE: output = shared experts applied to every token plus
+ *     the gate-weighted sum of the K_r selected routed experts; affinities are
+ *     sigmoid(u_t . e_i) and the gating values are the selected affinities
+ *     normalised among the selected experts.
+ *   - §2.1.2 auxiliary-loss-free balancing: a per-expert bias b_i is added to
+ *     the affinity for the top-K choice only; the gate uses the un-biased
+ *     affinity; after each step b_i moves by gamma against the expert's
+ *     whole-batch load; node-limited routing keeps each token on at most M
+ *     groups of experts; no token is dropped.
+ *   - §3.3 FP8 training: activations grouped in 1 x N_c tiles and weights in
+ *     N_c x N_c blocks (N_c = 128), each group with its own scale; partial
+ *     sums promoted to fp32 every N_c products.
+ *   - §4.2 hyper-parameters: d = 7168, 1 shared + 256 routed experts, expert
+ *     intermediate size 2048, 8 routed experts per token, at most 4 nodes,
+ *     gamma = 0.001.
+ *
+ * The garbled pages drop the display equations, so several steps are readings
+ * of the surrounding prose; each is marked "reading:" where it is used.
+ *
+ * Arithmetic policy: every dot product is a sequential sum in double precision
+ * (fp64) over the values the inputs decode to; every stored intermediate is
+ * rounded exactly once into its storage format (fp32, bf16 or e4m3+scale).
+ * Loops are parallel over independent outputs only; no sum is reordered.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <float.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_E4M3 = 2 };
+enum { OR_ADD_RESIDUAL = 1u };
+
+#define OR_NC 128          /* quantisation group size N_c (§3.3) */
+#define OR_E4M3_MAX 448.0  /* largest finite OCP E4M3FN value    */
+
+/* ------------------------------------------------------------------------ */
+/* Storage formats                                                          */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Round a finite double to a binary floating-point format with p significand
+ * bits (implicit bit included) and minimum normal exponent emin, to nearest,
+ * ties to even.  Below 2^emin the spacing stays 2^(emin-p+1) (gradual
+ * underflow).  A result whose magnitude exceeds maxfin becomes +-inf, or
+ * +-maxfin when sat is set.  The division by the power-of-two spacing is exact.
+ */
+double oracle_round_format(double x, int p, int emin, double maxfin, int sat)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    int ex;
+    frexp(x, &ex);                 /* |x| in [2^(ex-1), 2^ex) */
+    int e = ex - 1;
+    if (e < emin) e = emin;
+    double ulp = ldexp(1.0, e - (p - 1));
+    double r = nearbyint(x / ulp) * ulp;   /* default mode: ties to even */
+    if (fabs(r) > maxfin) r = sat ? copysign(maxfin, x) : copysign(INFINITY, x);
+    return r;
+}
+
+static double bf16_max(void) { return ldexp(2.0 - ldexp(1.0, -7), 127); }
+
+/* bf16 = the upper half of an IEEE binary32: 8 significand bits, emin -126 */
+double oracle_round_bf16(double x) { return oracle_round_format(x, 8, -126, bf16_max(), 0); }
+
+uint16_t oracle_encode_bf16(double x)
+{
+    float f = (float)oracle_round_bf16(x);   /* exact: a bf16 value is a binary32 value */
+    uint32_t b;
+    memcpy(&b, &f, 4);
+    return (uint16_t)(b >> 16);
+}
+
+static inline double dec_bf16(uint16_t h)
+{
+    uint32_t b = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &b, 4);
+    return (double)f;
+}
+
+/* OCP E4M3FN: 1 sign, 4 exponent (bias 7), 3 mantissa bits, no infinities,
+ * S.1111.111 is NaN, largest finite 448, smallest subnormal 2^-9. */
+double oracle_decode_e4m3(uint8_t c)
+{
+    int s = c >> 7, E = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (E == 15 && m == 7) return NAN;
+    if (E == 0) v = ldexp((double)m, -9);                  /* m/8 * 2^-6 */
+    else v = ldexp(1.0 + m / 8.0, E - 7);
+    return s ? -v : v;
+}
+
+double oracle_round_e4m3(double x) { return oracle_round_format(x, 4, -6, OR_E4M3_MAX, 1); }
+
+uint8_t oracle_encode_e4m3(double x)
+{
+    double r = oracle_round_e4m3(x);
+    uint8_t s = (r < 0.0 || (r == 0.0 && signbit(r))) ? 0x80 : 0;
+    double a = fabs(r);
+    if (a == 0.0) return s;
+    if (a < ldexp(1.0, -6)) return s | (uint8_t)(a / ldexp(1.0, -9));   /* subnormal */
+    int ex;
+    frexp(a, &ex);
+    int e = ex - 1;                                                     /* a in [2^e, 2^(e+1)) */
+    int m = (int)((a / ldexp(1.0, e) - 1.0) * 8.0);
+    return s | (uint8_t)((e + 7) << 3) | (uint8_t)m;
+}
+
+static double e4m3_table[256];
+static int e4m3_table_ready = 0;
+static void init_tables(void)
+{
+    if (e4m3_table_ready) return;
+    for (int c = 0; c < 256; ++c) e4m3_table[c] = oracle_decode_e4m3((uint8_t)c);
+    e4m3_table_ready = 1;
+}
+
+/* Value of element i of a row stored in dtype (fp32, bf16).  */
+static inline double load_plain(int dtype, const void *p, int64_t i)
+{
+    if (dtype == OR_F32) return (double)((const float *)p)[i];
+    return dec_bf16(((const uint16_t *)p)[i]);
+}
+
+/* Store a double into dtype with one rounding. */
+static inline void store_plain(int dtype, void *p, int64_t i, double v)
+{
+    if (dtype == OR_F32) ((float *)p)[i] = (float)v;          /* C cast: IEEE nearest-even */
+    else ((uint16_t *)p)[i] = oracle_encode_bf16(v);
+}
+
+/*
+ * Quantiser Q for one group of n fp32 values (§3.3: one scale per 1 x N_c
+ * activation tile or N_c x N_c weight block).  reading: the scale is the
+ * group's absolute maximum divided by the largest finite E4M3FN value, as a
+ * plain fp32 quotient (1 for an all-zero group); each element is divided by
+ * the scale in fp32, clamped to +-448 and rounded to nearest-even E4M3FN.
+ */
+static float quant_scale(float amax) { return amax == 0.0f ? 1.0f : amax / 448.0f; }
+static uint8_t quant_one(float x, float scale)
+{
+    float q = x / scale;                    /* binary32 division */
+    if (q > 448.0f) q = 448.0f;
+    if (q < -448.0f) q = -448.0f;
+    return oracle_encode_e4m3((double)q);
+}
+
+/* 1 x N_c tiles along each row of x[rows][cols] (cols % 128 == 0).
+ * in_dtype is OR_F32 or OR_BF16; q[rows][cols], s[rows][cols/128]. */
+void oracle_quant_1x128(int64_t rows, int cols, int in_dtype, const void *x, uint8_t *q, float *s)
+{
+    init_tables();
+    int nb = cols / OR_NC;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int b = 0; b < nb; ++b) {
+            float amax = 0.0f;
+            for (int c = b * OR_NC; c < (b + 1) * OR_NC; ++c) {
+                float v = fabsf((float)load_plain(in_dtype, x, r * cols + c));
+                if (v > amax) amax = v;
+            }
+            float sc = quant_scale(amax);
+            s[r * nb + b] = sc;
+            for (int c = b * OR_NC; c < (b + 1) * OR_NC; ++c)
+                q[r * cols + c] = quant_one((float)load_plain(in_dtype, x, r * cols + c), sc);
+        }
+    }
+}
+
+/* N_c x N_c blocks over each of nmat matrices w[nmat][rows][cols]
+ * (rows, cols multiples of 128); s[nmat][rows/128][cols/128]. */
+void oracle_quant_128x128(int64_t nmat, int rows, int cols, int in_dtype, const void *w, uint8_t *q, float *s)
+{
+    init_tables();
+    int rb = rows / OR_NC, cb = cols / OR_NC;
+#pragma omp parallel for collapse(3) schedule(static)
+    for (int64_t m = 0; m < nmat; ++m)
+        for (int bi = 0; bi < rb; ++bi)
+            for (int bj = 0; bj < cb; ++bj) {
+                int64_t base = m * (int64_t)rows * cols;
+                float amax = 0.0f;
+                for (int i = bi * OR_NC; i < (bi + 1) * OR_NC; ++i)
+                    for (int j = bj * OR_NC; j < (bj + 1) * OR_NC; ++j) {
+                        float v = fabsf((float)load_plain(in_dtype, w, base + (int64_t)i * cols + j));
+                        if (v > amax) amax = v;
+                    }
+                float sc = quant_scale(amax);
+                s[(m * rb + bi) * cb + bj] = sc;
+                for (int i = bi * OR_NC; i < (bi + 1) * OR_NC; ++i)
+                    for (int j = bj * OR_NC; j < (bj + 1) * OR_NC; ++j) {
+                        int64_t k = base + (int64_t)i * cols + j;
+                        q[k] = quant_one((float)load_plain(in_dtype, w, k), sc);
+                    }
+            }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Routing (§2.1.2)                                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Selection and gating for one token from its fp32 affinities s[Nr].
+ * reading: groups are contiguous index ranges of Nr/G experts (experts are
+ * laid out node by node); a group's score is the sum of its two largest
+ * biased affinities (its single affinity when a group holds one expert); the
+ * Mg best groups are kept and the other experts masked to -inf; the K best
+ * biased affinities among the kept experts are chosen; every tie goes to the
+ * lower index; slots are ordered by decreasing biased affinity.  The gating
+ * value of slot j is s_j divided by the fp32 sum of the selected un-biased
+ * affinities, summed in slot order, times routed_scale. */
+static void select_token(int Nr, int G, int Mg, int K, const float *s, const float *bias,
+                         float routed_scale, int32_t *idx, float *w)
+{
+    float sb[1024];
+    float gsc[1024];
+    char gkeep[1024], taken[1024];
+    int gs = Nr / G;
+    for (int i = 0; i < Nr; ++i) sb[i] = s[i] + bias[i];          /* one fp32 add */
+
+    for (int g = 0; g < G; ++g) {
+        int a = -1;
+        for (int i = g * gs; i < (g + 1) * gs; ++i)
+            if (a < 0 || sb[i] > sb[a]) a = i;
+        if (gs == 1) { gsc[g] = sb[a]; continue; }
+        int b = -1;
+        for (int i = g * gs; i < (g + 1) * gs; ++i)
+            if (i != a && (b < 0 || sb[i] > sb[b])) b = i;
+        gsc[g] = sb[a] + sb[b];                                   /* one fp32 add */
+    }
+    memset(gkeep, 0, (size_t)G);
+    for (int r = 0; r < Mg; ++r) {
+        int best = -1;
+        for (int g = 0; g < G; ++g)
+            if (!gkeep[g] && (best < 0 || gsc[g] > gsc[best])) best = g;
+        gkeep[best] = 1;
+    }
+    for (int i = 0; i < Nr; ++i) {
+        if (!gkeep[i / gs]) sb[i] = -INFINITY;
+        taken[i] = 0;
+    }
+    for (int j = 0; j < K; ++j) {
+        int best = -1;
+        for (int i = 0; i < Nr; ++i)
+            if (!taken[i] && (best < 0 || sb[i] > sb[best])) best = i;
+        taken[best] = 1;
+        idx[j] = best;
+    }
+    float den = 0.0f;
+    for (int j = 0; j < K; ++j) den = den + s[idx[j]];
+    for (int j = 0; j < K; ++j) w[j] = (s[idx[j]] / den) * routed_scale;
+}
+
+/* Affinity of expert i for one token: sigmoid of the fp64 dot product of the
+ * token's FFN input with the expert's centroid, rounded once to fp32. */
+static float affinity(int d, int u_dtype, const void *u, int64_t t, int e_dtype, const void *e, int i)
+{
+    double z = 0.0;
+    for (int c = 0; c < d; ++c)
+        z += load_plain(u_dtype, u, t * d + c) * load_plain(e_dtype, e, (int64_t)i * d + c);
+    return (float)(1.0 / (1.0 + exp(-z)));
+}
+
+/*
+ * Route n_tok tokens (token ids tok[0..n_tok), or 0..n_tok-1 when tok is NULL).
+ * scores_in, when given, holds fp32 affinities [T_all][Nr] indexed by token id,
+ * and replaces the computed affinities.  scores_out[n_tok][Nr], topk_idx and
+ * topk_w[n_tok][K] are indexed by position in the token list.
+ */
+int oracle_route(int64_t n_tok, const int64_t *tok, int d, int Nr, int G, int Mg, int K,
+                 int u_dtype, const void *u, int e_dtype, const void *gate_w,
+                 const float *bias, const float *scores_in, float *scores_out,
+                 int32_t *topk_idx, float *topk_w, float routed_scale)
+{
+    if (Nr > 1024 || G < 1 || Nr % G || Mg < 1 || Mg > G || K < 1 || K > Mg * (Nr / G)) return -2;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t n = 0; n < n_tok; ++n) {
+        int64_t t = tok ? tok[n] : n;
+        float s[1024];
+        for (int i = 0; i < Nr; ++i)
+            s[i] = scores_in ? scores_in[t * Nr + i] : affinity(d, u_dtype, u, t, e_dtype, gate_w, i);
+        if (scores_out) memcpy(scores_out + n * Nr, s, sizeof(float) * (size_t)Nr);
+        select_token(Nr, G, Mg, K, s, bias, routed_scale, topk_idx + n * K, topk_w + n * K);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Dispatch bookkeeping                                                     */
+/* ------------------------------------------------------------------------ */
+
+/* counts[i] = number of (token, slot) pairs routed to expert i (whole-batch
+ * load, §2.1.2); offsets = exclusive prefix sum; rows offsets[i]..offsets[i+1)
+ * hold expert i's tokens in increasing token order; perm_token[row] = token;
+ * inv_perm[t*K + j] = the row of slot j of token t. */
+void oracle_permute(int64_t T, int K, int Nr, const int32_t *topk_idx,
+                    int32_t *counts, int32_t *offsets, int32_t *perm_token, int32_t *inv_perm)
+{
+    for (int i = 0; i < Nr; ++i) counts[i] = 0;
+    for (int64_t n = 0; n < T * K; ++n) counts[topk_idx[n]] += 1;
+    offsets[0] = 0;
+    for (int i = 0; i < Nr; ++i) offsets[i + 1] = offsets[i] + counts[i];
+    for (int i = 0; i < Nr; ++i) {
+        int32_t row = offsets[i];
+        for (int64_t t = 0; t < T; ++t)
+            for (int j = 0; j < K; ++j)
+                if (topk_idx[t * K + j] == i) {
+                    perm_token[row] = (int32_t)t;
+                    inv_perm[t * K + j] = row;
+                    ++row;
+                }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Expert FFN                                                               */
+/* ------------------------------------------------------------------------ */
+
+/* Decode row r of a [*, n] matrix into double.  For E4M3 the row's scales
+ * are the 1 x 128 tile scales sc[r][n/128] when blk_rows == 1, or the
+ * 128 x 128 block scales sc[r/128][n/128] when blk_rows == 128. */
+static void load_row(int dtype, const void *p, const float *sc, int blk_rows, int64_t r, int n, double *out)
+{
+    if (dtype == OR_E4M3) {
+        const uint8_t *q = (const uint8_t *)p + r * n;
+        const float *srow = sc + (r / blk_rows) * (n / OR_NC);
+        for (int c = 0; c < n; ++c) out[c] = e4m3_table[q[c]] * (double)srow[c / OR_NC];
+    } else {
+        for (int c = 0; c < n; ++c) out[c] = load_plain(dtype, p, r * n + c);
+    }
+}
+
+static double dot(const double *a, const double *b, int n)
+{
+    double z = 0.0;
+    for (int c = 0; c < n; ++c) z += a[c] * b[c];
+    return z;
+}
+
+/*
+ * One SwiGLU expert applied to one input row x[d] (already decoded):
+ *   h = SiLU(W_gate x) * (W_up x),  SiLU(a) = a * sigmoid(a)   (reading: the
+ *   expert form the pages leave implicit is SwiGLU without biases),
+ *   y = W_down h.
+ * w_dtype: storage of the weights [I][d] (gate, up) and [d][I] (down); for
+ * E4M3 with 128 x 128 block scales.  h is stored in h_dtype before the down
+ * projection: fp32, bf16, or (E4M3) quantised per 1 x 128 tile from its fp32
+ * value.  The returned y[d] is the exact fp64 result; the caller rounds it.
+ */
+static void expert_row(int d, int I, int w_dtype, const void *wg, const void *wu, const void *wd,
+                       const float *wg_s, const float *wu_s, const float *wd_s, int h_dtype,
+                       const double *x, double *y, double *wrow, double *h)
+{
+    for (int k = 0; k < I; ++k) {
+        load_row(w_dtype, wg, wg_s, OR_NC, k, d, wrow);
+        double a = dot(x, wrow, d);
+        load_row(w_dtype, wu, wu_s, OR_NC, k, d, wrow);
+        double b = dot(x, wrow, d);
+        double hv = a / (1.0 + exp(-a)) * b;
+        if (h_dtype == OR_F32) hv = (double)(float)hv;
+        else if (h_dtype == OR_BF16) hv = oracle_round_bf16(hv);
+        h[k] = hv;
+    }
+    if (h_dtype == OR_E4M3) {
+        for (int b = 0; b < I / OR_NC; ++b) {
+            float amax = 0.0f;
+            for (int k = b * OR_NC; k < (b + 1) * OR_NC; ++k) {
+                float v = fabsf((float)h[k]);
+                if (v > amax) amax = v;
+            }
+            float sc = quant_scale(amax);
+            for (int k = b * OR_NC; k < (b + 1) * OR_NC; ++k)
+                h[k] = e4m3_table[quant_one((float)h[k], sc)] * (double)sc;
+        }
+    }
+    for (int i = 0; i < d; ++i) {
+        load_row(w_dtype, wd, wd_s, OR_NC, i, I, wrow);
+        y[i] = dot(h, wrow, I);
+    }
+}
+
+static double round_to(int dtype, double v)
+{
+    return dtype == OR_F32 ? (double)(float)v : oracle_round_bf16(v);
+}
+
+/*
+ * Grouped FFN on selected rows: expert e owns rows offsets[e]..offsets[e+1)
+ * of x.  x is stored in x_dtype ([rows][d]; for E4M3 with 1 x 128 scales
+ * x_s[rows][d/128]); weights for all experts are concatenated
+ * ([n_exp][I][d] etc., E4M3 scales [n_exp][I/128][d/128] etc.).
+ * For each listed row r, y[n][d] = expert(r) applied to x[r], rounded once to
+ * y_dtype.
+ */
+int oracle_grouped_ffn(int n_exp, const int32_t *offsets, int64_t n_rows, const int64_t *rows,
+                       int d, int I, int x_dtype, const void *x, const float *x_s,
+                       int w_dtype, const void *wg, const void *wu, const void *wd,
+                       const float *wg_s, const float *wu_s, const float *wd_s,
+                       int h_dtype, int y_dtype, void *y)
+{
+    init_tables();
+    int esz = w_dtype == OR_F32 ? 4 : w_dtype == OR_BF16 ? 2 : 1;
+    int xsz = x_dtype == OR_F32 ? 4 : x_dtype == OR_BF16 ? 2 : 1;
+    int err = 0;
+#pragma omp parallel
+    {
+        double *xr = malloc(sizeof(double) * (size_t)d);
+        double *yr = malloc(sizeof(double) * (size_t)d);
+        double *wrow = malloc(sizeof(double) * (size_t)(d > I ? d : I));
+        double *h = malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t n = 0; n < n_rows; ++n) {
+            int64_t r = rows[n];
+            int e = -1;
+            for (int k = 0; k < n_exp; ++k)
+                if (r >= offsets[k] && r < offsets[k + 1]) e = k;
+            if (e < 0) { err = -1; continue; }
+            size_t wo = (size_t)e * I * d * esz;
+            size_t so = (size_t)e * (I / OR_NC) * (d / OR_NC);
+            load_row(x_dtype, (const char *)x, x_s, 1, r, d, xr);
+            (void)xsz;
+            expert_row(d, I, w_dtype, (const char *)wg + wo, (const char *)wu + wo, (const char *)wd + wo,
+                       w_dtype == OR_E4M3 ? wg_s + so : NULL, w_dtype == OR_E4M3 ? wu_s + so : NULL,
+                       w_dtype == OR_E4M3 ? wd_s + so : NULL, h_dtype, xr, yr, wrow, h);
+            for (int i = 0; i < d; ++i) store_plain(y_dtype, y, n * d + i, yr[i]);
+        }
+        free(xr); free(yr); free(wrow); free(h);
+    }
+    return err;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Combine (§2.1.2 output equation, stripped on the page; reading: the sum  */
+/* of the shared experts' outputs and the gate-weighted routed outputs,     */
+/* with the residual u_t added only when asked for)                         */
+/* ------------------------------------------------------------------------ */
+
+/* For listed tokens: out[n] = sum_j topk_w[t][j] * y_perm[inv_perm[t*K+j]]
+ *   + sum_s y_shared[s][t] (+ u[t]), in fp64, rounded once to y_dtype.
+ * y_perm, y_shared and out are stored in y_dtype; u in u_dtype. */
+void oracle_combine(int64_t n_tok, const int64_t *tok, int64_t T, int d, int K, int Ns, int y_dtype,
+                    const void *y_perm, const int32_t *inv_perm, const float *topk_w,
+                    const void *y_shared, int u_dtype, const void *u, void *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < n_tok; ++n) {
+        int64_t t = tok ? tok[n] : n;
+        for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < K; ++j)
+                acc += (double)topk_w[t * K + j] * load_plain(y_dtype, y_perm, (int64_t)inv_perm[t * K + j] * d + i);
+            for (int s = 0; s < Ns; ++s) acc += load_plain(y_dtype, y_shared, ((int64_t)s * T + t) * d + i);
+            if (u) acc += load_plain(u_dtype, u, t * d + i);
+            store_plain(y_dtype, out, n * d + i, acc);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Whole layer for a list of tokens                                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * out[n][d] for token tok[n]: route the token (own affinities, or scores_in),
+ * prepare its FFN input row (u itself, or for E4M3 weights its 1 x 128
+ * quantisation), apply its K experts and the Ns shared experts with the
+ * storage roundings of expert_row, round each expert output to out_dtype,
+ * then combine in fp64 and round once.
+ * Routed weights: [Nr][I][d], [Nr][I][d], [Nr][d][I]; shared: [Ns][...].
+ */
+int oracle_moe_forward(int64_t n_tok, const int64_t *tok, int d, int Nr, int Ns, int G, int Mg, int K, int I,
+                       int act_dtype, int w_dtype, int out_dtype, float routed_scale, unsigned flags,
+                       const void *u, const void *gate_w, const float *bias, const float *scores_in,
+                       const void *rwg, const void *rwu, const void *rwd,
+                       const float *rwg_s, const float *rwu_s, const float *rwd_s,
+                       const void *swg, const void *swu, const void *swd,
+                       const float *swg_s, const float *swu_s, const float *swd_s,
+                       void *out, int32_t *topk_idx, float *topk_w, float *scores_out)
+{
+    init_tables();
+    int rc = oracle_route(n_tok, tok, d, Nr, G, Mg, K, act_dtype, u, act_dtype, gate_w, bias, scores_in,
+                          scores_out, topk_idx, topk_w, routed_scale);
+    if (rc) return rc;
+    int h_dtype = w_dtype == OR_E4M3 ? OR_E4M3 : act_dtype;
+    int esz = w_dtype == OR_F32 ? 4 : w_dtype == OR_BF16 ? 2 : 1;
+    size_t wmat = (size_t)I * d;
+    size_t smat = (size_t)(I / OR_NC) * (d / OR_NC);
+    int nwork = K + Ns;
+    double *res = malloc(sizeof(double) * (size_t)n_tok * nwork * d);
+    if (!res) return -3;
+#pragma omp parallel
+    {
+        double *xr = malloc(sizeof(double) * (size_t)d);
+        double *wrow = malloc(sizeof(double) * (size_t)(d > I ? d : I));
+        double *h = malloc(sizeof(double) * (size_t)I);
+        uint8_t *xq = malloc((size_t)d);
+        float *xs = malloc(sizeof(float) * (size_t)(d / OR_NC + 1));
+#pragma omp for schedule(dynamic, 1) collapse(2)
+        for (int64_t n = 0; n < n_tok; ++n)
+            for (int j = 0; j < nwork; ++j) {
+                int64_t t = tok ? tok[n] : n;
+                if (w_dtype == OR_E4M3) {
+                    oracle_quant_1x128(1, d, act_dtype, (const char *)u + (size_t)t * d * (act_dtype == OR_F32 ? 4 : 2), xq, xs);
+                    load_row(OR_E4M3, xq, xs, 1, 0, d, xr);
+                } else {
+                    load_row(act_dtype, u, NULL, 1, t, d, xr);
+                }
+                const char *g, *up, *dn;
+                const float *gs = NULL, *us = NULL, *ds = NULL;
+                if (j < K) {
+                    int e = topk_idx[n * K + j];
+                    g = (const char *)rwg + (size_t)e * wmat * esz;
+                    up = (const char *)rwu + (size_t)e * wmat * esz;
+                    dn = (const char *)rwd + (size_t)e * wmat * esz;
+                    if (w_dtype == OR_E4M3) { gs = rwg_s + e * smat; us = rwu_s + e * smat; ds = rwd_s + e * smat; }
+                } else {
+                    int s = j - K;
+                    g = (const char *)swg + (size_t)s * wmat * esz;
+                    up = (const char *)swu + (size_t)s * wmat * esz;
+                    dn = (const char *)swd + (size_t)s * wmat * esz;
+                    if (w_dtype == OR_E4M3) { gs = swg_s + s * smat; us = swu_s + s * smat; ds = swd_s + s * smat; }
+                }
+                double *y = res + ((size_t)n * nwork + j) * d;
+                expert_row(d, I, w_dtype, g, up, dn, gs, us, ds, h_dtype, xr, y, wrow, h);
+                for (int i = 0; i < d; ++i) y[i] = round_to(out_dtype, y[i]);   /* expert output storage */
+            }
+        free(xr); free(wrow); free(h); free(xq); free(xs);
+    }
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < n_tok; ++n) {
+        int64_t t = tok ? tok[n] : n;
+        for (int i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int j = 0; j < K; ++j) acc += (double)topk_w[n * K + j] * res[((size_t)n * nwork + j) * d + i];
+            for (int s = 0; s < Ns; ++s) acc += res[((size_t)n * nwork + K + s) * d + i];
+            if (flags & OR_ADD_RESIDUAL) acc += load_plain(act_dtype, u, t * d + i);
+            store_plain(out_dtype, out, n * d + i, acc);
+        }
+    }
+    free(res);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Bias update (§2.1.2; rate gamma from §4.2)                               */
+/* ------------------------------------------------------------------------ */
+
+/* reading: an expert is overloaded when its load exceeds the mean load
+ * T*K/Nr (as fp32), underloaded when below; b_i moves by -gamma, +gamma, or
+ * not at all on an exact tie: b_i = fl32(b_i + gamma * sign(mean - load_i)). */
+void oracle_bias_update(int Nr, int64_t T, int K, const int32_t *counts, float *bias, float gamma)
+{
+    float mean = (float)((double)(float)(T * K) / (double)(float)Nr);
+    for (int i = 0; i < Nr; ++i) {
+        float load = (float)counts[i];
+        float sgn = load < mean ? 1.0f : (load > mean ? -1.0f : 0.0f);
+        bias[i] = bias[i] + gamma * sgn;
+    }
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
