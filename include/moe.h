@@ -1,0 +1,245 @@
+/*
+ * moe.h -- C ABI of libmoe, a DeepSeekMoE layer forward pass for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer is the one of the "DeepSeek-V3 Technical Report" (papers-reader
+ * rewrite of arXiv 2412.19437):
+ *   §2.1.2  DeepSeekMoE: for the FFN input u_t, the output is the sum of the
+ *           N_s shared experts applied to u_t and of the K_r selected routed
+ *           experts weighted by their gating values; affinities are
+ *           s_{i,t} = sigmoid(u_t . e_i) with e_i the centroid of routed
+ *           expert i; gating values are the selected affinities normalised
+ *           over the selected experts.
+ *   §2.1.2  auxiliary-loss-free balancing: a bias b_i is added to s_{i,t} for
+ *           the top-K choice only (the gating value uses the un-biased s);
+ *           after each step b_i moves by gamma against expert i's whole-batch
+ *           load; node-limited routing keeps a token on at most M groups;
+ *           no token is dropped.
+ *   §3.3    FP8: activations quantised in 1 x N_c tiles and weights in
+ *           N_c x N_c blocks (N_c = 128), each group with its own fp32 scale;
+ *           partial sums accumulated in fp32 every N_c products.
+ *   §4.2    shape: d = 7168, 1 shared + 256 routed experts, expert
+ *           intermediate size 2048, 8 routed experts per token, at most 4
+ *           nodes (groups) per token, gamma = 0.001.
+ *
+ * Conventions for every call
+ *   - Return 0 (MOE_OK) or a negative moe_status.  Argument checks run on the
+ *     host before any HIP call, so a rejected call touches no device state.
+ *     moe_last_error() gives a message for the calling thread's last failure.
+ *   - The moe_shape struct is host memory; every array argument is a device
+ *     pointer to row-major contiguous storage, owned by the caller.  The
+ *     library keeps no pointer after a call returns, but kernels read and
+ *     write the buffers until the stream reaches them.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) without host synchronisation; expert loads never leave the GPU.
+ *   - No call allocates device memory: scratch space comes from the caller's
+ *     workspace `ws` of `ws_bytes` bytes (size it with moe_workspace_bytes);
+ *     the workspace must be 256-byte aligned.
+ *   - Matrices of weights are stored [out][in] (the reduction dimension is
+ *     contiguous).  bf16 is stored as its 16-bit pattern; e4m3 is OCP E4M3FN
+ *     (largest finite 448) in one byte.
+ *   - Inputs must be finite; NaN and infinity are not checked.
+ *   - Calls on different streams that share a buffer race; the library holds
+ *     no global mutable state, so calls on different data may overlap.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,   /* null pointer, non-positive size, bad alignment */
+    MOE_ERR_UNSUPPORTED = -2,   /* shape or dtype combination outside the limits below */
+    MOE_ERR_WORKSPACE = -3,     /* ws_bytes smaller than moe_workspace_bytes() */
+    MOE_ERR_HIP = -4            /* a HIP runtime call or kernel launch failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype;
+
+/* flags */
+#define MOE_ADD_RESIDUAL 1u   /* moe_forward / moe_combine add u_t to the output */
+
+/*
+ * Shape and numerics of one layer (§2.1.2, §4.2).  Supported combinations
+ * (act_dtype, router_dtype, w_dtype, out_dtype):
+ *   (F32,  F32,  F32,  F32 )  fp32 everywhere
+ *   (BF16, BF16, BF16, BF16)  bf16 storage, fp32 accumulation
+ *   (BF16, BF16, E4M3, BF16)  bf16 u and centroids; expert GEMMs in e4m3 with
+ *                             1x128 activation / 128x128 weight fp32 scales
+ * Limits (MOE_ERR_UNSUPPORTED otherwise): n_routed % n_groups == 0,
+ * 1 <= topk_groups <= n_groups <= 64, 1 <= topk <= 32,
+ * topk <= topk_groups * n_routed / n_groups, n_routed <= 1024,
+ * 0 <= n_shared <= 8, d and inter multiples of 128, quant_block == 128,
+ * T * topk < 2^31, T * n_shared < 2^31.
+ */
+typedef struct moe_shape {
+    int64_t T;              /* tokens in the batch (T >= 0; T == 0 is a no-op) */
+    int32_t d;              /* hidden size (7168) */
+    int32_t n_routed;       /* N_r routed experts (256) */
+    int32_t n_shared;       /* N_s shared experts (1) */
+    int32_t n_groups;       /* expert groups (nodes) G (8); group g = experts [g*N_r/G, (g+1)*N_r/G) */
+    int32_t topk_groups;    /* M: groups a token may use (4) */
+    int32_t topk;           /* K_r: routed experts per token (8) */
+    int32_t inter;          /* expert intermediate size I (2048) */
+    int32_t act_dtype;      /* u, x_perm (non-e4m3), H (non-e4m3) storage: MOE_F32 | MOE_BF16 */
+    int32_t router_dtype;   /* centroids gate_w: equal to act_dtype */
+    int32_t w_dtype;        /* expert weights and GEMM inputs: act_dtype, or MOE_E4M3 */
+    int32_t out_dtype;      /* y_perm, y_shared, out: equal to act_dtype */
+    int32_t quant_block;    /* N_c = 128 */
+    float routed_scale;     /* factor on every gating value (1.0) */
+    uint32_t flags;         /* MOE_ADD_RESIDUAL or 0 */
+} moe_shape;
+
+/* ------------------------------------------------------------------------ */
+
+/*
+ * moe_route -- affinities, group-limited biased top-K, gating values
+ * (§2.1.2; the group rule and tie rule are readings of the prose):
+ *   s[t][i]  = sigmoid(sum_c u[t][c] * gate_w[i][c])   fp32 accumulation
+ *   s'       = s + bias (one fp32 add; used for selection only)
+ *   group g score = sum of its two largest s' (its only s' if N_r/G == 1);
+ *   the topk_groups best groups are kept, other experts are excluded;
+ *   the topk largest s' among kept experts are selected, slot order is
+ *   decreasing s'; every tie goes to the lower index;
+ *   topk_w[t][j] = routed_scale * s[t][e_j] / (s[t][e_0] + ... + s[t][e_{K-1}])
+ *   with the sum taken left to right in fp32.
+ * u [T][d] (act_dtype), gate_w [N_r][d] (router_dtype), bias [N_r] fp32.
+ * scores_in [T][N_r] fp32 or NULL: when given, u and gate_w are not read and
+ * selection runs on these affinities (bit-exact routing checks).
+ * scores_out [T][N_r] fp32 or NULL; topk_idx [T][K] int32; topk_w [T][K] fp32.
+ */
+int moe_route(const moe_shape *shape, const void *u, const void *gate_w, const float *bias,
+              const float *scores_in, float *scores_out, int32_t *topk_idx, float *topk_w,
+              void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_permute -- dispatch bookkeeping and row gather (§2.1.2: every
+ * (token, slot) pair is kept; "whole-batch load" = pairs per expert):
+ *   counts[i]   = #{(t, j) : topk_idx[t][j] == i}
+ *   offsets     = exclusive prefix sum of counts, offsets[N_r] = T*K
+ *   rows offsets[i] .. offsets[i+1]-1 belong to expert i, in increasing t
+ *   perm_token[row] = t,   inv_perm[t*K + j] = row
+ *   x_perm[row] = u[t]              when w_dtype != E4M3 (act_dtype copy)
+ *   x_perm[row] = Q_1x128(u[t]) with x_scales[row][d/128] when w_dtype == E4M3
+ *     (Q: scale = amax/448 in fp32, 1 for an all-zero tile; code =
+ *      E4M3 round-to-nearest-even of clamp(x/scale, -448, 448); §3.3).
+ * x_perm may be NULL (index outputs only); then u and x_scales are ignored.
+ * topk_idx entries must lie in [0, N_r) and be distinct within a token.
+ * ws: moe_workspace_bytes(shape, MOE_WS_PERMUTE).
+ */
+int moe_permute(const moe_shape *shape, const int32_t *topk_idx, const void *u,
+                int32_t *counts, int32_t *offsets, int32_t *perm_token, int32_t *inv_perm,
+                void *x_perm, float *x_scales, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_grouped_ffn -- SwiGLU experts over ragged row groups (§2.1.2 experts;
+ * the SwiGLU form is the reading of the unstated expert FFN):
+ *   for expert e and each of its rows r in [offsets[e], offsets[e+1]):
+ *     a = W_gate[e] x_r,  b = W_up[e] x_r        (fp32 accumulation)
+ *     h = SiLU(a) * b,    SiLU(a) = a / (1 + exp(-a)),   stored as
+ *         act_dtype, or for E4M3 quantised per 1x128 tile of I (Q above)
+ *     y[r] = W_down[e] h  (fp32 accumulation), stored in out_dtype
+ *   x_r = x[gather[r]] when gather != NULL, else x[r].
+ *   For E4M3 every 128-long block of the reduction is an fp32 partial sum of
+ *   code products, multiplied by (activation scale * weight block scale) and
+ *   added to the fp32 accumulator (§3.3 promotion every N_c products).
+ * n_exp experts; offsets [n_exp+1] int32 on the device, offsets[0] = 0,
+ * non-decreasing, offsets[n_exp] <= max_rows.
+ * x [*][d] in act_dtype, or e4m3 with x_scales [*][d/128] fp32.
+ * w_gate, w_up [n_exp][I][d]; w_down [n_exp][d][I] in w_dtype;
+ * w_scales: NULL unless E4M3, then 3 device pointers to fp32 block scales
+ * [n_exp][I/128][d/128], [n_exp][I/128][d/128], [n_exp][d/128][I/128]
+ * (the array of 3 pointers itself is host memory).
+ * y [max_rows][d] out_dtype.  ws: moe_ffn_workspace_bytes(shape, max_rows).
+ */
+int moe_grouped_ffn(const moe_shape *shape, int32_t n_exp, const int32_t *offsets, int64_t max_rows,
+                    const int32_t *gather, const void *x, const float *x_scales,
+                    const void *w_gate, const void *w_up, const void *w_down,
+                    const float *const *w_scales, void *y, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * moe_combine -- the layer output (§2.1.2 output equation; stripped on the
+ * page, read as shared experts plus gate-weighted routed experts):
+ *   out[t] = sum_j topk_w[t][j] * y_perm[inv_perm[t*K + j]]
+ *          + sum_s y_shared[s][t]  (+ u[t] if MOE_ADD_RESIDUAL)
+ * computed in fp32 and rounded once to out_dtype.
+ * y_perm [T*K][d], y_shared [N_s][T][d] (NULL when N_s == 0), out [T][d] in
+ * out_dtype; residual = u [T][d] (act_dtype), read only with the flag.
+ */
+int moe_combine(const moe_shape *shape, const void *y_perm, const int32_t *inv_perm, const float *topk_w,
+                const void *y_shared, const void *residual, void *out, void *stream);
+
+/*
+ * moe_forward -- the whole layer: moe_route, dispatch, the routed and shared
+ * grouped FFNs and moe_combine in one enqueue.  For E4M3, u is quantised
+ * once per token (1x128) and rows are gathered inside the expert GEMM instead
+ * of being copied.
+ * routed_w = {W_gate [N_r][I][d], W_up [N_r][I][d], W_down [N_r][d][I]};
+ * shared_w = the same with N_s (NULL when N_s == 0).  routed_s / shared_s:
+ * the 3 block-scale arrays for E4M3, else NULL.  (Pointer arrays are host
+ * memory; their elements are device pointers.)
+ * Optional outputs (NULL to skip): topk_idx_out [T][K], topk_w_out [T][K],
+ * counts_out [N_r], scores_out [T][N_r].
+ * ws: moe_workspace_bytes(shape, MOE_WS_FORWARD).
+ */
+int moe_forward(const moe_shape *shape, const void *u, const void *gate_w, const float *bias,
+                const void *const *routed_w, const float *const *routed_s,
+                const void *const *shared_w, const float *const *shared_s,
+                void *out, int32_t *topk_idx_out, float *topk_w_out, int32_t *counts_out,
+                float *scores_out, void *ws, size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* helpers                                                                  */
+
+enum { MOE_WS_ROUTE = 0, MOE_WS_PERMUTE = 1, MOE_WS_FORWARD = 2 };
+
+/* Workspace bytes for moe_route / moe_permute / moe_forward at this shape,
+ * or 0 when the shape is rejected (see moe_last_error). */
+size_t moe_workspace_bytes(const moe_shape *shape, int which);
+
+/* Workspace bytes for moe_grouped_ffn with max_rows rows (0 when rejected). */
+size_t moe_ffn_workspace_bytes(const moe_shape *shape, int64_t max_rows);
+
+/*
+ * moe_bias_update -- one auxiliary-loss-free step (§2.1.2; gamma = 0.001 in
+ * §4.2): mean = fp32(T*K) / fp32(N_r);
+ *   bias[i] = bias[i] + gamma * sign(mean - counts[i])   (sign(0) = 0)
+ * (reading: "overloaded" = load above the mean; an exact tie leaves b_i).
+ * counts [N_r] int32, bias [N_r] fp32 updated in place.
+ */
+int moe_bias_update(const moe_shape *shape, const int32_t *counts, float *bias, float gamma, void *stream);
+
+/*
+ * moe_quantize_1x128 -- Q over 1x128 tiles of each row of x [rows][cols]
+ * (x_dtype MOE_F32 or MOE_BF16; cols % 128 == 0): q [rows][cols] e4m3,
+ * s [rows][cols/128] fp32 (§3.3 activation tiles).
+ */
+int moe_quantize_1x128(int64_t rows, int32_t cols, int32_t x_dtype, const void *x, uint8_t *q, float *s,
+                       void *stream);
+
+/*
+ * moe_quantize_weights_128x128 -- Q over 128x128 blocks of nmat matrices
+ * w [nmat][rows][cols] (w_dtype MOE_F32 or MOE_BF16; rows, cols % 128 == 0):
+ * q [nmat][rows][cols] e4m3, s [nmat][rows/128][cols/128] fp32 (§3.3 weight
+ * blocks).  Weight preparation, not part of the per-step path.
+ */
+int moe_quantize_weights_128x128(int64_t nmat, int32_t rows, int32_t cols, int32_t w_dtype, const void *w,
+                                 uint8_t *q, float *s, void *stream);
+
+/* Message for the calling thread's last failed call ("" if none). */
+const char *moe_last_error(void);
+
+/* Library version string. */
+const char *moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

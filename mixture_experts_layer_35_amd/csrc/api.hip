@@ -1,0 +1,476 @@
+// api.hip -- the C ABI of libmoe (declared in include/moe.h): host-side
+// argument checks, workspace layout and the launch sequence of each call.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+
+#include "moe.h"
+#include "internal.h"
+
+namespace moe {
+
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cache[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int code, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_check(hipError_t e, const char *what) {
+    if (e == hipSuccess) return MOE_OK;
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIPCHK(expr)                                      \
+    do {                                                  \
+        int rc_ = hip_check((expr), #expr);               \
+        if (rc_ != MOE_OK) return rc_;                    \
+    } while (0)
+
+#define NEED(ptr)                                                                            \
+    do {                                                                                     \
+        if (!(ptr)) return fail(MOE_ERR_INVALID_ARG, "%s: %s must not be NULL", fn, #ptr); \
+    } while (0)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int esize(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
+
+// Checks everything about the shape that the kernels rely on.
+int check_shape(const moe_shape *s, const char *fn) {
+    if (!s) return fail(MOE_ERR_INVALID_ARG, "%s: shape must not be NULL", fn);
+    if (s->T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T = %lld is negative", fn, (long long)s->T);
+    if (s->d <= 0 || s->n_routed <= 0 || s->n_groups <= 0 || s->topk_groups <= 0 || s->topk <= 0 || s->inter <= 0 ||
+        s->n_shared < 0)
+        return fail(MOE_ERR_INVALID_ARG, "%s: sizes must be positive (n_shared >= 0)", fn);
+    const bool f32 = s->act_dtype == MOE_F32 && s->router_dtype == MOE_F32 && s->w_dtype == MOE_F32 &&
+                     s->out_dtype == MOE_F32;
+    const bool bf16 = s->act_dtype == MOE_BF16 && s->router_dtype == MOE_BF16 && s->w_dtype == MOE_BF16 &&
+                      s->out_dtype == MOE_BF16;
+    const bool fp8 = s->act_dtype == MOE_BF16 && s->router_dtype == MOE_BF16 && s->w_dtype == MOE_E4M3 &&
+                     s->out_dtype == MOE_BF16;
+    if (!f32 && !bf16 && !fp8)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: dtype combination (act %d, router %d, w %d, out %d) is not supported",
+                    fn, s->act_dtype, s->router_dtype, s->w_dtype, s->out_dtype);
+    if (s->n_routed > kMaxExperts)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: n_routed = %d exceeds %d", fn, s->n_routed, kMaxExperts);
+    if (s->n_routed % s->n_groups)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: n_routed = %d is not a multiple of n_groups = %d", fn, s->n_routed,
+                    s->n_groups);
+    if (s->n_groups > 64 || s->topk_groups > s->n_groups)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: need topk_groups <= n_groups <= 64 (got %d, %d)", fn, s->topk_groups,
+                    s->n_groups);
+    if (s->topk > 32 || (int64_t)s->topk > (int64_t)s->topk_groups * (s->n_routed / s->n_groups))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: topk = %d must be <= 32 and <= topk_groups * n_routed / n_groups", fn,
+                    s->topk);
+    if (s->topk > s->n_routed)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: topk = %d exceeds n_routed", fn, s->topk);
+    if (s->n_shared > 8) return fail(MOE_ERR_UNSUPPORTED, "%s: n_shared = %d exceeds 8", fn, s->n_shared);
+    if (s->d % 128 || s->inter % 128)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: d = %d and inter = %d must be multiples of 128", fn, s->d, s->inter);
+    if (s->quant_block != 128)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: quant_block = %d (only 128 is supported)", fn, s->quant_block);
+    if (s->T * (int64_t)s->topk >= (1ll << 31) || s->T * (int64_t)(s->n_shared ? s->n_shared : 1) >= (1ll << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: T * topk and T * n_shared must be below 2^31", fn);
+    if (s->flags & ~MOE_ADD_RESIDUAL) return fail(MOE_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, s->flags);
+    return MOE_OK;
+}
+
+int ws_check(void *ws, size_t have, size_t need, const char *fn) {
+    if (need == 0) return MOE_OK;
+    if (!ws) return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got NULL", fn, need);
+    if ((uintptr_t)ws & 255) return fail(MOE_ERR_INVALID_ARG, "%s: workspace must be 256-byte aligned", fn);
+    if (have < need) return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu", fn, need, have);
+    return MOE_OK;
+}
+
+int dt_of(int d) { return d == MOE_F32 ? DT_F32 : d == MOE_BF16 ? DT_BF16 : DT_E4M3; }
+
+// ---- workspace layouts --------------------------------------------------------
+
+struct FwdLayout {
+    size_t scores, idx, w, counts, offsets, bc, perm, inv, uq, us, h, hs, hsh, hshs, yperm, ysh, total;
+};
+
+FwdLayout fwd_layout(const moe_shape *s) {
+    FwdLayout L{};
+    const int64_t T = s->T, TK = T * s->topk, TS = T * s->n_shared;
+    const bool fp8 = s->w_dtype == MOE_E4M3;
+    const int hsz = fp8 ? 1 : esize(s->act_dtype);
+    const int osz = esize(s->out_dtype);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
+    L.scores = take((size_t)T * s->n_routed * 4);
+    L.idx = take((size_t)TK * 4);
+    L.w = take((size_t)TK * 4);
+    L.counts = take((size_t)s->n_routed * 4);
+    L.offsets = take((size_t)(s->n_routed + 1) * 4);
+    L.bc = take((size_t)perm_blocks(T) * s->n_routed * 4);
+    L.perm = take((size_t)TK * 4);
+    L.inv = take((size_t)TK * 4);
+    L.uq = take(fp8 ? (size_t)T * s->d : 0);
+    L.us = take(fp8 ? (size_t)T * (s->d / 128) * 4 : 0);
+    L.h = take((size_t)TK * s->inter * hsz);
+    L.hs = take(fp8 ? (size_t)TK * (s->inter / 128) * 4 : 0);
+    L.hsh = take((size_t)TS * s->inter * hsz);
+    L.hshs = take(fp8 ? (size_t)TS * (s->inter / 128) * 4 : 0);
+    L.yperm = take((size_t)TK * s->d * osz);
+    L.ysh = take((size_t)TS * s->d * osz);
+    L.total = o;
+    return L;
+}
+
+size_t ffn_ws(const moe_shape *s, int64_t max_rows) {
+    const bool fp8 = s->w_dtype == MOE_E4M3;
+    const int hsz = fp8 ? 1 : esize(s->act_dtype);
+    return align256((size_t)max_rows * s->inter * hsz) + (fp8 ? align256((size_t)max_rows * (s->inter / 128) * 4) : 0);
+}
+
+int run_ffn_pair(const moe_shape *s, const FfnProblem *gu, const FfnProblem *dn, int nprob, hipStream_t st) {
+    FfnArgs a{};
+    a.nprob = nprob;
+    a.K = s->d;
+    a.F = s->inter;
+    for (int i = 0; i < nprob; ++i) a.p[i] = gu[i];
+    HIPCHK(launch_ffn(dt_of(s->w_dtype), true, a, st));
+    a.K = s->inter;
+    a.F = s->d;
+    for (int i = 0; i < nprob; ++i) a.p[i] = dn[i];
+    HIPCHK(launch_ffn(dt_of(s->w_dtype), false, a, st));
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_last_error(void) { return g_err.c_str(); }
+
+const char *moe_version(void) { return "libmoe 0.1 (gfx950)"; }
+
+size_t moe_workspace_bytes(const moe_shape *s, int which) {
+    if (check_shape(s, "moe_workspace_bytes") != MOE_OK) return 0;
+    switch (which) {
+        case MOE_WS_ROUTE: return align256((size_t)s->T * s->n_routed * 4);
+        case MOE_WS_PERMUTE: return align256((size_t)perm_blocks(s->T) * s->n_routed * 4);
+        case MOE_WS_FORWARD: return fwd_layout(s).total;
+        default: fail(MOE_ERR_INVALID_ARG, "moe_workspace_bytes: unknown workspace kind %d", which); return 0;
+    }
+}
+
+size_t moe_ffn_workspace_bytes(const moe_shape *s, int64_t max_rows) {
+    if (check_shape(s, "moe_ffn_workspace_bytes") != MOE_OK) return 0;
+    if (max_rows < 0) { fail(MOE_ERR_INVALID_ARG, "moe_ffn_workspace_bytes: max_rows < 0"); return 0; }
+    return ffn_ws(s, max_rows);
+}
+
+int moe_route(const moe_shape *s, const void *u, const void *gate_w, const float *bias, const float *scores_in,
+              float *scores_out, int32_t *topk_idx, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "moe_route";
+    int rc = check_shape(s, fn);
+    if (rc) return rc;
+    NEED(bias);
+    NEED(topk_idx);
+    NEED(topk_w);
+    if (!scores_in) {
+        NEED(u);
+        NEED(gate_w);
+    }
+    float *scores = scores_out;
+    if (!scores_in && !scores) {
+        rc = ws_check(ws, ws_bytes, align256((size_t)s->T * s->n_routed * 4), fn);
+        if (rc) return rc;
+        scores = (float *)ws;
+    }
+    if (s->T == 0) return MOE_OK;
+    hipStream_t st = (hipStream_t)stream;
+    if (scores_in) {
+        if (scores_out)
+            HIPCHK(hipMemcpyAsync(scores_out, scores_in, (size_t)s->T * s->n_routed * 4, hipMemcpyDeviceToDevice, st));
+        scores = (float *)scores_in;
+    } else {
+        HIPCHK(launch_router_gemm(dt_of(s->act_dtype), u, gate_w, scores, s->T, s->d, s->n_routed, st));
+    }
+    HIPCHK(launch_router_select(scores, bias, s->T, s->n_routed, s->n_groups, s->topk_groups, s->topk,
+                                s->routed_scale, topk_idx, topk_w, st));
+    return MOE_OK;
+}
+
+int moe_permute(const moe_shape *s, const int32_t *topk_idx, const void *u, int32_t *counts, int32_t *offsets,
+                int32_t *perm_token, int32_t *inv_perm, void *x_perm, float *x_scales, void *ws, size_t ws_bytes,
+                void *stream) {
+    const char *fn = "moe_permute";
+    int rc = check_shape(s, fn);
+    if (rc) return rc;
+    NEED(topk_idx);
+    NEED(counts);
+    NEED(offsets);
+    NEED(perm_token);
+    NEED(inv_perm);
+    const bool fp8 = s->w_dtype == MOE_E4M3;
+    if (x_perm) {
+        NEED(u);
+        if (fp8) NEED(x_scales);
+    }
+    rc = ws_check(ws, ws_bytes, align256((size_t)perm_blocks(s->T) * s->n_routed * 4), fn);
+    if (rc) return rc;
+    hipStream_t st = (hipStream_t)stream;
+    const int64_t TK = s->T * s->topk;
+    int32_t *bc = (int32_t *)ws;
+    HIPCHK(launch_perm_hist(topk_idx, s->T, s->topk, s->n_routed, bc, st));
+    HIPCHK(launch_perm_scan(bc, s->T, s->n_routed, counts, offsets, st));
+    HIPCHK(launch_perm_scatter(topk_idx, bc, s->T, s->topk, s->n_routed, perm_token, inv_perm, st));
+    if (x_perm) {
+        if (fp8)
+            HIPCHK(launch_quant_rows(dt_of(s->act_dtype), u, perm_token, TK, s->d, (uint8_t *)x_perm, x_scales, st));
+        else
+            HIPCHK(launch_gather_rows(dt_of(s->act_dtype), u, perm_token, TK, s->d, x_perm, st));
+    }
+    return MOE_OK;
+}
+
+int moe_grouped_ffn(const moe_shape *s, int32_t n_exp, const int32_t *offsets, int64_t max_rows,
+                    const int32_t *gather, const void *x, const float *x_scales, const void *w_gate,
+                    const void *w_up, const void *w_down, const float *const *w_scales, void *y, void *ws,
+                    size_t ws_bytes, void *stream) {
+    const char *fn = "moe_grouped_ffn";
+    int rc = check_shape(s, fn);
+    if (rc) return rc;
+    if (n_exp <= 0 || n_exp > kMaxExperts)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: n_exp = %d must be in [1, %d]", fn, n_exp, kMaxExperts);
+    if (max_rows < 0 || max_rows >= (1ll << 31)) return fail(MOE_ERR_INVALID_ARG, "%s: max_rows out of range", fn);
+    NEED(offsets);
+    NEED(x);
+    NEED(w_gate);
+    NEED(w_up);
+    NEED(w_down);
+    NEED(y);
+    const bool fp8 = s->w_dtype == MOE_E4M3;
+    if (fp8) {
+        NEED(x_scales);
+        NEED(w_scales);
+        if (!w_scales[0] || !w_scales[1] || !w_scales[2])
+            return fail(MOE_ERR_INVALID_ARG, "%s: w_scales entries must not be NULL", fn);
+    }
+    rc = ws_check(ws, ws_bytes, ffn_ws(s, max_rows), fn);
+    if (rc) return rc;
+    if (max_rows == 0) return MOE_OK;
+    char *h = (char *)ws;
+    float *hs = fp8 ? (float *)(h + align256((size_t)max_rows * s->inter)) : nullptr;
+    FfnProblem gu{}, dn{};
+    gu.n_exp = dn.n_exp = n_exp;
+    gu.offsets = dn.offsets = offsets;
+    gu.gather = gather;
+    gu.x = x;
+    gu.xs = x_scales;
+    gu.w0 = w_gate;
+    gu.w1 = w_up;
+    gu.s0 = fp8 ? w_scales[0] : nullptr;
+    gu.s1 = fp8 ? w_scales[1] : nullptr;
+    gu.out = h;
+    gu.out_s = hs;
+    dn.x = h;
+    dn.xs = hs;
+    dn.w0 = w_down;
+    dn.s0 = fp8 ? w_scales[2] : nullptr;
+    dn.out = y;
+    return run_ffn_pair(s, &gu, &dn, 1, (hipStream_t)stream);
+}
+
+int moe_combine(const moe_shape *s, const void *y_perm, const int32_t *inv_perm, const float *topk_w,
+                const void *y_shared, const void *residual, void *out, void *stream) {
+    const char *fn = "moe_combine";
+    int rc = check_shape(s, fn);
+    if (rc) return rc;
+    NEED(y_perm);
+    NEED(inv_perm);
+    NEED(topk_w);
+    NEED(out);
+    if (s->n_shared > 0) NEED(y_shared);
+    if (s->flags & MOE_ADD_RESIDUAL) NEED(residual);
+    HIPCHK(launch_combine(dt_of(s->out_dtype), dt_of(s->act_dtype), y_perm, inv_perm, topk_w,
+                          s->n_shared ? y_shared : nullptr, s->n_shared,
+                          (s->flags & MOE_ADD_RESIDUAL) ? residual : nullptr, out, s->T, s->d, s->topk,
+                          (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_forward(const moe_shape *s, const void *u, const void *gate_w, const float *bias,
+                const void *const *routed_w, const float *const *routed_s, const void *const *shared_w,
+                const float *const *shared_s, void *out, int32_t *topk_idx_out, float *topk_w_out,
+                int32_t *counts_out, float *scores_out, void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "moe_forward";
+    int rc = check_shape(s, fn);
+    if (rc) return rc;
+    NEED(u);
+    NEED(gate_w);
+    NEED(bias);
+    NEED(routed_w);
+    NEED(out);
+    if (!routed_w[0] || !routed_w[1] || !routed_w[2])
+        return fail(MOE_ERR_INVALID_ARG, "%s: routed_w entries must not be NULL", fn);
+    const bool fp8 = s->w_dtype == MOE_E4M3;
+    if (fp8) {
+        NEED(routed_s);
+        if (!routed_s[0] || !routed_s[1] || !routed_s[2])
+            return fail(MOE_ERR_INVALID_ARG, "%s: routed_s entries must not be NULL", fn);
+    }
+    if (s->n_shared > 0) {
+        NEED(shared_w);
+        if (!shared_w[0] || !shared_w[1] || !shared_w[2])
+            return fail(MOE_ERR_INVALID_ARG, "%s: shared_w entries must not be NULL", fn);
+        if (fp8) {
+            NEED(shared_s);
+            if (!shared_s[0] || !shared_s[1] || !shared_s[2])
+                return fail(MOE_ERR_INVALID_ARG, "%s: shared_s entries must not be NULL", fn);
+        }
+    }
+    const FwdLayout L = fwd_layout(s);
+    rc = ws_check(ws, ws_bytes, L.total, fn);
+    if (rc) return rc;
+    if (s->T == 0) return MOE_OK;
+
+    hipStream_t st = (hipStream_t)stream;
+    char *W = (char *)ws;
+    const int64_t T = s->T, TK = T * s->topk;
+    float *scores = scores_out ? scores_out : (float *)(W + L.scores);
+    int32_t *idx = topk_idx_out ? topk_idx_out : (int32_t *)(W + L.idx);
+    float *tw = topk_w_out ? topk_w_out : (float *)(W + L.w);
+    int32_t *counts = counts_out ? counts_out : (int32_t *)(W + L.counts);
+    int32_t *offsets = (int32_t *)(W + L.offsets);
+    int32_t *bc = (int32_t *)(W + L.bc);
+    int32_t *perm = (int32_t *)(W + L.perm);
+    int32_t *inv = (int32_t *)(W + L.inv);
+
+    // 1. affinities and selection
+    HIPCHK(launch_router_gemm(dt_of(s->act_dtype), u, gate_w, scores, T, s->d, s->n_routed, st));
+    HIPCHK(launch_router_select(scores, bias, T, s->n_routed, s->n_groups, s->topk_groups, s->topk, s->routed_scale,
+                                idx, tw, st));
+    // 2. dispatch bookkeeping (rows are gathered inside the expert GEMM)
+    HIPCHK(launch_perm_hist(idx, T, s->topk, s->n_routed, bc, st));
+    HIPCHK(launch_perm_scan(bc, T, s->n_routed, counts, offsets, st));
+    HIPCHK(launch_perm_scatter(idx, bc, T, s->topk, s->n_routed, perm, inv, st));
+    // 3. fp8: one 1x128 quantisation per token
+    const void *xin = u;
+    const float *xs = nullptr;
+    if (fp8) {
+        HIPCHK(launch_quant_rows(dt_of(s->act_dtype), u, nullptr, T, s->d, (uint8_t *)(W + L.uq), (float *)(W + L.us),
+                                 st));
+        xin = W + L.uq;
+        xs = (const float *)(W + L.us);
+    }
+    // 4. routed and shared experts
+    FfnProblem gu[2] = {}, dn[2] = {};
+    gu[0].n_exp = dn[0].n_exp = s->n_routed;
+    gu[0].offsets = dn[0].offsets = offsets;
+    gu[0].gather = perm;
+    gu[0].x = xin;
+    gu[0].xs = xs;
+    gu[0].w0 = routed_w[0];
+    gu[0].w1 = routed_w[1];
+    gu[0].s0 = fp8 ? routed_s[0] : nullptr;
+    gu[0].s1 = fp8 ? routed_s[1] : nullptr;
+    gu[0].out = W + L.h;
+    gu[0].out_s = fp8 ? (float *)(W + L.hs) : nullptr;
+    dn[0].x = W + L.h;
+    dn[0].xs = gu[0].out_s;
+    dn[0].w0 = routed_w[2];
+    dn[0].s0 = fp8 ? routed_s[2] : nullptr;
+    dn[0].out = W + L.yperm;
+    int nprob = 1;
+    if (s->n_shared > 0) {
+        nprob = 2;
+        gu[1].n_exp = dn[1].n_exp = s->n_shared;
+        gu[1].offsets = dn[1].offsets = nullptr;
+        gu[1].rows_fixed = dn[1].rows_fixed = T;
+        gu[1].x_local = 1;
+        gu[1].x = xin;
+        gu[1].xs = xs;
+        gu[1].w0 = shared_w[0];
+        gu[1].w1 = shared_w[1];
+        gu[1].s0 = fp8 ? shared_s[0] : nullptr;
+        gu[1].s1 = fp8 ? shared_s[1] : nullptr;
+        gu[1].out = W + L.hsh;
+        gu[1].out_s = fp8 ? (float *)(W + L.hshs) : nullptr;
+        dn[1].x = W + L.hsh;
+        dn[1].xs = gu[1].out_s;
+        dn[1].w0 = shared_w[2];
+        dn[1].s0 = fp8 ? shared_s[2] : nullptr;
+        dn[1].out = W + L.ysh;
+    }
+    rc = run_ffn_pair(s, gu, dn, nprob, st);
+    if (rc) return rc;
+    // 5. gate-weighted combine plus shared experts
+    HIPCHK(launch_combine(dt_of(s->out_dtype), dt_of(s->act_dtype), W + L.yperm, inv, tw,
+                          s->n_shared ? W + L.ysh : nullptr, s->n_shared,
+                          (s->flags & MOE_ADD_RESIDUAL) ? u : nullptr, out, T, s->d, s->topk, st));
+    (void)TK;
+    return MOE_OK;
+}
+
+int moe_bias_update(const moe_shape *s, const int32_t *counts, float *bias, float gamma, void *stream) {
+    const char *fn = "moe_bias_update";
+    int rc = check_shape(s, fn);
+    if (rc) return rc;
+    NEED(counts);
+    NEED(bias);
+    HIPCHK(launch_bias_update(counts, bias, s->T, s->topk, s->n_routed, gamma, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_quantize_1x128(int64_t rows, int32_t cols, int32_t x_dtype, const void *x, uint8_t *q, float *sc,
+                       void *stream) {
+    const char *fn = "moe_quantize_1x128";
+    if (rows < 0 || cols <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad size", fn);
+    if (cols % 128) return fail(MOE_ERR_UNSUPPORTED, "%s: cols = %d is not a multiple of 128", fn, cols);
+    if (x_dtype != MOE_F32 && x_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: x_dtype %d", fn, x_dtype);
+    NEED(x);
+    NEED(q);
+    NEED(sc);
+    HIPCHK(launch_quant_rows(dt_of(x_dtype), x, nullptr, rows, cols, q, sc, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_quantize_weights_128x128(int64_t nmat, int32_t rows, int32_t cols, int32_t w_dtype, const void *w,
+                                 uint8_t *q, float *sc, void *stream) {
+    const char *fn = "moe_quantize_weights_128x128";
+    if (nmat < 0 || rows <= 0 || cols <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad size", fn);
+    if (rows % 128 || cols % 128) return fail(MOE_ERR_UNSUPPORTED, "%s: rows and cols must be multiples of 128", fn);
+    if (w_dtype != MOE_F32 && w_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "%s: w_dtype %d", fn, w_dtype);
+    if (nmat * (rows / 128) * (int64_t)(cols / 128) >= (1ll << 31))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: too many blocks for one call", fn);
+    NEED(w);
+    NEED(q);
+    NEED(sc);
+    HIPCHK(launch_quant_blocks(dt_of(w_dtype), w, nmat, rows, cols, q, sc, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,77 @@
+// internal.h -- launchers shared between the libmoe translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
+
+// Number of compute units of the current device (cached per device).
+int device_cus();
+
+// ---- router ----------------------------------------------------------------
+// scores[T][Nr] = sigmoid(u[T][d] . gate_w[Nr][d]^T), fp32 accumulation.
+hipError_t launch_router_gemm(int dt, const void *u, const void *gate_w, float *scores, int64_t T, int d, int Nr,
+                              hipStream_t s);
+// Group-limited biased top-K selection and normalised gates from fp32 scores.
+hipError_t launch_router_select(const float *scores, const float *bias, int64_t T, int Nr, int G, int Mg, int K,
+                                float routed_scale, int32_t *topk_idx, float *topk_w, hipStream_t s);
+
+// ---- dispatch --------------------------------------------------------------
+// Block histogram (64 tokens per block) -> blockcounts[nb][Nr].
+hipError_t launch_perm_hist(const int32_t *topk_idx, int64_t T, int K, int Nr, int32_t *blockcounts,
+                            hipStream_t s);
+// counts, offsets, per-block row bases (in place in blockcounts).
+hipError_t launch_perm_scan(int32_t *blockcounts, int64_t T, int Nr, int32_t *counts, int32_t *offsets,
+                            hipStream_t s);
+// perm_token / inv_perm from topk_idx and per-block row bases.
+hipError_t launch_perm_scatter(const int32_t *topk_idx, const int32_t *blockbase, int64_t T, int K, int Nr,
+                               int32_t *perm_token, int32_t *inv_perm, hipStream_t s);
+inline int64_t perm_blocks(int64_t T) { return (T + 63) / 64; }
+
+// dst[r] = src[idx ? idx[r] : r] for r < rows, row = cols elements of dtype dt (copy).
+hipError_t launch_gather_rows(int dt, const void *src, const int32_t *idx, int64_t rows, int cols, void *dst,
+                              hipStream_t s);
+// q[r], sc[r] = Q_1x128(src[idx ? idx[r] : r]); src dtype dt (F32 / BF16).
+hipError_t launch_quant_rows(int dt, const void *src, const int32_t *idx, int64_t rows, int cols, uint8_t *q,
+                             float *sc, hipStream_t s);
+// 128x128 block quantisation of nmat [rows][cols] matrices.
+hipError_t launch_quant_blocks(int dt, const void *w, int64_t nmat, int rows, int cols, uint8_t *q, float *sc,
+                               hipStream_t s);
+
+// ---- grouped FFN -------------------------------------------------------------
+struct FfnProblem {
+    int n_exp;              // experts
+    int x_local;            // x row of local row r is r (shared experts over u)
+    const int32_t *offsets; // [n_exp+1] device row offsets, or null: expert e owns rows [e*rows_fixed, +rows_fixed)
+    int64_t rows_fixed;
+    const int32_t *gather;  // x row of problem row R is gather[R] (null: R, or local r when x_local)
+    const void *x;          // activations, rows of K elements
+    const float *xs;        // E4M3: [rows][K/128] scales
+    const void *w0;         // gate (gate/up pass) or down weights, [n_exp][F][K]
+    const void *w1;         // up weights (gate/up pass)
+    const float *s0, *s1;   // E4M3 block scales [n_exp][F/128][K/128]
+    void *out;              // gate/up: H [rows][F]; down: y [rows][F]
+    float *out_s;           // E4M3 gate/up: H scales [rows][F/128]
+};
+struct FfnArgs {
+    FfnProblem p[2];
+    int nprob;
+    int K;   // reduction length
+    int F;   // output features (I for gate/up, d for down)
+};
+constexpr int kMaxExperts = 1024;
+hipError_t launch_ffn(int dt, bool gateup, const FfnArgs &a, hipStream_t s);
+
+// ---- combine / bias ----------------------------------------------------------
+hipError_t launch_combine(int dt_out, int dt_res, const void *y_perm, const int32_t *inv_perm, const float *topk_w,
+                          const void *y_shared, int Ns, const void *residual, void *out, int64_t T, int d, int K,
+                          hipStream_t s);
+hipError_t launch_bias_update(const int32_t *counts, float *bias, int64_t T, int K, int Nr, float gamma,
+                              hipStream_t s);
+hipError_t launch_set_offsets(int32_t *offsets, int n, int64_t step, hipStream_t s);
+
+}  // namespace moe

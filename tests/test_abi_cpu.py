@@ -1,0 +1,140 @@
+"""Host-side checks of libmoe that need no GPU: the library loads, exports every
+entry point declared in include/moe.h, lays out moe_shape as the binding does,
+and rejects bad arguments with the documented codes before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mixture_experts_layer_35_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(moe.LIB_PATH):
+        from mixture_experts_layer_35_amd import build
+        build.build()
+    return moe.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", text, re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert {"moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(moe.EXPORTED) == set(names)
+
+
+def test_shape_struct_layout_matches_header(tmp_path, lib):
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "moe.h"\n'
+                   'int main(void){printf("%zu %zu %zu %zu %zu\\n", sizeof(moe_shape), offsetof(moe_shape, d),'
+                   ' offsetof(moe_shape, act_dtype), offsetof(moe_shape, routed_scale), offsetof(moe_shape, flags));'
+                   'return 0;}\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    S = moe.MoeShape
+    assert [int(x) for x in out] == [ctypes.sizeof(S), S.d.offset, S.act_dtype.offset, S.routed_scale.offset,
+                                     S.flags.offset]
+
+
+def tiny(**kw):
+    s = moe.make_shape(256, 256, 16, 1, 4, 2, 2, 128, "fp32")
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+FAKE = 1 << 20     # an aligned non-null address; rejected calls never dereference it
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (dict(d=200), moe.MOE_ERR_UNSUPPORTED),
+    (dict(inter=100), moe.MOE_ERR_UNSUPPORTED),
+    (dict(n_routed=18), moe.MOE_ERR_UNSUPPORTED),          # not a multiple of n_groups
+    (dict(topk=9), moe.MOE_ERR_UNSUPPORTED),               # more than topk_groups * group size
+    (dict(topk=33, n_routed=64, n_groups=1, topk_groups=1), moe.MOE_ERR_UNSUPPORTED),
+    (dict(topk_groups=5), moe.MOE_ERR_UNSUPPORTED),
+    (dict(n_groups=128, n_routed=128), moe.MOE_ERR_UNSUPPORTED),
+    (dict(n_routed=2048, n_groups=8), moe.MOE_ERR_UNSUPPORTED),
+    (dict(n_shared=9), moe.MOE_ERR_UNSUPPORTED),
+    (dict(quant_block=64), moe.MOE_ERR_UNSUPPORTED),
+    (dict(w_dtype=moe.MOE_E4M3), moe.MOE_ERR_UNSUPPORTED),  # fp32 activations with e4m3 weights
+    (dict(out_dtype=moe.MOE_BF16), moe.MOE_ERR_UNSUPPORTED),
+    (dict(T=-1), moe.MOE_ERR_INVALID_ARG),
+    (dict(d=0), moe.MOE_ERR_INVALID_ARG),
+    (dict(T=1 << 29, topk=8, n_routed=64, n_groups=8, topk_groups=4), moe.MOE_ERR_UNSUPPORTED),   # T*K >= 2^31
+    (dict(flags=4), moe.MOE_ERR_INVALID_ARG),
+])
+def test_shape_rejections(lib, mutate, code):
+    s = tiny(**mutate)
+    rc = lib.moe_route(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None)
+    assert rc == code, moe.moe_last_error()
+    assert moe.moe_last_error()
+    assert lib.moe_workspace_bytes(ctypes.byref(s), moe.MOE_WS_FORWARD) == 0
+
+
+def test_null_pointer_and_workspace_rejections(lib):
+    s = tiny()
+    assert lib.moe_route(None, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_route(ctypes.byref(s), None, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_INVALID_ARG
+    assert "u must not be NULL" in moe.moe_last_error()
+    # no scores_out: the affinities need workspace
+    assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None, 0, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 16, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE + 4, 1 << 30, None) == \
+        moe.MOE_ERR_INVALID_ARG                            # misaligned workspace
+    need = lib.moe_workspace_bytes(ctypes.byref(s), moe.MOE_WS_PERMUTE)
+    assert need > 0
+    assert lib.moe_permute(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, need - 1, None) == \
+        moe.MOE_ERR_WORKSPACE
+    ffn = lib.moe_ffn_workspace_bytes(ctypes.byref(s), 512)
+    assert ffn >= 512 * 128 * 4
+    assert lib.moe_grouped_ffn(ctypes.byref(s), 0, FAKE, 512, None, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                               ffn, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_grouped_ffn(ctypes.byref(s), 4, FAKE, 512, None, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                               ffn - 1, None) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_combine(ctypes.byref(s), FAKE, FAKE, FAKE, None, None, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    s8 = moe.make_shape(256, 256, 16, 1, 4, 2, 2, 128, "fp8")
+    assert lib.moe_grouped_ffn(ctypes.byref(s8), 4, FAKE, 512, None, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, FAKE,
+                               1 << 30, None) == moe.MOE_ERR_INVALID_ARG   # e4m3 needs scales
+    assert lib.moe_quantize_1x128(4, 100, moe.MOE_BF16, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_quantize_weights_128x128(1, 128, 96, moe.MOE_BF16, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_empty_batch_is_a_noop(lib):
+    # T = 0: checks pass and the call returns before touching the device
+    s = tiny(T=0)
+    need = lib.moe_workspace_bytes(ctypes.byref(s), moe.MOE_WS_FORWARD)
+    arr = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    p = ctypes.cast(arr, ctypes.c_void_p)
+    rc = lib.moe_forward(ctypes.byref(s), FAKE, FAKE, FAKE, p, None, p, None, FAKE, None, None, None, None, FAKE,
+                         need, None)
+    assert rc == moe.MOE_OK, moe.moe_last_error()
+    assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_OK
+
+
+def test_workspace_grows_with_tokens(lib):
+    a = lib.moe_workspace_bytes(ctypes.byref(moe.make_shape(4096, 7168, 256, 1, 8, 4, 8, 2048, "bf16")), 2)
+    b = lib.moe_workspace_bytes(ctypes.byref(moe.make_shape(8192, 7168, 256, 1, 8, 4, 8, 2048, "bf16")), 2)
+    assert 0 < a < b
+    # y_perm alone: T*K rows of d bf16
+    assert a > 4096 * 8 * 7168 * 2
+
+
+def test_binding_raises_with_message(lib):
+    s = tiny(d=200)
+    with pytest.raises(moe.MoeError) as e:
+        moe.moe_route(s, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, stream=0)
+    assert "multiples of 128" in str(e.value) and e.value.code == moe.MOE_ERR_UNSUPPORTED
