@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Throughput of the DeepSeekMoE layer forward pass on one MI355X.
+
+A step is one moe_forward call (router, dispatch, gate/up and down expert
+kernels, combine) over one batch of synthetic tokens already resident in HBM.
+Default workload: the V3-shape bf16 prefill batch (T = 4096, d = 7168, 256
+routed + 1 shared experts, top-8 of 8 groups with top-4 groups, I = 2048).
+
+Prints one JSON line: tokens/s as `value`, plus layer TFLOP/s, per-stage times
+measured with HIP events on the launch stream, a `roofline` object for the
+dominant kernel and a `cpu_baseline` object (the CPU oracle on a bounded
+sample of the same workload, timed on this host).
+
+  python bench.py [--steps K] [--warmup W] [--config v3_prefill|v3_decode|v3_fp8|v3_skew|tiny]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0                          # MI355X HBM3E
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp32": 157.3}
+STAGES = ("router", "dispatch", "ffn_gate_up", "ffn_down", "combine")
+
+
+def esz(dtype):
+    return {"fp32": 4, "bf16": 2, "fp8": 1}[dtype]
+
+
+def algorithmic(cfg, n_touched):
+    """Algorithmic FLOPs and HBM bytes per launch of the two expert kernels:
+    every weight of a touched expert read once, activations in and H / y out
+    once (no padding rows, no re-reads)."""
+    T, d, I, K, Ns = cfg.T, cfg.d, cfg.I, cfg.K, cfg.Ns
+    rows = T * K + T * Ns
+    wsz = esz(cfg.dtype)
+    act = 2 if cfg.dtype != "fp32" else 4
+    hsz = 1 if cfg.dtype == "fp8" else act
+    sc = 4.0 / (128 * 128) if cfg.dtype == "fp8" else 0.0           # block scales per weight
+    asc = 4.0 / 128 if cfg.dtype == "fp8" else 0.0                   # tile scales per activation
+    xin = T * d * (1 + asc) if cfg.dtype == "fp8" else T * d * act   # u (or its e4m3 copy) read once
+    experts = n_touched + Ns
+    gu_bytes = experts * 2 * I * d * (wsz + sc) + xin + rows * I * (hsz + asc)
+    dn_bytes = experts * I * d * (wsz + sc) + rows * I * (hsz + asc) + rows * d * act
+    return dict(ffn_gate_up=(rows * 4.0 * I * d, gu_bytes), ffn_down=(rows * 2.0 * I * d, dn_bytes))
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for f in ("ffn.hip", "common.h", "internal.h"):
+        with open(os.path.join(ROOT, "mixture_experts_layer_35_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(cfg, kernel, n_launch_bytes):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC summary,
+    or None when there is none for this workload or the kernel source changed."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_pmc.md" % (kernel, cfg.name))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not t or m.group(1) != source_hash():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(cfg, inp, n_tokens):
+    import numpy as np
+    import oracle
+    wcode = {"fp32": oracle.F32, "bf16": oracle.BF16, "fp8": oracle.E4M3}[cfg.dtype]
+    ocode = oracle.F32 if cfg.dtype == "fp32" else oracle.BF16
+    tokens = np.arange(min(n_tokens, cfg.T))
+    routed = (inp["wg"], inp["wu"], inp["wd"])
+    shared = (inp["swg"], inp["swu"], inp["swd"]) if cfg.Ns else None
+    rs = ss = None
+    t0 = time.perf_counter()
+    if cfg.dtype == "fp8":
+        # the oracle quantises only the weights this sample touches
+        _, idx, _ = oracle.route(inp["u"], inp["gate_w"], inp["bias"], G=cfg.G, Mg=cfg.Mg, K=cfg.K, tokens=tokens)
+        need = np.unique(idx)
+        qs, ssc = [], []
+        for w in routed:
+            q = np.zeros(w.shape, np.uint8)
+            s = np.ones((w.shape[0], w.shape[1] // 128, w.shape[2] // 128), np.float32)
+            q[need], s[need] = oracle.quant_128x128(w[need])
+            qs.append(q)
+            ssc.append(s)
+        routed, rs = tuple(qs), tuple(ssc)
+        if shared is not None:
+            pairs = [oracle.quant_128x128(w) for w in shared]
+            shared, ss = tuple(p[0] for p in pairs), tuple(p[1] for p in pairs)
+    oracle.moe_forward(inp["u"], inp["gate_w"], inp["bias"], routed, shared, G=cfg.G, Mg=cfg.Mg, K=cfg.K,
+                       w_code=wcode, out_code=ocode, tokens=tokens, routed_scales=rs, shared_scales=ss)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(tokens) / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "first %d tokens of the same %d-token batch: routing, %d routed + %d shared SwiGLU experts "
+                      "each, combine (fp64 sums)%s; %.1f s" % (len(tokens), cfg.T, cfg.K, cfg.Ns,
+                                                               ", weight quantisation of touched experts"
+                                                               if cfg.dtype == "fp8" else "", dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="v3_prefill")
+    ap.add_argument("--cpu-tokens", type=int, default=96, help="tokens in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (reference kernel for HBM counter scaling)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the layer on a single GPU only (expert-parallel sharding across GPUs is "
+              "not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_synth as syn
+    import mixture_experts_layer_35_amd as moe
+    from mixture_experts_layer_35_amd.layer import MoeLayer, to_device
+
+    cfg = syn.CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    moe.lib()
+    t_gen = time.perf_counter()
+    inp = syn.layer_inputs(cfg)
+    t_gen = time.perf_counter() - t_gen
+    print("# inputs generated in %.1f s" % t_gen, file=sys.stderr, flush=True)
+    shape = moe.make_shape(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.G, cfg.Mg, cfg.K, cfg.I, cfg.dtype)
+    layer = MoeLayer.from_host(shape, inp["gate_w"], inp["bias"], inp["wg"], inp["wu"], inp["wd"], inp["swg"],
+                               inp["swu"], inp["swd"])
+    u = to_device(inp["u"])
+    T = cfg.T
+    out = torch.empty((T, cfg.d), dtype=u.dtype, device="cuda")
+    counts = torch.empty(cfg.Nr, dtype=torch.int32, device="cuda")
+    ws = layer.workspace(T)
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        moe.moe_forward_timed(shape, u, layer.gate_w, layer.bias, layer.routed_w, layer.routed_s, layer.shared_w,
+                              layer.shared_s, out, None, None, counts, None, ws, stream, events)
+
+    for _ in range(args.warmup):
+        step()
+    # events: created and recorded once so that their handles exist
+    evs = []
+    for _ in range(args.steps):
+        row = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        for e in row:
+            e.record()
+        evs.append(row)
+    torch.cuda.synchronize()
+    handles = [[e.cuda_event for e in row] for row in evs]
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(handles[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1000.0 / args.steps
+    stage_ms = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
+                for i, name in enumerate(STAGES)}
+
+    n_touched = int((counts.cpu().numpy() > 0).sum())
+    alg = algorithmic(cfg, n_touched)
+    dom = max(("ffn_gate_up", "ffn_down"), key=lambda k: stage_ms[k])
+    flops, nbytes = alg[dom]
+    t_dom = stage_ms[dom] / 1000.0
+    peak_f = PEAK_TFLOPS[cfg.dtype]
+    ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if flops / nbytes < ridge:
+        roof = {"bound": "hbm", "achieved": round(nbytes / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    else:
+        roof = {"bound": "mfma", "achieved": round(flops / t_dom / 1e12, 1), "peak": peak_f, "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    tr = traffic_from_profile(cfg, dom, nbytes)
+    roof["traffic"] = tr
+    roof["kernel"] = dom
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_flops"] = flops
+    roof["kernel_ms"] = round(stage_ms[dom], 4)
+
+    layer_flops = T * cfg.flops_per_token
+    tflops = layer_flops / (ms / 1000.0) / 1e12
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    cpu = None
+    if args.cpu_tokens > 0:
+        cpu = cpu_baseline(cfg, inp, args.cpu_tokens)
+
+    wl = ("%s: DeepSeekMoE layer forward, T=%d tokens, d=%d, %d routed + %d shared SwiGLU experts (I=%d), "
+          "%d groups / top-%d groups / top-%d experts, %s" % (cfg.name, T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.G, cfg.Mg,
+                                                           cfg.K, {"bf16": "bf16 storage, fp32 accumulation",
+                                                                   "fp8": "e4m3 expert GEMMs (1x128 / 128x128 fp32 "
+                                                                          "scales), bf16 in/out",
+                                                                   "fp32": "fp32"}[cfg.dtype]))
+    line = {
+        "metric": "MoE layer tokens/s + achieved TFLOP/s (% MFMA peak), V3 shape bf16/fp8",
+        "value": round(T / (ms / 1000.0), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "fp8": "fp8e4m3", "fp32": "f32"}[cfg.dtype],
+        "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights; no trained weights)",
+        "config": {"workload": wl, "T": T, "d": cfg.d, "n_routed": cfg.Nr, "n_shared": cfg.Ns, "topk": cfg.K,
+                   "n_groups": cfg.G, "topk_groups": cfg.Mg, "inter": cfg.I, "parallelism": "single GPU"},
+        "tflops": round(tflops, 2),
+        "mfma_peak_frac": round(tflops / peak_f, 4),
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "experts_touched": n_touched,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -194,6 +194,23 @@ int moe_forward(const moe_shape *shape, const void *u, const void *gate_w, const
                 void *out, int32_t *topk_idx_out, float *topk_w_out, int32_t *counts_out,
                 float *scores_out, void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * moe_forward_timed -- moe_forward that also records caller-created HIP
+ * events (hipEvent_t) on `stream` at its stage boundaries, for per-kernel
+ * timing without a profiler:
+ *   stage_events[0] before the router        [1] after routing (affinities + selection)
+ *   [2] after dispatch (and e4m3 quantisation of u)
+ *   [3] after the gate/up expert kernel      [4] after the down expert kernel
+ *   [5] after the combine
+ * NULL entries (or a NULL array, 6 entries otherwise) are skipped.  The array
+ * itself is host memory.  Results are identical to moe_forward.
+ */
+int moe_forward_timed(const moe_shape *shape, const void *u, const void *gate_w, const float *bias,
+                      const void *const *routed_w, const float *const *routed_s,
+                      const void *const *shared_w, const float *const *shared_s,
+                      void *out, int32_t *topk_idx_out, float *topk_w_out, int32_t *counts_out,
+                      float *scores_out, void *ws, size_t ws_bytes, void *stream, void *const *stage_events);
+
 /* ------------------------------------------------------------------------ */
 /* helpers                                                                  */
 

@@ -24,7 +24,8 @@ MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_ADD_RESIDUAL = 1
 MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_FORWARD = 0, 1, 2
 
-EXPORTED = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_workspace_bytes",
+EXPORTED = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_timed",
+            "moe_workspace_bytes",
             "moe_ffn_workspace_bytes", "moe_bias_update", "moe_quantize_1x128", "moe_quantize_weights_128x128",
             "moe_last_error", "moe_version")
 
@@ -75,6 +76,7 @@ def lib():
                 "moe_grouped_ffn": [S, i32, P, i64, P, P, P, P, P, P, P, P, P, sz, P],
                 "moe_combine": [S, P, P, P, P, P, P, P],
                 "moe_forward": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P],
+                "moe_forward_timed": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P, P],
                 "moe_bias_update": [S, P, P, ctypes.c_float, P],
                 "moe_quantize_1x128": [i64, i32, i32, P, P, P, P],
                 "moe_quantize_weights_128x128": [i64, i32, i32, i32, P, P, P, P],
@@ -194,6 +196,21 @@ def moe_forward(shape, u, gate_w, bias, routed_w, routed_s, shared_w, shared_s, 
                                     rs[0] if rs else None, sw[0] if sw else None, ss[0] if ss else None, _ptr(out),
                                     _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(counts_out), _ptr(scores_out),
                                     _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_forward_timed(shape, u, gate_w, bias, routed_w, routed_s, shared_w, shared_s, out, topk_idx_out=None,
+                      topk_w_out=None, counts_out=None, scores_out=None, ws=None, stream=None, stage_events=None):
+    """stage_events: 6 raw hipEvent_t handles (ints) or None."""
+    rw, rs, sw, ss = (_ptr_array(x) for x in (routed_w, routed_s, shared_w, shared_s))
+    ev = None
+    if stage_events is not None:
+        arr = (ctypes.c_void_p * 6)(*stage_events)
+        ev = ctypes.cast(arr, ctypes.c_void_p)
+    return _check(lib().moe_forward_timed(ctypes.byref(shape), _ptr(u), _ptr(gate_w), _ptr(bias),
+                                          rw[0] if rw else None, rs[0] if rs else None, sw[0] if sw else None,
+                                          ss[0] if ss else None, _ptr(out), _ptr(topk_idx_out), _ptr(topk_w_out),
+                                          _ptr(counts_out), _ptr(scores_out), _ptr(ws), _nbytes(ws),
+                                          _stream(stream), ev))
 
 
 def moe_bias_update(shape, counts, bias, gamma, stream=None):

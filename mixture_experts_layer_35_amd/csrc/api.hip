@@ -326,6 +326,15 @@ int moe_forward(const moe_shape *s, const void *u, const void *gate_w, const flo
                 const void *const *routed_w, const float *const *routed_s, const void *const *shared_w,
                 const float *const *shared_s, void *out, int32_t *topk_idx_out, float *topk_w_out,
                 int32_t *counts_out, float *scores_out, void *ws, size_t ws_bytes, void *stream) {
+    return moe_forward_timed(s, u, gate_w, bias, routed_w, routed_s, shared_w, shared_s, out, topk_idx_out,
+                             topk_w_out, counts_out, scores_out, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, const float *bias,
+                      const void *const *routed_w, const float *const *routed_s, const void *const *shared_w,
+                      const float *const *shared_s, void *out, int32_t *topk_idx_out, float *topk_w_out,
+                      int32_t *counts_out, float *scores_out, void *ws, size_t ws_bytes, void *stream,
+                      void *const *ev) {
     const char *fn = "moe_forward";
     int rc = check_shape(s, fn);
     if (rc) return rc;
@@ -369,10 +378,15 @@ int moe_forward(const moe_shape *s, const void *u, const void *gate_w, const flo
     int32_t *perm = (int32_t *)(W + L.perm);
     int32_t *inv = (int32_t *)(W + L.inv);
 
+    auto mark = [&](int i) -> hipError_t {
+        return (ev && ev[i]) ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
+    };
     // 1. affinities and selection
+    HIPCHK(mark(0));
     HIPCHK(launch_router_gemm(dt_of(s->act_dtype), u, gate_w, scores, T, s->d, s->n_routed, st));
     HIPCHK(launch_router_select(scores, bias, T, s->n_routed, s->n_groups, s->topk_groups, s->topk, s->routed_scale,
                                 idx, tw, st));
+    HIPCHK(mark(1));
     // 2. dispatch bookkeeping (rows are gathered inside the expert GEMM)
     HIPCHK(launch_perm_hist(idx, T, s->topk, s->n_routed, bc, st));
     HIPCHK(launch_perm_scan(bc, T, s->n_routed, counts, offsets, st));
@@ -386,6 +400,7 @@ int moe_forward(const moe_shape *s, const void *u, const void *gate_w, const flo
         xin = W + L.uq;
         xs = (const float *)(W + L.us);
     }
+    HIPCHK(mark(2));
     // 4. routed and shared experts
     FfnProblem gu[2] = {}, dn[2] = {};
     gu[0].n_exp = dn[0].n_exp = s->n_routed;
@@ -425,12 +440,25 @@ int moe_forward(const moe_shape *s, const void *u, const void *gate_w, const flo
         dn[1].s0 = fp8 ? shared_s[2] : nullptr;
         dn[1].out = W + L.ysh;
     }
-    rc = run_ffn_pair(s, gu, dn, nprob, st);
-    if (rc) return rc;
+    {
+        FfnArgs a{};
+        a.nprob = nprob;
+        a.K = s->d;
+        a.F = s->inter;
+        for (int i = 0; i < nprob; ++i) a.p[i] = gu[i];
+        HIPCHK(launch_ffn(dt_of(s->w_dtype), true, a, st));
+        HIPCHK(mark(3));
+        a.K = s->inter;
+        a.F = s->d;
+        for (int i = 0; i < nprob; ++i) a.p[i] = dn[i];
+        HIPCHK(launch_ffn(dt_of(s->w_dtype), false, a, st));
+        HIPCHK(mark(4));
+    }
     // 5. gate-weighted combine plus shared experts
     HIPCHK(launch_combine(dt_of(s->out_dtype), dt_of(s->act_dtype), W + L.yperm, inv, tw,
                           s->n_shared ? W + L.ysh : nullptr, s->n_shared,
                           (s->flags & MOE_ADD_RESIDUAL) ? u : nullptr, out, T, s->d, s->topk, st));
+    HIPCHK(mark(5));
     (void)TK;
     return MOE_OK;
 }
