@@ -61,38 +61,43 @@ struct FTraits<DT_E4M3> {
     }
 };
 
-// XOR swizzle of the eight 16-byte chunks of a staged 128-byte row.  Lanes
-// 0-15 of a fragment read take one chunk column of 16 consecutive rows; with
-// this permutation those land in distinct banks whether the LDS serves 8 or
-// 16 such reads per cycle.
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+// Staged rows hold CB bytes of the reduction dimension (128: one e4m3 MFMA
+// step, two bf16 steps, eight fp32 steps), as CB/16 chunks of 16 bytes in
+// XOR-permuted slots.  Lanes 0-15 of a fragment read take one chunk
+// column of 16 consecutive rows; the permutations put those reads in distinct
+// banks whether the LDS serves 8 or 16 such reads per cycle.
+template <int CB>
+__device__ __forceinline__ int swz(int row) {
+    if (CB == 128) return (row & 7) ^ ((row >> 3) & 1);
+    return ((row >> 1) ^ (row >> 3)) & 3;
+}
 
 template <int DT>
 struct Frag;
 template <>
 struct Frag<DT_F32> {
-    static constexpr int kSub = 8;   // 16x16x4 steps per 128-byte row
+    static constexpr int CB = 128, kSub = 8;  // 16x16x4 steps per 128-byte row
     typedef float t;
     __device__ static t load(const char *stage, int row, int s, int lane) {
-        return *(const float *)(stage + row * 128 + ((s ^ swz(row)) << 4) + (lane >> 4) * 4);
+        return *(const float *)(stage + row * CB + ((s ^ swz<CB>(row)) << 4) + (lane >> 4) * 4);
     }
 };
 template <>
 struct Frag<DT_BF16> {
-    static constexpr int kSub = 2;   // 16x16x32 steps per 128-byte row
+    static constexpr int CB = 128, kSub = 2;  // 16x16x32 steps per 128-byte row
     typedef bf16x8 t;
     __device__ static t load(const char *stage, int row, int s, int lane) {
-        return *(const bf16x8 *)(stage + row * 128 + (((s * 4 + (lane >> 4)) ^ swz(row)) << 4));
+        return *(const bf16x8 *)(stage + row * CB + (((s * 4 + (lane >> 4)) ^ swz<CB>(row)) << 4));
     }
 };
 template <>
 struct Frag<DT_E4M3> {
-    static constexpr int kSub = 1;   // one 16x16x128 step per 128-byte row
+    static constexpr int CB = 128, kSub = 1;  // one 16x16x128 step per 128-byte row
     typedef i32x8 t;
     __device__ static t load(const char *stage, int row, int s, int lane) {
         const int c = 2 * (lane >> 4);
-        const i32x4 lo = *(const i32x4 *)(stage + row * 128 + ((c ^ swz(row)) << 4));
-        const i32x4 hi = *(const i32x4 *)(stage + row * 128 + (((c + 1) ^ swz(row)) << 4));
+        const i32x4 lo = *(const i32x4 *)(stage + row * CB + ((c ^ swz<CB>(row)) << 4));
+        const i32x4 hi = *(const i32x4 *)(stage + row * CB + (((c + 1) ^ swz<CB>(row)) << 4));
         return i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
 };
@@ -193,7 +198,6 @@ constexpr int WRW = WR / WF;            // weight rows per wave (64)
 constexpr int RB = WRW / 16;            // 16-row weight blocks per wave (4)
 constexpr int TB = BM / WM / 16;        // 16-token blocks per wave (8)
 constexpr int SCL_BYTES = 2048;         // fp8: per-stage scale area (BM activation + 2 weight scales)
-constexpr int MAX_DMA = (WR + BM) / 8 / NW;   // 16-byte DMA instructions per wave per stage, at most
 constexpr int LDS_TOTAL = 160 * 1024;
 
 // LDS bytes besides the ring: tile prefixes of both problems (n_exp + 1 each).
@@ -254,6 +258,11 @@ __device__ __forceinline__ void compute_step(const char *st, const float *sc, in
 template <int DT, bool GATEUP>
 __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_bytes) {
     constexpr int esz = FTraits<DT>::esz;
+    constexpr int CB = Frag<DT>::CB;              // staged bytes per row per reduction step
+    constexpr int RPI = 1024 / CB;                // rows per 1 KB DMA instruction
+    constexpr int NP = 4;                         // producer waves (issue every load)
+    constexpr int QW = WR / RPI / NP;             // weight DMA instructions per producer per step
+    constexpr int QX = BM / RPI / NP;             // token DMA instructions per producer per step, at most
     constexpr int BF = GATEUP ? WR / 2 : WR;      // output features per tile
     constexpr bool FP8 = DT == DT_E4M3;
     static_assert(!FP8 || !GATEUP || BF == 128, "fp8 H quantisation needs whole 128-feature groups per tile");
@@ -270,8 +279,8 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
     const int K = a.K, F = a.F;
     const int ftiles = (F + BF - 1) / BF;
     const int64_t rowbytes = (int64_t)K * esz;
-    const int KT = (int)(rowbytes / 128);
-    const int kb_per_row = K / 128;               // fp8 scale blocks along K
+    const int KT = (int)(rowbytes / CB);
+    const int kb_per_row = K / 128;               // fp8 scale blocks along K (one per step)
 
     int *pre1 = pre + a.p[0].n_exp + 1;
     tile_prefix<NT>(a.p[0], BM, ftiles, pre, scan);
@@ -299,75 +308,101 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
         const int n0 = nt * BF;
 
         // Stage layout: WR weight rows, then the valid token rows rounded up to
-        // 8, then (fp8) the scales.  The ring holds as many stages as fit.
-        const int trows = (valid + 7) & ~7;
+        // whole DMA instructions, then (fp8) the scales.  The ring holds as many
+        // stages as fit.
+        const int trows = (valid + RPI - 1) / RPI * RPI;
         const int srows = WR + trows;
-        const int stage_bytes = srows * 128 + (FP8 ? SCL_BYTES : 0);
-        // the last slot's token blocks may read up to `over` bytes past the staged rows
-        const int over = ((valid <= BM / 2 ? BM / 2 : BM) - trows) * 128;
+        const int stage_bytes = srows * CB + (FP8 ? SCL_BYTES : 0);
+        // token blocks this tile needs per wave: NTB = ceil(valid / (16*WM)) rounded up to an even
+        // count, so the specialised loops below cover 64, 128, 192 or 256 tokens; the last slot's
+        // blocks may read up to `over` bytes past the staged rows
+        const int ntb = min(TB, ((valid + 16 * WM - 1) / (16 * WM) + 1) & ~1);
+        const int over = max(0, ntb * 16 * WM - trows) * CB;
         const int S = min((ring_bytes - over) / stage_bytes, 8);
-        const int ninstr = srows / 8;             // 16-byte DMA instructions per stage (1 KB each)
 
-        // Global source of each DMA this wave issues per stage.  Instruction i
-        // (issued by wave i % NW) fills staged rows 8i .. 8i+7; lane l covers
-        // row 8i + l/8 and stores into chunk slot l%8, which holds the row's
-        // chunk (l%8) ^ swz(row).  Weight rows past F clamp to F-1.
-        const char *src[MAX_DMA];
-        int nlive = 0;
+        // Loads are issued by the NP producer waves only (one per SIMD), so each
+        // SIMD always has a consumer wave free to run MFMAs while its producer
+        // waits on a full load queue.  Instruction i (issued by producer i % NP)
+        // fills staged rows RPI*i .. RPI*i+RPI-1; lane l covers row
+        // RPI*i + l/(CB/16) and stores into chunk slot l%(CB/16), which holds the
+        // row's chunk slot ^ swz(row).  Weight rows past F clamp to F-1.
+        const bool producer = wid < NP;
+        const int csub = lane / (CB / 16), cslot = lane % (CB / 16);
+        // weight rows: instruction q < QW of this producer covers row RPI*(q*NP+wid) + csub.  The
+        // chunk permutation does not depend on q (RPI*NP rows apart), so one base pointer per
+        // weight matrix plus a per-instruction row stride addresses them all; in a ragged last
+        // tile (F - n0 < WR) the instructions past F re-read the last full instruction's rows.
+        const int wrow0 = RPI * wid + csub;
+        const int wchunk = (cslot ^ swz<CB>(wrow0)) << 4;
+        const char *wbase0 = (const char *)P.w0 + ((int64_t)e * F + n0 + wrow0) * rowbytes + wchunk;
+        const char *wbase1 = GATEUP ? (const char *)P.w1 + ((int64_t)e * F + n0 + wrow0) * rowbytes + wchunk : wbase0;
+        const int qmax = GATEUP ? QW / 2 - 1 : min(QW, (F - n0) / (RPI * NP)) - 1;
+        // token rows: instruction q of this producer covers token RPI*(q*NP+wid) + csub
+        int xrow[QX];
+        int nxq = 0;
 #pragma unroll
-        for (int q = 0; q < MAX_DMA; ++q) {
-            const int ins = q * NW + wid;
-            const int row = 8 * ins + (lane >> 3);
-            const int chunk = (lane & 7) ^ swz(row);
-            const char *ptr;
-            if (row < WR) {
-                const bool up = GATEUP && row >= BF;
-                const char *w = (const char *)(up ? P.w1 : P.w0);
-                const int f = min(n0 + (up ? row - BF : row), F - 1);
-                ptr = w + ((int64_t)e * F + f) * rowbytes;
-            } else {
-                const int r = min(row - WR, valid - 1);
-                const int64_t R = base + r0 + r;
-                const int64_t xr = P.gather ? (int64_t)P.gather[R] : (P.x_local ? (int64_t)(r0 + r) : R);
-                ptr = (const char *)P.x + xr * rowbytes;
-            }
-            src[q] = ptr + chunk * 16;
-            nlive += ins < ninstr ? 1 : 0;
+        for (int q = 0; q < QX; ++q) {
+            const int tr = RPI * (q * NP + wid) + csub;
+            const int r = min(tr, valid - 1);
+            const int64_t R = base + r0 + r;
+            xrow[q] = P.gather ? P.gather[R] : (int)(P.x_local ? (int64_t)(r0 + r) : R);
+            nxq += RPI * (q * NP + wid) < trows ? 1 : 0;
         }
-        // fp8 scales, 4-byte DMAs into the stage's scale area: waves 0..3 stage
+        int nlive = producer ? QW + nxq : 0;
+        // fp8 scales, 4-byte DMAs into the stage's scale area: producer w stages
         // the activation scales of tokens 64w .. 64w+63 (while any is valid);
-        // wave 4 stages the two weight block scales at slots BM, BM+1 (gate/up:
-        // gate and up block; down: first and second 128-row block).
-        const float *ssrc = nullptr;
-        bool sc_live = false;
-        if (FP8) {
-            if (wid < 4) {
-                const int r = min(wid * 64 + lane, valid - 1);
-                const int64_t R = base + r0 + r;
-                const int64_t xr = P.gather ? (int64_t)P.gather[R] : (P.x_local ? (int64_t)(r0 + r) : R);
-                ssrc = P.xs + xr * kb_per_row;
-                sc_live = wid * 64 < valid;
-            } else if (wid == 4) {
-                const int nb = F / 128;
-                if (GATEUP) {
-                    const float *sbase = (lane & 1) ? P.s1 : P.s0;
-                    ssrc = sbase + ((int64_t)e * nb + n0 / 128) * kb_per_row;
-                } else {
-                    const int fb = min(n0 / 128 + (lane & 1), nb - 1);
-                    ssrc = P.s0 + ((int64_t)e * nb + fb) * kb_per_row;
-                }
-                sc_live = true;
+        // producer 0 also stages the two weight block scales at slots BM, BM+1
+        // (gate/up: gate and up block; down: first and second 128-row block).
+        const float *xssrc = nullptr, *wssrc = nullptr;
+        bool xs_live = false;
+        if (FP8 && producer) {
+            const int r = min(wid * 64 + lane, valid - 1);
+            const int64_t R = base + r0 + r;
+            const int64_t xr = P.gather ? (int64_t)P.gather[R] : (P.x_local ? (int64_t)(r0 + r) : R);
+            xssrc = P.xs + xr * kb_per_row;
+            xs_live = wid * 64 < valid;
+            const int nb = F / 128;
+            if (GATEUP) {
+                const float *sbase = (lane & 1) ? P.s1 : P.s0;
+                wssrc = sbase + ((int64_t)e * nb + n0 / 128) * kb_per_row;
+            } else {
+                const int fb = min(n0 / 128 + (lane & 1), nb - 1);
+                wssrc = P.s0 + ((int64_t)e * nb + fb) * kb_per_row;
             }
-            nlive += sc_live ? 1 : 0;
+            nlive += (xs_live ? 1 : 0) + (wid == 0 ? 1 : 0);
         }
+        const char *xbase = (const char *)P.x;
 
         int slot_issue = 0;   // ring slot of the next stage issued
         auto issue = [&](int ks) {
             char *st = ring + slot_issue * stage_bytes;
+            if (producer) {
+                // an opaque copy of the row stride keeps the per-instruction addresses
+                // from being hoisted out of the reduction loop (they would occupy
+                // ~32 VGPRs for the whole tile); recomputing them costs a few SALU/VALU ops
+                int64_t rb = rowbytes;
+                asm volatile("" : "+s"(rb));
 #pragma unroll
-            for (int q = 0; q < MAX_DMA; ++q)
-                if (q * NW + wid < ninstr) dma16(src[q] + (int64_t)ks * 128, st + (q * NW + wid) * 1024);
-            if (FP8 && sc_live) dma4(ssrc + ks, st + srows * 128 + (wid < 4 ? wid * 256 : BM * 4));
+                for (int q = 0; q < QW; ++q) {
+                    // gate/up: instructions q < QW/2 read gate rows, the rest the matching up rows
+                    const bool up = GATEUP && q >= QW / 2;
+                    const int qq = min(GATEUP ? (up ? q - QW / 2 : q) : q, qmax);
+                    const char *src = (up ? wbase1 : wbase0) + (int64_t)qq * (RPI * NP) * rb + (int64_t)ks * CB;
+                    dma16(src, st + (q * NP + wid) * 1024);
+                }
+#pragma unroll
+                for (int q = 0; q < QX; ++q) {
+                    const int ins = q * NP + wid;
+                    if (RPI * ins >= trows) continue;
+                    const int row = WR + RPI * ins + csub;
+                    const char *src = xbase + (int64_t)xrow[q] * rb + (int64_t)ks * CB + ((cslot ^ swz<CB>(row)) << 4);
+                    dma16(src, st + (WR / RPI + ins) * 1024);
+                }
+                if (FP8) {
+                    if (xs_live) dma4(xssrc + ks, st + srows * CB + wid * 256);
+                    if (wid == 0) dma4(wssrc + ks, st + srows * CB + BM * 4);
+                }
+            }
             slot_issue = slot_issue + 1 == S ? 0 : slot_issue + 1;
         };
 
@@ -387,17 +422,21 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
             int slot = 0;
             for (int kt = 0; kt < KT; ++kt) {
                 // step kt has landed once at most the later steps' loads are outstanding
-                if (kt + S - 2 < KT) wait_vmcnt_dyn(nlive * (S - 2));
-                else wait_vmcnt<0>();
+                if (producer) {
+                    if (kt + S - 2 < KT) wait_vmcnt_dyn(nlive * (S - 2));
+                    else wait_vmcnt<0>();
+                }
                 cta_barrier();
                 if (kt + S - 1 < KT) issue(kt + S - 1);
                 const char *st = ring + slot * stage_bytes;
-                const float *sc = (const float *)(st + srows * 128);
+                const float *sc = (const float *)(st + srows * CB);
                 compute_step<DT, GATEUP, NTB>(st, sc, trows, acc, wm, wf, lane);
                 slot = slot + 1 == S ? 0 : slot + 1;
             }
         };
-        if (valid <= BM / 2) kloop(std::integral_constant<int, TB / 2>{});
+        if (ntb == 2) kloop(std::integral_constant<int, 2>{});
+        else if (ntb == 4) kloop(std::integral_constant<int, 4>{});
+        else if (ntb == 6) kloop(std::integral_constant<int, 6>{});
         else kloop(std::integral_constant<int, TB>{});
 
         // ---- epilogue ----
@@ -495,11 +534,9 @@ hipError_t run(const FfnArgs &a, hipStream_t s) {
     if (attr_err != hipSuccess) return attr_err;
     const int pb = prefix_bytes(a.p[0].n_exp, a.nprob > 1 ? a.p[1].n_exp : 0);
     const int ring = LDS_TOTAL - pb;
-    // the ring must hold two full stages (256 weight rows + 256 token rows + scales) plus the
-    // largest read past the last slot, (BM - BM/2 - 8) rows for a tile just over half full
-    if (ring < 2 * ((WR + BM) * 128 + (DT == DT_E4M3 ? SCL_BYTES : 0)) ||
-        ring < 2 * ((WR + BM / 2 + 8) * 128 + (DT == DT_E4M3 ? SCL_BYTES : 0)) + (BM / 2 - 8) * 128)
-        return hipErrorInvalidValue;
+    // the ring must hold two stages of any tile plus its read past the last slot (at most 56 rows)
+    constexpr int CB = Frag<DT>::CB;
+    if (ring < 2 * ((WR + BM) * CB + (DT == DT_E4M3 ? SCL_BYTES : 0)) + 56 * CB) return hipErrorInvalidValue;
     int grid = device_cus();
     grid = (grid + 7) / 8 * 8;
     ffn_kernel<DT, GATEUP><<<grid, NT, LDS_TOTAL, s>>>(a, ring);
