@@ -14,7 +14,6 @@ sample of the same workload, timed on this host).
   python bench.py [--steps K] [--warmup W] [--config v3_prefill|v3_decode|v3_fp8|v3_skew|tiny]
 """
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -51,23 +50,48 @@ def algorithmic(cfg, n_touched):
     return dict(ffn_gate_up=(rows * 4.0 * I * d, gu_bytes), ffn_down=(rows * 2.0 * I * d, dn_bytes))
 
 
-def source_hash():
-    h = hashlib.sha256()
-    for f in ("ffn.hip", "common.h", "internal.h"):
-        with open(os.path.join(ROOT, "mixture_experts_layer_35_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
+def stage_bytes(cfg):
+    """Algorithmic HBM bytes of the three memory-bound stages (each operand
+    read or written once): the router reads u and the centroids and writes
+    the top-k indices and weights; dispatch reads the indices twice (histogram
+    and scatter) and writes the permutation (and, for e4m3, reads u once and
+    writes its 1x128-quantised copy); combine reads every expert output row,
+    the shared output, the inverse permutation and gate weights, and writes
+    the layer output."""
+    T, d, K, Nr, Ns = cfg.T, cfg.d, cfg.K, cfg.Nr, cfg.Ns
+    act = 4 if cfg.dtype == "fp32" else 2
+    router = T * d * act + Nr * d * act + T * K * 8
+    dispatch = T * K * 4 * 2 + T * K * 8 + Nr * 8
+    if cfg.dtype == "fp8":
+        dispatch += T * d * act + T * d * (1 + 4.0 / 128)
+    combine = T * K * d * act + Ns * T * d * act + T * K * 8 + T * d * act
+    return dict(router=router, dispatch=dispatch, combine=combine)
 
 
-def traffic_from_profile(cfg, kernel, n_launch_bytes):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 PMC summary,
-    or None when there is none for this workload or the kernel source changed."""
-    path = os.path.join(ROOT, "profiles", "%s_%s_pmc.md" % (kernel, cfg.name))
+def profile_path(cfg):
+    return os.path.join(ROOT, "profiles", "moe_forward_%s_pmc.md" % cfg.name)
+
+
+STAGE_KERNELS = {"router": ("router_gemm_kernel", "router_select_kernel"),
+                 "dispatch": ("perm_hist_kernel", "perm_scan_kernel", "perm_scatter_kernel", "quant_rows_kernel"),
+                 "combine": ("combine_kernel",)}
+
+
+def traffic_from_profile(cfg, kernel):
+    """HBM bytes per launch of `kernel` (a name or a tuple of names, summed)
+    from the committed rocprofv3 PMC summary, or None when there is none for
+    this workload or the kernel sources changed since it was taken."""
+    if isinstance(kernel, tuple):
+        parts = [traffic_from_profile(cfg, k) for k in kernel]
+        parts = [p for p in parts if p is not None]
+        return sum(parts) if parts else None
+    from mixture_experts_layer_35_amd.profsum import source_hash
+    path = profile_path(cfg)
     if not os.path.exists(path):
         return None
     text = open(path).read()
     m = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
-    t = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    t = re.search(r"hbm_bytes_per_launch\[%s\]:\s*([0-9.eE+]+)" % re.escape(kernel), text)
     if not m or not t or m.group(1) != source_hash():
         return None
     return float(t.group(1))
@@ -82,9 +106,9 @@ def cpu_baseline(cfg, inp, n_tokens):
     routed = (inp["wg"], inp["wu"], inp["wd"])
     shared = (inp["swg"], inp["swu"], inp["swd"]) if cfg.Ns else None
     rs = ss = None
-    t0 = time.perf_counter()
     if cfg.dtype == "fp8":
-        # the oracle quantises only the weights this sample touches
+        # weights are quantised once before timing, as on the GPU; only the
+        # experts this sample touches
         _, idx, _ = oracle.route(inp["u"], inp["gate_w"], inp["bias"], G=cfg.G, Mg=cfg.Mg, K=cfg.K, tokens=tokens)
         need = np.unique(idx)
         qs, ssc = [], []
@@ -98,14 +122,16 @@ def cpu_baseline(cfg, inp, n_tokens):
         if shared is not None:
             pairs = [oracle.quant_128x128(w) for w in shared]
             shared, ss = tuple(p[0] for p in pairs), tuple(p[1] for p in pairs)
+    t0 = time.perf_counter()
     oracle.moe_forward(inp["u"], inp["gate_w"], inp["bias"], routed, shared, G=cfg.G, Mg=cfg.Mg, K=cfg.K,
                        w_code=wcode, out_code=ocode, tokens=tokens, routed_scales=rs, shared_scales=ss)
     dt = time.perf_counter() - t0
     return {"value": round(len(tokens) / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "first %d tokens of the same %d-token batch: routing, %d routed + %d shared SwiGLU experts "
                       "each, combine (fp64 sums)%s; %.1f s" % (len(tokens), cfg.T, cfg.K, cfg.Ns,
-                                                               ", weight quantisation of touched experts"
-                                                               if cfg.dtype == "fp8" else "", dt)}
+                                                               ", activation and H quantisation (weights "
+                                                               "pre-quantised)" if cfg.dtype == "fp8" else "",
+                                                               dt)}
 
 
 def main():
@@ -114,7 +140,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="v3_prefill")
-    ap.add_argument("--cpu-tokens", type=int, default=96, help="tokens in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-tokens", type=int, default=640, help="tokens in the CPU-oracle sample (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counter scaling)")
     args = ap.parse_args()
@@ -186,13 +212,19 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(flops / t_dom / 1e12, 1), "peak": peak_f, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    tr = traffic_from_profile(cfg, dom, nbytes)
+    tr = traffic_from_profile(cfg, dom)
     roof["traffic"] = tr
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
     roof["kernel_ms"] = round(stage_ms[dom], 4)
 
+    hbm_stages = {}
+    for name, nb in stage_bytes(cfg).items():
+        gbs = nb / (stage_ms[name] / 1000.0) / 1e9
+        hbm_stages[name] = {"algorithmic_bytes": int(nb), "ms": round(stage_ms[name], 4), "GB/s": round(gbs, 1),
+                            "frac": round(gbs / PEAK_HBM_GBS, 4),
+                            "traffic": traffic_from_profile(cfg, STAGE_KERNELS[name])}
     layer_flops = T * cfg.flops_per_token
     tflops = layer_flops / (ms / 1000.0) / 1e12
     if args.copy_calibration:
@@ -232,6 +264,7 @@ def main():
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "experts_touched": n_touched,
         "roofline": roof,
+        "hbm_stages": hbm_stages,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
