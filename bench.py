@@ -137,7 +137,8 @@ def cpu_baseline(cfg, inp, n_tokens):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20; 10 for v3_skew, whose run is 10 bias-update steps)")
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="v3_prefill")
     ap.add_argument("--cpu-tokens", type=int, default=640, help="tokens in the CPU-oracle sample (0: skip)")
@@ -158,6 +159,8 @@ def main():
     from mixture_experts_layer_35_amd.layer import MoeLayer, to_device
 
     cfg = syn.CONFIGS[args.config]
+    if args.steps is None:
+        args.steps = syn.SKEW_STEPS if cfg.skew else 20
     torch.cuda.set_device(0)
     moe.lib()
     t_gen = time.perf_counter()
@@ -167,19 +170,30 @@ def main():
     shape = moe.make_shape(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.G, cfg.Mg, cfg.K, cfg.I, cfg.dtype)
     layer = MoeLayer.from_host(shape, inp["gate_w"], inp["bias"], inp["wg"], inp["wu"], inp["wd"], inp["swg"],
                                inp["swu"], inp["swd"])
-    u = to_device(inp["u"])
     T = cfg.T
-    out = torch.empty((T, cfg.d), dtype=u.dtype, device="cuda")
-    counts = torch.empty(cfg.Nr, dtype=torch.int32, device="cuda")
+    if cfg.skew:
+        # the skewed-load run: step s routes batch s (seed 1000 + s) and then
+        # moves the selection bias against that step's expert loads
+        batches = [syn.hidden(cfg, seed=syn.SKEW_STEP_SEED + s) for s in range(syn.SKEW_STEPS)]
+        inp["u"] = batches[0]
+        us = [to_device(b) for b in batches]
+    else:
+        us = [to_device(inp["u"])]
+    out = torch.empty((T, cfg.d), dtype=us[0].dtype, device="cuda")
+    counts = torch.zeros((max(args.steps, 1), cfg.Nr), dtype=torch.int32, device="cuda")
     ws = layer.workspace(T)
     stream = torch.cuda.current_stream()
+    bias0 = layer.bias.clone()
 
-    def step(events=None):
-        moe.moe_forward_timed(shape, u, layer.gate_w, layer.bias, layer.routed_w, layer.routed_s, layer.shared_w,
-                              layer.shared_s, out, None, None, counts, None, ws, stream, events)
+    def step(k, events=None):
+        moe.moe_forward_timed(shape, us[k % len(us)], layer.gate_w, layer.bias, layer.routed_w, layer.routed_s,
+                              layer.shared_w, layer.shared_s, out, None, None, counts[k], None, ws, stream, events)
+        if cfg.skew:
+            moe.moe_bias_update(shape, counts[k], layer.bias, syn.SKEW_GAMMA, stream)
 
     for _ in range(args.warmup):
-        step()
+        step(0)
+    layer.bias.copy_(bias0)
     # events: created and recorded once so that their handles exist
     evs = []
     for _ in range(args.steps):
@@ -193,14 +207,23 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(handles[k])
+        step(k, handles[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1000.0 / args.steps
     stage_ms = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
                 for i, name in enumerate(STAGES)}
 
-    n_touched = int((counts.cpu().numpy() > 0).sum())
+    cnt = counts.cpu().numpy()
+    n_touched = int(np.mean([(c > 0).sum() for c in cnt]))
+    skew = None
+    if cfg.skew:
+        mean = T * cfg.K / cfg.Nr
+        skew = {"gamma": syn.SKEW_GAMMA, "step_seeds": "u of step s drawn with seed %d + s" % syn.SKEW_STEP_SEED,
+                "max_over_mean": [round(float(c.max() / mean), 3) for c in cnt],
+                "min_over_mean": [round(float(c.min() / mean), 3) for c in cnt],
+                "step_ms": [round(float(evs[k][0].elapsed_time(evs[k][5])), 4) for k in range(args.steps)],
+                "bias_range_after": [round(float(layer.bias.min()), 4), round(float(layer.bias.max()), 4)]}
     alg = algorithmic(cfg, n_touched)
     dom = max(("ffn_gate_up", "ffn_down"), key=lambda k: stage_ms[k])
     flops, nbytes = alg[dom]
@@ -265,6 +288,7 @@ def main():
         "experts_touched": n_touched,
         "roofline": roof,
         "hbm_stages": hbm_stages,
+        "skew": skew,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

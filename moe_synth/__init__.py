@@ -11,6 +11,10 @@ weights and the training corpus are not available, so normal draws stand in):
   * W_gate, W_up ~ N(0, 1/d)           [n, I, d]   (fan_in = d)
   * W_down ~ N(0, 1/I)                 [n, d, I]   (fan_in = I)
   * bias: zeros, or U(-0.1, 0.1) for the tiny fp32 layer
+  * skewed-load layer: centroid row i scaled by a calibrated sigma_i so that
+    expert popularity follows a flattened Zipf(1.2) whose hottest expert gets
+    8x the mean load (calibrate_skew.py); step s of its bias-update run
+    draws u with seed 1000 + s
 Every tensor (and every expert's matrix) has its own numpy PCG64 stream seeded
 by the tuple (seed, tag, index); draws are float32 and are rounded to nearest
 even into bf16 when the layer stores bf16.  bf16 arrays are returned as uint16
@@ -106,10 +110,15 @@ def default_threads() -> int:
     return max(1, min(16, n))
 
 
+SKEW_STEP_SEED = 1000
+SKEW_STEPS = 10
+SKEW_GAMMA = 0.001
+
+
 def skew_sigma(cfg: LayerConfig) -> np.ndarray:
     """Per-expert row scales of the centroids that make expert popularity
-    follow the skewed target of the skewed-load workload (calibrated once,
-    see calibrate_skew.py)."""
+    follow the skewed target of the skewed-load workload (calibrated once by
+    calibrate_skew.py and stored in skew_sigma.json)."""
     with open(os.path.join(_HERE, "skew_sigma.json")) as f:
         table = json.load(f)
     assert table["Nr"] == cfg.Nr and table["d"] == cfg.d
@@ -127,12 +136,14 @@ def hidden(cfg: LayerConfig, seed=None, T=None):
     return normal((T, cfg.d), 1.0, seed, TAG_U, 0, store_of(cfg))
 
 
-def router_params(cfg: LayerConfig, seed=None):
-    """(gate_w [Nr, d], bias [Nr] fp32)."""
+def router_params(cfg: LayerConfig, seed=None, sigma=None):
+    """(gate_w [Nr, d], bias [Nr] fp32).  For the skewed-load workload each
+    centroid row i is scaled by sigma[i] (the calibrated table unless
+    `sigma` is given) before rounding to the storage format."""
     seed = cfg.seed if seed is None else seed
     g = normal((cfg.Nr, cfg.d), 1.0 / np.sqrt(cfg.d), seed, TAG_GATE, 0, "fp32")
-    if cfg.skew:
-        g *= skew_sigma(cfg)[:, None]
+    if cfg.skew or sigma is not None:
+        g *= (skew_sigma(cfg) if sigma is None else np.asarray(sigma, np.float32))[:, None]
     if store_of(cfg) == "bf16":
         g = to_bf16_bits(g)
     if cfg.bias == "uniform":
