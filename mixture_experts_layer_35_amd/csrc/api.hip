@@ -445,12 +445,14 @@ int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, con
         a.nprob = nprob;
         a.K = s->d;
         a.F = s->inter;
-        for (int i = 0; i < nprob; ++i) a.p[i] = gu[i];
+        // the shared experts' tiles go first: every workgroup starts at the same time, so the
+        // row blocks of one shared weight block run together and share it through L2
+        for (int i = 0; i < nprob; ++i) a.p[i] = gu[nprob - 1 - i];
         HIPCHK(launch_ffn(dt_of(s->w_dtype), true, a, st));
         HIPCHK(mark(3));
         a.K = s->inter;
         a.F = s->d;
-        for (int i = 0; i < nprob; ++i) a.p[i] = dn[i];
+        for (int i = 0; i < nprob; ++i) a.p[i] = dn[nprob - 1 - i];
         HIPCHK(launch_ffn(dt_of(s->w_dtype), false, a, st));
         HIPCHK(mark(4));
     }

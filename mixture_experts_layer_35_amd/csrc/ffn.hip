@@ -13,16 +13,19 @@
 // 256 weight rows, block of up to 256 tokens); row blocks of one (expert,
 // weight block) are adjacent in the list and consecutive tiles run on one XCD,
 // so a weight tile shared by several row blocks is fetched once into that
-// XCD's L2.  Up to two problems (routed and shared experts) share a launch.
+// XCD's L2.  Up to two problems (e.g. shared and routed experts) share a launch.
 //
 // Data movement.  The reduction dimension is walked in 128-byte steps.  Each
 // step's weight rows and token rows are copied from global memory straight
 // into an LDS ring by global_load_lds (no register staging), 16 bytes per lane,
-// into XOR-swizzled rows.  Only the tile's valid token rows are staged, so the
-// ring depth is chosen per tile from the LDS that the stage size leaves: three
-// steps deep for a typical expert.  Loads complete in order, so each wave waits
-// with an exact vmcnt for its own loads of the step it consumes, then the
-// workgroup meets at a fence-free barrier.
+// into XOR-swizzled rows.  Four producer waves (one per SIMD) issue all loads;
+// each waits with an exact vmcnt for its own loads of the step about to be
+// consumed, then the workgroup meets at a fence-free barrier.  The ring depth
+// is chosen per tile: a tile stages only its valid token rows when that leaves
+// three or more slots, and loads a whole step ahead right after the barrier;
+// otherwise (large token blocks, two slots) it stages whole 32-token blocks and
+// spreads each step's loads over the producer's products.  The next tile's
+// first steps are loaded while the current tile's results are written.
 //
 // MFMA orientation: weights are the MFMA row operand and tokens the column
 // operand, so a lane's four accumulators are four consecutive output features
@@ -117,6 +120,9 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// s_waitcnt with only the LDS/scalar counter constrained (lgkmcnt(0)).
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4)); }
+
 // s_waitcnt vmcnt(n) for a wave-uniform n (the immediate is encoded per case;
 // counts above 47 wait for everything, which is only more conservative).
 __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
@@ -204,15 +210,25 @@ constexpr int LDS_TOTAL = 160 * 1024;
 __host__ __device__ inline int prefix_bytes(int n0, int n1) { return ((n0 + 1 + n1 + 1) * 4 + 255) & ~255; }
 
 // One 128-byte reduction step of the tile: products of the wave's RB weight
-// blocks with its first NTB token blocks.
-// Token blocks past the staged rows read whatever follows the stage in the
-// ring (the ring depth leaves room for it); those columns are never stored.
-template <int DT, bool GATEUP, int NTB>
-__device__ __forceinline__ void compute_step(const char *st, const float *sc, int trows, f32x4 (&acc)[RB][TB],
-                                             int wm, int wf, int lane) {
+// blocks with its first NTB token blocks.  A producer wave (PROD) also issues
+// the NDMA loads of a later step, spread over the step's product groups (one
+// group per token block and sub-step): group g issues loads
+// [g*NDMA/NG, (g+1)*NDMA/NG).  A load that has to wait for room in the memory
+// pipeline then stalls the wave between products instead of ahead of them.
+template <int DT, bool GATEUP, int NTB, bool PROD, int NDMA, class Dma>
+__device__ __forceinline__ void compute_step(const char *st, const float *sc, f32x4 (&acc)[RB][TB], int wm, int wf,
+                                             int lane, const Dma &dma) {
     typedef FTraits<DT> Tr;
     typedef Frag<DT> Fr;
     constexpr int BF = GATEUP ? WR / 2 : WR;
+    constexpr int NG = Fr::kSub * NTB;
+    auto group_dma = [&](int g) {
+        if (PROD) {
+#pragma unroll
+            for (int q = g * NDMA / NG; q < (g + 1) * NDMA / NG; ++q) dma(q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
 #pragma unroll
     for (int s = 0; s < Fr::kSub; ++s) {
         typename Fr::t af[RB];
@@ -239,6 +255,7 @@ __device__ __forceinline__ void compute_step(const char *st, const float *sc, in
 #pragma unroll
                     for (int q = 0; q < 4; ++q) acc[i][j][q] += part[q] * cc;
                 }
+                group_dma(s * NTB + j);
             }
         } else {
             typename Fr::t bfr[NTB];
@@ -248,12 +265,19 @@ __device__ __forceinline__ void compute_step(const char *st, const float *sc, in
             // group of products waits only for its own operands
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int j = 0; j < NTB; ++j)
+            for (int j = 0; j < NTB; ++j) {
 #pragma unroll
                 for (int i = 0; i < RB; ++i) acc[i][j] = Tr::mma(af[i], bfr[j], acc[i][j]);
+                group_dma(s * NTB + j);
+            }
         }
     }
 }
+
+// LDS bytes of the fp8 H-quantisation scratch (per-wave row maxima), kept
+// apart from the ring so the next tile's loads can land during the epilogue.
+template <int DT, bool GATEUP>
+__host__ __device__ constexpr int red_bytes() { return (DT == DT_E4M3 && GATEUP) ? WF * BM * 4 : 0; }
 
 template <int DT, bool GATEUP>
 __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_bytes) {
@@ -269,10 +293,11 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
     static_assert(!FP8 || 128 % (GATEUP ? WRW / 2 : WRW) == 0, "fp8: a wave's rows sit in one weight block");
 
     extern __shared__ __align__(1024) char smem[];
+    const int pbytes = prefix_bytes(a.p[0].n_exp, a.nprob > 1 ? a.p[1].n_exp : 0);
     int *pre = (int *)smem;                                            // [n0 + 1] then [n1 + 1]
-    char *ring = smem + prefix_bytes(a.p[0].n_exp, a.nprob > 1 ? a.p[1].n_exp : 0);
+    float *red = (float *)(smem + pbytes);                             // fp8 gate/up: [WF][BM]
+    char *ring = smem + pbytes + red_bytes<DT, GATEUP>();
     int *scan = (int *)ring;                                           // start-up scratch, aliases the ring
-    float *red = (float *)ring;                                        // fp8 epilogue scratch, aliases the ring
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wm = wid % WM, wf = wid / WM;
@@ -288,137 +313,175 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
     const int total0 = pre[a.p[0].n_exp];
     const int total = total0 + (a.nprob > 1 ? pre1[a.p[1].n_exp] : 0);
 
-    // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous run of tiles.
-    const int G = gridDim.x;
-    const int first = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    // Loads are issued by the NP producer waves only (one per SIMD), so each
+    // SIMD always has a consumer wave free to run MFMAs while its producer
+    // waits on a full load queue.  Instruction i (issued by producer i % NP)
+    // fills staged rows RPI*i .. RPI*i+RPI-1; lane l covers row
+    // RPI*i + l/(CB/16) and stores into chunk slot l%(CB/16), which holds the
+    // row's chunk slot ^ swz(row).
+    const bool producer = wid < NP;
+    const int csub = lane / (CB / 16), cslot = lane % (CB / 16);
+    const int wrow0 = RPI * wid + csub;
+    const int wchunk = (cslot ^ swz<CB>(wrow0)) << 4;
 
-    for (int t = first; t < total; t += G) {
-        const int p = t < total0 ? 0 : 1;
-        const FfnProblem P = pick(a, p);
-        const int *ppre = p ? pre1 : pre;
-        const int lt = t - (p ? total0 : 0);
+    // Everything one tile's loads and stores need.
+    struct Tile {
+        int p, valid, r0, n0, ntb, S, stage_bytes, srows, qmax, nextra;
+        int nx;                       // token instructions of this producer per step
+        bool spread;                  // double-buffered: loads spread over the products
+        int64_t base;                 // first row of the tile's expert
+        const char *wbase0, *wbase1;  // this producer's first weight row (gate and up, or down)
+        const float *xssrc, *wssrc;   // fp8 scale sources
+        bool xs_live;
+        int xrow[QX];                 // token rows of this producer's token instructions
+    };
+    auto setup = [&](int t, Tile &T) {
+        T.p = t < total0 ? 0 : 1;
+        const FfnProblem P = pick(a, T.p);
+        const int *ppre = T.p ? pre1 : pre;
+        const int lt = t - (T.p ? total0 : 0);
         const int e = find_expert(ppre, P.n_exp, lt);
-        const int64_t base = P.offsets ? (int64_t)P.offsets[e] : (int64_t)e * P.rows_fixed;
+        T.base = P.offsets ? (int64_t)P.offsets[e] : (int64_t)e * P.rows_fixed;
         const int Me = P.offsets ? P.offsets[e + 1] - P.offsets[e] : (int)P.rows_fixed;
         const int mt = (Me + BM - 1) / BM;
         const int ln = lt - ppre[e];
         const int nt = ln / mt, mi = ln - nt * mt;
-        const int r0 = mi * BM;
-        const int valid = min(BM, Me - r0);
-        const int n0 = nt * BF;
-
-        // Stage layout: WR weight rows, then the valid token rows rounded up to
-        // whole DMA instructions, then (fp8) the scales.  The ring holds as many
-        // stages as fit.
-        const int trows = (valid + RPI - 1) / RPI * RPI;
-        const int srows = WR + trows;
-        const int stage_bytes = srows * CB + (FP8 ? SCL_BYTES : 0);
-        // token blocks this tile needs per wave: NTB = ceil(valid / (16*WM)) rounded up to an even
-        // count, so the specialised loops below cover 64, 128, 192 or 256 tokens; the last slot's
-        // blocks may read up to `over` bytes past the staged rows
-        const int ntb = min(TB, ((valid + 16 * WM - 1) / (16 * WM) + 1) & ~1);
-        const int over = max(0, ntb * 16 * WM - trows) * CB;
-        const int S = min((ring_bytes - over) / stage_bytes, 8);
-
-        // Loads are issued by the NP producer waves only (one per SIMD), so each
-        // SIMD always has a consumer wave free to run MFMAs while its producer
-        // waits on a full load queue.  Instruction i (issued by producer i % NP)
-        // fills staged rows RPI*i .. RPI*i+RPI-1; lane l covers row
-        // RPI*i + l/(CB/16) and stores into chunk slot l%(CB/16), which holds the
-        // row's chunk slot ^ swz(row).  Weight rows past F clamp to F-1.
-        const bool producer = wid < NP;
-        const int csub = lane / (CB / 16), cslot = lane % (CB / 16);
+        T.r0 = mi * BM;
+        T.valid = min(BM, Me - T.r0);
+        T.n0 = nt * BF;
+        // Token blocks this tile needs per wave: NTB = ceil(valid / (16*WM)) rounded up to an
+        // even count, so the specialised loops below cover 64, 128, 192 or 256 tokens.  Stage
+        // layout: WR weight rows, then the token rows, then (fp8) the scales.  Staging only the
+        // valid rows (rounded to whole instructions) keeps stages small; the token blocks then
+        // read up to `over` bytes past the last slot, which the ring keeps free.  When that
+        // still leaves only two slots, the stage holds all 32*NTB token rows instead (rows past
+        // the valid ones repeat the last valid token and are never stored) so that every
+        // producer issues the same loads each step, spread over its products.
+        T.ntb = min(TB, ((T.valid + 16 * WM - 1) / (16 * WM) + 1) & ~1);
+        {
+            const int tmin = (T.valid + RPI - 1) / RPI * RPI, tfull = T.ntb * 16 * WM;
+            const int over = (tfull - tmin) * CB;
+            const int smin = min((ring_bytes - over) / ((WR + tmin) * CB + (FP8 ? SCL_BYTES : 0)), 8);
+            T.spread = smin < 3;
+            const int trows = T.spread ? tfull : tmin;
+            T.srows = WR + trows;
+            T.stage_bytes = T.srows * CB + (FP8 ? SCL_BYTES : 0);
+            T.S = T.spread ? min(ring_bytes / T.stage_bytes, 8) : smin;
+            T.nx = 0;
+#pragma unroll
+            for (int q = 0; q < QX; ++q) T.nx += RPI * (q * NP + wid) < trows ? 1 : 0;
+        }
         // weight rows: instruction q < QW of this producer covers row RPI*(q*NP+wid) + csub.  The
         // chunk permutation does not depend on q (RPI*NP rows apart), so one base pointer per
         // weight matrix plus a per-instruction row stride addresses them all; in a ragged last
         // tile (F - n0 < WR) the instructions past F re-read the last full instruction's rows.
-        const int wrow0 = RPI * wid + csub;
-        const int wchunk = (cslot ^ swz<CB>(wrow0)) << 4;
-        const char *wbase0 = (const char *)P.w0 + ((int64_t)e * F + n0 + wrow0) * rowbytes + wchunk;
-        const char *wbase1 = GATEUP ? (const char *)P.w1 + ((int64_t)e * F + n0 + wrow0) * rowbytes + wchunk : wbase0;
-        const int qmax = GATEUP ? QW / 2 - 1 : min(QW, (F - n0) / (RPI * NP)) - 1;
+        T.wbase0 = (const char *)P.w0 + ((int64_t)e * F + T.n0 + wrow0) * rowbytes + wchunk;
+        T.wbase1 = GATEUP ? (const char *)P.w1 + ((int64_t)e * F + T.n0 + wrow0) * rowbytes + wchunk : T.wbase0;
+        T.qmax = GATEUP ? QW / 2 - 1 : min(QW, (F - T.n0) / (RPI * NP)) - 1;
         // token rows: instruction q of this producer covers token RPI*(q*NP+wid) + csub
-        int xrow[QX];
-        int nxq = 0;
 #pragma unroll
         for (int q = 0; q < QX; ++q) {
-            const int tr = RPI * (q * NP + wid) + csub;
-            const int r = min(tr, valid - 1);
-            const int64_t R = base + r0 + r;
-            xrow[q] = P.gather ? P.gather[R] : (int)(P.x_local ? (int64_t)(r0 + r) : R);
-            nxq += RPI * (q * NP + wid) < trows ? 1 : 0;
+            const int r = min(RPI * (q * NP + wid) + csub, T.valid - 1);
+            const int64_t R = T.base + T.r0 + r;
+            T.xrow[q] = P.gather ? P.gather[R] : (int)(P.x_local ? (int64_t)(T.r0 + r) : R);
         }
-        int nlive = producer ? QW + nxq : 0;
         // fp8 scales, 4-byte DMAs into the stage's scale area: producer w stages
         // the activation scales of tokens 64w .. 64w+63 (while any is valid);
         // producer 0 also stages the two weight block scales at slots BM, BM+1
         // (gate/up: gate and up block; down: first and second 128-row block).
-        const float *xssrc = nullptr, *wssrc = nullptr;
-        bool xs_live = false;
+        T.nextra = 0;
+        T.xssrc = T.wssrc = nullptr;
+        T.xs_live = false;
         if (FP8 && producer) {
-            const int r = min(wid * 64 + lane, valid - 1);
-            const int64_t R = base + r0 + r;
-            const int64_t xr = P.gather ? (int64_t)P.gather[R] : (P.x_local ? (int64_t)(r0 + r) : R);
-            xssrc = P.xs + xr * kb_per_row;
-            xs_live = wid * 64 < valid;
+            const int r = min(wid * 64 + lane, T.valid - 1);
+            const int64_t R = T.base + T.r0 + r;
+            const int64_t xr = P.gather ? (int64_t)P.gather[R] : (P.x_local ? (int64_t)(T.r0 + r) : R);
+            T.xssrc = P.xs + xr * kb_per_row;
+            T.xs_live = wid * 64 < T.valid;
             const int nb = F / 128;
             if (GATEUP) {
                 const float *sbase = (lane & 1) ? P.s1 : P.s0;
-                wssrc = sbase + ((int64_t)e * nb + n0 / 128) * kb_per_row;
+                T.wssrc = sbase + ((int64_t)e * nb + T.n0 / 128) * kb_per_row;
             } else {
-                const int fb = min(n0 / 128 + (lane & 1), nb - 1);
-                wssrc = P.s0 + ((int64_t)e * nb + fb) * kb_per_row;
+                const int fb = min(T.n0 / 128 + (lane & 1), nb - 1);
+                T.wssrc = P.s0 + ((int64_t)e * nb + fb) * kb_per_row;
             }
-            nlive += (xs_live ? 1 : 0) + (wid == 0 ? 1 : 0);
+            T.nextra = (T.xs_live ? 1 : 0) + (wid == 0 ? 1 : 0);
         }
-        const char *xbase = (const char *)P.x;
-
-        int slot_issue = 0;   // ring slot of the next stage issued
-        auto issue = [&](int ks) {
-            char *st = ring + slot_issue * stage_bytes;
-            if (producer) {
-                // an opaque copy of the row stride keeps the per-instruction addresses
-                // from being hoisted out of the reduction loop (they would occupy
-                // ~32 VGPRs for the whole tile); recomputing them costs a few SALU/VALU ops
-                int64_t rb = rowbytes;
-                asm volatile("" : "+s"(rb));
+    };
+    // Load q of one step by this producer: q < QW are weight instructions, the
+    // rest token instructions (NTB of them cover 32*NTB token rows).
+    auto dma_one = [&](const Tile &T, int q, int ks, char *st) {
+        // an opaque copy of the row stride keeps the per-instruction addresses
+        // from being hoisted out of the reduction loop (they would occupy
+        // ~32 VGPRs for the whole tile); recomputing them costs a few SALU/VALU ops
+        int64_t rb = rowbytes;
+        asm volatile("" : "+s"(rb));
+        if (q < QW) {
+            // gate/up: instructions q < QW/2 read gate rows, the rest the matching up rows
+            const bool up = GATEUP && q >= QW / 2;
+            const int qq = min(GATEUP ? (up ? q - QW / 2 : q) : q, T.qmax);
+            const char *src = (up ? T.wbase1 : T.wbase0) + (int64_t)qq * (RPI * NP) * rb + (int64_t)ks * CB;
+            dma16(src, st + (q * NP + wid) * 1024);
+        } else {
+            const int qx = q - QW;
+            const int ins = qx * NP + wid;
+            const int row = WR + RPI * ins + csub;
+            const char *src = (const char *)pick(a, T.p).x + (int64_t)T.xrow[qx] * rb + (int64_t)ks * CB +
+                              ((cslot ^ swz<CB>(row)) << 4);
+            dma16(src, st + (WR / RPI + ins) * 1024);
+        }
+    };
+    auto dma_scales = [&](const Tile &T, int ks, char *st) {
+        if (FP8) {
+            if (T.xs_live) dma4(T.xssrc + ks, st + T.srows * CB + wid * 256);
+            if (wid == 0) dma4(T.wssrc + ks, st + T.srows * CB + BM * 4);
+        }
+    };
+    // The first S-1 steps of a tile (issued while the ring is otherwise idle).
+    auto prologue = [&](const Tile &T) {
+        if (!producer) return;
+        const int ndma = QW + T.nx;
+        for (int ks = 0; ks < T.S - 1 && ks < KT; ++ks) {
+            char *st = ring + ks * T.stage_bytes;
+            dma_scales(T, ks, st);
 #pragma unroll
-                for (int q = 0; q < QW; ++q) {
-                    // gate/up: instructions q < QW/2 read gate rows, the rest the matching up rows
-                    const bool up = GATEUP && q >= QW / 2;
-                    const int qq = min(GATEUP ? (up ? q - QW / 2 : q) : q, qmax);
-                    const char *src = (up ? wbase1 : wbase0) + (int64_t)qq * (RPI * NP) * rb + (int64_t)ks * CB;
-                    dma16(src, st + (q * NP + wid) * 1024);
-                }
-#pragma unroll
-                for (int q = 0; q < QX; ++q) {
-                    const int ins = q * NP + wid;
-                    if (RPI * ins >= trows) continue;
-                    const int row = WR + RPI * ins + csub;
-                    const char *src = xbase + (int64_t)xrow[q] * rb + (int64_t)ks * CB + ((cslot ^ swz<CB>(row)) << 4);
-                    dma16(src, st + (WR / RPI + ins) * 1024);
-                }
-                if (FP8) {
-                    if (xs_live) dma4(xssrc + ks, st + srows * CB + wid * 256);
-                    if (wid == 0) dma4(wssrc + ks, st + srows * CB + BM * 4);
-                }
-            }
-            slot_issue = slot_issue + 1 == S ? 0 : slot_issue + 1;
-        };
+            for (int q = 0; q < QW + QX; ++q)
+                if (q < ndma) dma_one(T, q, ks, st);
+        }
+    };
 
+    // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous run of tiles.
+    const int G = gridDim.x;
+    const int first = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    Tile cur, nxt;
+    if (first < total) {
+        setup(first, cur);
+        cta_barrier();   // the start-up scratch in the ring is no longer read
+        prologue(cur);
+    }
+
+    for (int t = first; t < total; t += G) {
         f32x4 acc[RB][TB];
 #pragma unroll
         for (int i = 0; i < RB; ++i)
 #pragma unroll
             for (int j = 0; j < TB; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
 
-        cta_barrier();   // every wave is done with the ring (previous tile, start-up or epilogue scratch)
-        for (int ks = 0; ks < S - 1 && ks < KT; ++ks) issue(ks);
-
         // The reduction loop, specialised on how many of the wave's token blocks
-        // (j*WM + wm, j < NTB) can hold valid tokens.
-        auto kloop = [&](auto ntb) {
+        // (j*WM + wm, j < NTB) can hold valid tokens.  Step kt sits in ring slot
+        // kt % S; the loads of step kt+S-1 go to the slot step kt-1 used, which
+        // every wave has finished with once it passes step kt's barrier.  The
+        // first S-1 steps were loaded before the previous tile's epilogue, whose
+        // stores are younger than them in this wave's memory counter: waiting
+        // for at most (S-2) steps outstanding covers them conservatively.
+        const int S = cur.S, stage_bytes = cur.stage_bytes, srows = cur.srows;
+        auto kloop = [&](auto ntb, auto spread) {
             constexpr int NTB = decltype(ntb)::value;
+            constexpr bool SPREAD = decltype(spread)::value;
+            constexpr int NDMA = QW + NTB * 16 * WM / RPI / NP;   // loads per producer per step, at most
+            const int nlive = QW + cur.nx + cur.nextra;
+            const int kmain = KT - (S - 1);   // steps during which a later step is loaded
             int slot = 0;
             for (int kt = 0; kt < KT; ++kt) {
                 // step kt has landed once at most the later steps' loads are outstanding
@@ -427,19 +490,51 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                     else wait_vmcnt<0>();
                 }
                 cta_barrier();
-                if (kt + S - 1 < KT) issue(kt + S - 1);
                 const char *st = ring + slot * stage_bytes;
                 const float *sc = (const float *)(st + srows * CB);
-                compute_step<DT, GATEUP, NTB>(st, sc, trows, acc, wm, wf, lane);
+                if (producer && kt < kmain) {
+                    char *dst = ring + (slot == 0 ? S - 1 : slot - 1) * stage_bytes;
+                    const int ks = kt + S - 1;
+                    dma_scales(cur, ks, dst);
+                    if (!SPREAD) {
+                        // a deeper ring has room to load ahead: issue the whole step first
+#pragma unroll
+                        for (int q = 0; q < NDMA; ++q)
+                            if (q < QW + cur.nx) dma_one(cur, q, ks, dst);
+                        compute_step<DT, GATEUP, NTB, false, NDMA>(st, sc, acc, wm, wf, lane, [](int) {});
+                    } else {
+                        // double buffering: spread the loads over the products so this
+                        // wave's share of the products is not held up behind them
+                        compute_step<DT, GATEUP, NTB, true, NDMA>(st, sc, acc, wm, wf, lane,
+                                                                  [&](int q) { dma_one(cur, q, ks, dst); });
+                    }
+                } else {
+                    compute_step<DT, GATEUP, NTB, false, NDMA>(st, sc, acc, wm, wf, lane, [](int) {});
+                }
                 slot = slot + 1 == S ? 0 : slot + 1;
             }
         };
-        if (ntb == 2) kloop(std::integral_constant<int, 2>{});
-        else if (ntb == 4) kloop(std::integral_constant<int, 4>{});
-        else if (ntb == 6) kloop(std::integral_constant<int, 6>{});
-        else kloop(std::integral_constant<int, TB>{});
+        auto kloop_s = [&](auto ntb) {
+            if (cur.spread) kloop(ntb, std::true_type{});
+            else kloop(ntb, std::false_type{});
+        };
+        if (cur.ntb == 2) kloop_s(std::integral_constant<int, 2>{});
+        else if (cur.ntb == 4) kloop_s(std::integral_constant<int, 4>{});
+        else if (cur.ntb == 6) kloop_s(std::integral_constant<int, 6>{});
+        else kloop_s(std::integral_constant<int, TB>{});
+
+        // Every wave is done with the ring: start the next tile's loads, then
+        // write this tile's results while they are in flight.
+        cta_barrier();
+        if (t + G < total) {
+            setup(t + G, nxt);
+            prologue(nxt);
+        }
 
         // ---- epilogue ----
+        const FfnProblem P = pick(a, cur.p);
+        const int valid = cur.valid, n0 = cur.n0;
+        const int64_t rbase = cur.base + cur.r0;
         // h for gate block i pairs with up block i + RB/2 (same features); it is
         // recomputed from the accumulators per 16-token block to keep registers low.
         auto hval = [&](int i, int j, int q) {
@@ -450,7 +545,6 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
             if (FP8) {
                 // 1 x 128 groups of H along features: the tile's 128 features of a token live in
                 // 4 lanes x (RB/2) blocks x 4 values in each of the WF waves of its token column
-                cta_barrier();   // the ring is free: every wave has finished its last step
 #pragma unroll
                 for (int j = 0; j < TB; ++j) {
                     float m = 0.0f;
@@ -462,7 +556,8 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                     m = fmaxf(m, __shfl_xor(m, 32, 64));
                     if (lane < 16) red[wf * BM + (j * WM + wm) * 16 + lane] = m;
                 }
-                __syncthreads();
+                wait_lgkm0();
+                cta_barrier();
 #pragma unroll
                 for (int j = 0; j < TB; ++j) {
                     if ((j * WM + wm) * 16 >= valid) continue;
@@ -472,7 +567,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                     for (int o = 0; o < WF; ++o) amax = fmaxf(amax, red[o * BM + tok]);
                     const float scale = quant_scale(amax);
                     if (tok >= valid) continue;
-                    const int64_t R = base + r0 + tok;
+                    const int64_t R = rbase + tok;
                     uint8_t *orow = (uint8_t *)P.out + R * F;
 #pragma unroll
                     for (int i = 0; i < RB / 2; ++i) {
@@ -488,7 +583,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                 for (int j = 0; j < TB; ++j) {
                     const int tok = (j * WM + wm) * 16 + (lane & 15);
                     if (tok >= valid) continue;
-                    const int64_t R = base + r0 + tok;
+                    const int64_t R = rbase + tok;
 #pragma unroll
                     for (int i = 0; i < RB / 2; ++i) {
                         const int f = n0 + wf * (BF / WF) + i * 16 + 4 * (lane >> 4);
@@ -506,7 +601,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
             for (int j = 0; j < TB; ++j) {
                 const int tok = (j * WM + wm) * 16 + (lane & 15);
                 if (tok >= valid) continue;
-                const int64_t R = base + r0 + tok;
+                const int64_t R = rbase + tok;
 #pragma unroll
                 for (int i = 0; i < RB; ++i) {
                     const int f = n0 + wf * WRW + i * 16 + 4 * (lane >> 4);
@@ -520,6 +615,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                 }
             }
         }
+        cur = nxt;
     }
 }
 
@@ -533,10 +629,10 @@ hipError_t run(const FfnArgs &a, hipStream_t s) {
     });
     if (attr_err != hipSuccess) return attr_err;
     const int pb = prefix_bytes(a.p[0].n_exp, a.nprob > 1 ? a.p[1].n_exp : 0);
-    const int ring = LDS_TOTAL - pb;
-    // the ring must hold two stages of any tile plus its read past the last slot (at most 56 rows)
+    const int ring = LDS_TOTAL - pb - red_bytes<DT, GATEUP>();
+    // the ring must hold two stages of any tile
     constexpr int CB = Frag<DT>::CB;
-    if (ring < 2 * ((WR + BM) * CB + (DT == DT_E4M3 ? SCL_BYTES : 0)) + 56 * CB) return hipErrorInvalidValue;
+    if (ring < 2 * ((WR + BM) * CB + (DT == DT_E4M3 ? SCL_BYTES : 0))) return hipErrorInvalidValue;
     int grid = device_cus();
     grid = (grid + 7) / 8 * 8;
     ffn_kernel<DT, GATEUP><<<grid, NT, LDS_TOTAL, s>>>(a, ring);
