@@ -35,33 +35,68 @@ __global__ __launch_bounds__(64) void perm_hist_kernel(const int32_t *__restrict
 
 // One workgroup: counts[e] = sum over blocks; offsets = exclusive scan of counts;
 // blockcounts[b][e] becomes the first row of block b's pairs for expert e.
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ bc, int64_t nb, int Nr,
-                                                        int32_t *__restrict__ counts, int32_t *__restrict__ offsets) {
-    __shared__ int sums[1024];
-    const int e = threadIdx.x;
+// Thread (part, e) walks a contiguous range of blocks of expert e (P = 1024/Nr
+// parts per expert; neighbouring threads read neighbouring experts of one
+// block), 16 independent loads at a time.
+constexpr int SCAN_NT = 1024;
+constexpr int SCAN_UNROLL = 16;
+
+__global__ __launch_bounds__(SCAN_NT) void perm_scan_kernel(int32_t *__restrict__ bc, int64_t nb, int Nr,
+                                                           int32_t *__restrict__ counts, int32_t *__restrict__ offsets) {
+    __shared__ int part_sum[SCAN_NT];     // [part][e]: block-range sums, then their exclusive prefix
+    __shared__ int sums[SCAN_NT];
+    const int tid = threadIdx.x;
+    const int P = SCAN_NT / Nr;           // Nr <= 1024
+    const int e = tid % Nr, part = tid / Nr;
+    const bool active = part < P;
+    const int64_t chunk = (nb + P - 1) / P;
+    const int64_t lo = active ? min(nb, (int64_t)part * chunk) : 0, hi = active ? min(nb, lo + chunk) : 0;
+
+    int local = 0;
+    for (int64_t b0 = lo; b0 < hi; b0 += SCAN_UNROLL) {
+        int v[SCAN_UNROLL];
+#pragma unroll
+        for (int u = 0; u < SCAN_UNROLL; ++u) v[u] = b0 + u < hi ? bc[(b0 + u) * Nr + e] : 0;
+#pragma unroll
+        for (int u = 0; u < SCAN_UNROLL; ++u) local += v[u];
+    }
+    if (active) part_sum[part * Nr + e] = local;
+    __syncthreads();
     int total = 0;
-    if (e < Nr) {
-        for (int64_t b = 0; b < nb; ++b) {
-            int c = bc[b * Nr + e];
-            bc[b * Nr + e] = total;          // running base inside the expert
+    if (tid < Nr) {
+        for (int p = 0; p < P; ++p) {     // exclusive prefix over the parts of expert tid
+            const int c = part_sum[p * Nr + tid];
+            part_sum[p * Nr + tid] = total;
             total += c;
         }
     }
-    sums[e] = e < Nr ? total : 0;
+    sums[tid] = tid < Nr ? total : 0;
     __syncthreads();
-    // Hillis-Steele inclusive scan over 1024 entries
-    for (int off = 1; off < 1024; off <<= 1) {
-        int v = e >= off ? sums[e - off] : 0;
+    // Hillis-Steele inclusive scan over the expert totals
+    for (int off = 1; off < SCAN_NT; off <<= 1) {
+        const int v = tid >= off ? sums[tid - off] : 0;
         __syncthreads();
-        sums[e] += v;
+        sums[tid] += v;
         __syncthreads();
     }
-    if (e < Nr) {
-        int base = sums[e] - total;          // exclusive
-        counts[e] = total;
-        offsets[e] = base;
-        if (e == Nr - 1) offsets[Nr] = sums[e];
-        for (int64_t b = 0; b < nb; ++b) bc[b * Nr + e] += base;
+    if (tid < Nr) {
+        counts[tid] = total;
+        offsets[tid] = sums[tid] - total;  // exclusive
+        if (tid == Nr - 1) offsets[Nr] = sums[tid];
+    }
+    if (!active) return;
+    // first row of this thread's first block for expert e: the expert's exclusive
+    // offset plus the pairs of the earlier parts
+    int run = (e > 0 ? sums[e - 1] : 0) + part_sum[part * Nr + e];
+    for (int64_t b0 = lo; b0 < hi; b0 += SCAN_UNROLL) {
+        int v[SCAN_UNROLL];
+#pragma unroll
+        for (int u = 0; u < SCAN_UNROLL; ++u) v[u] = b0 + u < hi ? bc[(b0 + u) * Nr + e] : 0;
+#pragma unroll
+        for (int u = 0; u < SCAN_UNROLL; ++u) {
+            if (b0 + u < hi) bc[(b0 + u) * Nr + e] = run;
+            run += v[u];
+        }
     }
 }
 

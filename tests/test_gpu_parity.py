@@ -114,7 +114,10 @@ def test_route_selection_bitexact(moe, orc, T, Nr, G, Mg, K, ties):
 
 
 def test_route_affinities_close_and_selection_consistent(moe, orc):
-    for cfg in (syn.CONFIGS["tiny"], small_cfg("bf16", 200, d=1024, Nr=64, G=8, Mg=4, K=8)):
+    # the last two shapes have enough 128-token tiles to take the wide gate-GEMM tiles
+    for cfg in (syn.CONFIGS["tiny"], small_cfg("bf16", 200, d=1024, Nr=64, G=8, Mg=4, K=8),
+                small_cfg("bf16", 4200, d=256, Nr=1024, G=16, Mg=4, K=8),
+                small_cfg("fp32", 4100, d=128, Nr=1024, G=8, Mg=2, K=6)):
         u = syn.hidden(cfg)
         g, b = syn.router_params(cfg)
         shape = shape_of(cfg)
