@@ -250,10 +250,11 @@ def test_grouped_ffn_integer_inputs_bitexact(moe, orc):
 # combine
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,Ns,flags", [("fp32", 1, 0), ("bf16", 2, 0), ("bf16", 0, 1), ("fp32", 1, 1)])
-def test_combine(moe, orc, dtype, Ns, flags):
-    rng = np.random.default_rng(9)
-    T, K, d = 77, 6, 384
+@pytest.mark.parametrize("dtype,Ns,flags,K", [("fp32", 1, 0, 6), ("bf16", 2, 0, 6), ("bf16", 0, 1, 6), ("fp32", 1, 1, 6),
+                                             ("bf16", 1, 0, 8), ("bf16", 1, 1, 12), ("fp32", 2, 0, 10)])
+def test_combine(moe, orc, dtype, Ns, flags, K):
+    rng = np.random.default_rng(9 + K)
+    T, d = 77, 384
     cfg = small_cfg(dtype, T, d=d, Nr=16, G=1, Mg=1, K=K, Ns=Ns)
     conv = (lambda a: syn.to_bf16_bits(a)) if dtype == "bf16" else (lambda a: a)
     y = conv(rng.standard_normal((T * K, d)).astype(np.float32))
