@@ -130,20 +130,25 @@ __device__ __forceinline__ void compute_step(const char *st, const float *sc, f3
             af[i] = Fr::load(st, wrow + (lane & 15), s, lane);
         }
         if (DT == DT_E4M3) {
+            const float sw0 = sc[BM], sw1 = sc[BM + 1];
+            // down: the wave's rows sit in the first or the second 128-row block
+            const float swd = ((wf * WRW) >= 128) ? sw1 : sw0;
 #pragma unroll
             for (int j = 0; j < NTB; ++j) {
                 const int tok = (j * WM + wm) * 16 + (lane & 15);
                 const typename Fr::t bfr = Fr::load(st, WR + tok, s, lane);
                 const float sa = sc[tok];
-                const float c0 = sa * sc[BM], c1 = sa * sc[BM + 1];
-                // down: the wave's rows sit in the first or the second 128-row block
-                const float cdown = ((wf * WRW) >= 128) ? c1 : c0;
+                // the block's products first, then their scaling: the scaling of one
+                // product then waits only for that product, not for a chain of them
+                f32x4 part[RB];
+#pragma unroll
+                for (int i = 0; i < RB; ++i) part[i] = Tr::mma(af[i], bfr, f32x4{0, 0, 0, 0});
+                const float c0 = sa * sw0, c1 = sa * sw1, cd = sa * swd;
 #pragma unroll
                 for (int i = 0; i < RB; ++i) {
-                    const f32x4 part = Tr::mma(af[i], bfr, f32x4{0, 0, 0, 0});
-                    const float cc = GATEUP ? ((i >= RB / 2) ? c1 : c0) : cdown;
+                    const float cc = GATEUP ? ((i >= RB / 2) ? c1 : c0) : cd;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[i][j][q] += part[q] * cc;
+                    for (int q = 0; q < 4; ++q) acc[i][j][q] += part[i][q] * cc;
                 }
                 group_dma(s * NTB + j);
             }
