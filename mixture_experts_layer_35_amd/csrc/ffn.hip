@@ -238,11 +238,14 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
         const int e = find_expert(ppre, P.n_exp, lt);
         T.base = P.offsets ? (int64_t)P.offsets[e] : (int64_t)e * P.rows_fixed;
         const int Me = P.offsets ? P.offsets[e + 1] - P.offsets[e] : (int)P.rows_fixed;
+        // the expert's rows are split evenly over its row blocks, so row blocks that share
+        // a weight block take equally long and stay close enough to share it through L2
         const int mt = (Me + BM - 1) / BM;
         const int ln = lt - ppre[e];
         const int nt = ln / mt, mi = ln - nt * mt;
-        T.r0 = mi * BM;
-        T.valid = min(BM, Me - T.r0);
+        const int mq = Me / mt, mr = Me - mq * mt;
+        T.r0 = mi * mq + min(mi, mr);
+        T.valid = mq + (mi < mr ? 1 : 0);
         T.n0 = nt * BF;
         // Token blocks this tile needs per wave: NTB = ceil(valid / (16*WM)) rounded up to an
         // even count, so the specialised loops below cover 64, 128, 192 or 256 tokens.  Stage
