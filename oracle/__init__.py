@@ -83,6 +83,8 @@ def _load():
                                                + [P] * 4 + [P] * 6 + [P] * 6 + [P] * 4)
             lib.oracle_bias_update.restype = None
             lib.oracle_bias_update.argtypes = [i32, i64, i32, P, P, f32]
+            lib.oracle_seq_balance.restype = None
+            lib.oracle_seq_balance.argtypes = [i64, i32, i32, P, P, i64, f32, P, P, P]
             lib.oracle_num_threads.restype = i32
             lib.oracle_num_threads.argtypes = []
             _lib = lib
@@ -336,6 +338,23 @@ def bias_update(counts, bias, T, K, gamma=0.001):
     b = np.array(bias, dtype=np.float32, copy=True)
     _load().oracle_bias_update(b.shape[0], T, K, _p(counts), _p(b), gamma)
     return b
+
+
+def seq_balance(scores, topk_idx, seq_len, alpha=1e-4):
+    """Complementary sequence-wise balance statistic per sequence of seq_len
+    consecutive tokens (§2.1.2; alpha from §4.2): returns (loss [n_seq] fp32,
+    counts [n_seq, Nr] int32 (selected slots per expert), P [n_seq, Nr] fp32
+    (mean affinity share))."""
+    scores = _c(scores, np.float32)
+    topk_idx = _c(topk_idx, np.int32)
+    T, Nr = scores.shape
+    K = topk_idx.shape[1]
+    n_seq = (T + seq_len - 1) // seq_len
+    loss = np.empty(n_seq, np.float32)
+    counts = np.empty((n_seq, Nr), np.int32)
+    share = np.empty((n_seq, Nr), np.float32)
+    _load().oracle_seq_balance(T, Nr, K, _p(scores), _p(topk_idx), seq_len, alpha, _p(loss), _p(counts), _p(share))
+    return loss, counts, share
 
 
 # ----------------------------------------------------------------------------

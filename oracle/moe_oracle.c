@@ -569,6 +569,50 @@ void oracle_bias_update(int Nr, int64_t T, int K, const int32_t *counts, float *
     }
 }
 
+/*
+ * Complementary sequence-wise balance statistic (§2.1.2: a tiny loss
+ * alpha * sum_i f_i P_i kept next to the bias rule; §4.2: alpha = 0.0001).
+ * The pages name f_i and P_i but their definitions are stripped; reading:
+ * for a sequence of Ts tokens,
+ *   f_i = N_r / (K * Ts) * #{(t, j) : topk_idx[t][j] == i}   (selected load, 1 when even)
+ *   P_i = (1 / Ts) * sum_t s_{i,t} / sum_k s_{k,t}           (affinity share over all routed experts)
+ * Sequences are consecutive runs of seq_len tokens (the last may be shorter).
+ * All sums in double, each output rounded once.  counts_out [n_seq][Nr] and
+ * share_out [n_seq][Nr] (P_i) may be NULL.
+ */
+void oracle_seq_balance(int64_t T, int Nr, int K, const float *scores, const int32_t *topk_idx, int64_t seq_len,
+                        float alpha, float *loss_out, int32_t *counts_out, float *share_out)
+{
+    const int64_t n_seq = (T + seq_len - 1) / seq_len;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(dynamic)
+#endif
+    for (int64_t q = 0; q < n_seq; ++q) {
+        const int64_t t0 = q * seq_len;
+        const int64_t t1 = t0 + seq_len < T ? t0 + seq_len : T;
+        const double Ts = (double)(t1 - t0);
+        int64_t *cnt = (int64_t *)calloc((size_t)Nr, sizeof(int64_t));
+        double *share = (double *)calloc((size_t)Nr, sizeof(double));
+        for (int64_t t = t0; t < t1; ++t) {
+            double row = 0.0;
+            for (int i = 0; i < Nr; ++i) row += (double)scores[t * Nr + i];
+            for (int i = 0; i < Nr; ++i) share[i] += (double)scores[t * Nr + i] / row;
+            for (int j = 0; j < K; ++j) cnt[topk_idx[t * K + j]] += 1;
+        }
+        double loss = 0.0;
+        for (int i = 0; i < Nr; ++i) {
+            const double f = (double)Nr / ((double)K * Ts) * (double)cnt[i];
+            const double P = share[i] / Ts;
+            loss += f * P;
+            if (counts_out) counts_out[q * Nr + i] = (int32_t)cnt[i];
+            if (share_out) share_out[q * Nr + i] = (float)P;
+        }
+        loss_out[q] = (float)((double)alpha * loss);
+        free(cnt);
+        free(share);
+    }
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -463,3 +463,57 @@ def test_v3_configs_match_the_pages_hyper_parameters():
     assert hp["quant_group"] == 128 and hp["bias_update_speed"] == 0.001
     # FLOPs per token: 9 experts x 6 d I + 2 d Nr
     assert syn.CONFIGS["v3_prefill"].flops_per_token == 796_393_472
+
+
+# ---------------------------------------------------------------------------
+# complementary sequence-wise balance statistic (§2.1.2; alpha = 1e-4 from §4.2)
+# ---------------------------------------------------------------------------
+
+def test_seq_balance_even_routing_gives_alpha(orc):
+    """Every expert taken equally often and equal affinities: f_i = 1 and
+    P_i = 1/N_r, so the loss is alpha * N_r * (1/N_r) = alpha."""
+    Nr, K, Ts = 32, 4, 64
+    scores = np.full((Ts, Nr), 0.3, np.float32)
+    idx = np.array([[(t * K + j) % Nr for j in range(K)] for t in range(Ts)], np.int32)
+    loss, counts, share = orc.seq_balance(scores, idx, Ts, alpha=1e-4)
+    assert (counts == Ts * K // Nr).all()
+    assert np.allclose(share, 1.0 / Nr, rtol=0, atol=1e-8)
+    assert loss[0] == np.float32(1e-4)
+
+
+def test_seq_balance_concentrated_closed_form(orc):
+    """All tokens pick the same K experts A, with affinity 1 on A and eps
+    elsewhere: f_A = N_r/K, P_A = 1/(K + (N_r-K) eps), f = 0 off A, so
+    loss = alpha * N_r / (K + (N_r - K) eps)."""
+    Nr, K, Ts, eps = 64, 8, 50, 1e-3
+    A = np.arange(5, 5 + K)
+    scores = np.full((Ts, Nr), eps, np.float32)
+    scores[:, A] = 1.0
+    idx = np.tile(A.astype(np.int32), (Ts, 1))
+    loss, counts, _ = orc.seq_balance(scores, idx, Ts, alpha=1e-4)
+    expect = 1e-4 * Nr / (K + (Nr - K) * float(np.float32(eps)))
+    assert abs(float(loss[0]) - expect) <= 2 ** -23 * expect
+    assert counts[0, A].tolist() == [Ts] * K and counts[0].sum() == Ts * K
+
+
+def test_seq_balance_invariants_and_sequence_split(orc):
+    """Per sequence the counts sum to K*Ts and the affinity shares sum to 1;
+    a batch of sequences gives each sequence the loss it has alone; a shorter
+    last sequence is normalised by its own length."""
+    rng = np.random.default_rng(4)
+    Nr, K, L = 48, 6, 37
+    T = 3 * L + 11
+    scores = rng.uniform(0.01, 1.0, (T, Nr)).astype(np.float32)
+    idx = np.stack([rng.permutation(Nr)[:K] for _ in range(T)]).astype(np.int32)
+    loss, counts, share = orc.seq_balance(scores, idx, L)
+    assert loss.shape == (4,)
+    lens = [L, L, L, 11]
+    for q, n in enumerate(lens):
+        assert counts[q].sum() == K * n
+        assert abs(share[q].astype(np.float64).sum() - 1.0) <= Nr * 2 ** -23
+        alone, c1, s1 = orc.seq_balance(scores[q * L:q * L + n], idx[q * L:q * L + n], n)
+        assert alone[0] == loss[q] and (c1[0] == counts[q]).all() and (s1[0] == share[q]).all()
+    # permuting tokens inside a sequence changes nothing but rounding order
+    perm = np.concatenate([rng.permutation(L), np.arange(L, T)])
+    lp, cp, _ = orc.seq_balance(scores[perm], idx[perm], L)
+    assert (cp == counts).all() and abs(float(lp[0]) - float(loss[0])) <= 1e-6 * float(loss[0])
