@@ -233,6 +233,29 @@ size_t moe_ffn_workspace_bytes(const moe_shape *shape, int64_t max_rows);
 int moe_bias_update(const moe_shape *shape, const int32_t *counts, float *bias, float gamma, void *stream);
 
 /*
+ * moe_seq_balance -- complementary sequence-wise balance statistic (§2.1.2: a
+ * tiny loss alpha * sum_i f_i P_i kept beside the bias rule; §4.2: alpha =
+ * 0.0001).  The pages name f_i and P_i without defining them; reading, for a
+ * sequence of Ts tokens:
+ *   f_i = N_r / (K * Ts) * (slots of the sequence routed to expert i),
+ *   P_i = (1/Ts) * sum_t s_{i,t} / sum_k s_{k,t}   (affinity share over all
+ *         routed experts, un-biased s).
+ * Sequences are consecutive runs of seq_len tokens of the batch (the last one
+ * may be shorter): n_seq = ceil(T / seq_len).
+ * scores [T][N_r] fp32 (moe_route's scores_out), topk_idx [T][K] int32.
+ * loss [n_seq] fp32; counts [n_seq][N_r] int32 and share [n_seq][N_r] fp32
+ * (P_i) are optional (NULL).  fp32 sums in a fixed order (deterministic).
+ * ws: moe_seq_balance_workspace_bytes(shape, seq_len).
+ * Errors: MOE_ERR_INVALID_ARG for seq_len < 1 or a NULL required pointer.
+ */
+int moe_seq_balance(const moe_shape *shape, const float *scores, const int32_t *topk_idx, int64_t seq_len,
+                    float alpha, float *loss, int32_t *counts, float *share, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* Workspace bytes for moe_seq_balance (0 when rejected). */
+size_t moe_seq_balance_workspace_bytes(const moe_shape *shape, int64_t seq_len);
+
+/*
  * moe_quantize_1x128 -- Q over 1x128 tiles of each row of x [rows][cols]
  * (x_dtype MOE_F32 or MOE_BF16; cols % 128 == 0): q [rows][cols] e4m3,
  * s [rows][cols/128] fp32 (§3.3 activation tiles).

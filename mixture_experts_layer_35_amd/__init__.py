@@ -26,8 +26,8 @@ MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_FORWARD = 0, 1, 2
 
 EXPORTED = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_timed",
             "moe_workspace_bytes",
-            "moe_ffn_workspace_bytes", "moe_bias_update", "moe_quantize_1x128", "moe_quantize_weights_128x128",
-            "moe_last_error", "moe_version")
+            "moe_ffn_workspace_bytes", "moe_bias_update", "moe_seq_balance", "moe_seq_balance_workspace_bytes",
+            "moe_quantize_1x128", "moe_quantize_weights_128x128", "moe_last_error", "moe_version")
 
 
 class MoeError(RuntimeError):
@@ -78,6 +78,7 @@ def lib():
                 "moe_forward": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P],
                 "moe_forward_timed": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P, P],
                 "moe_bias_update": [S, P, P, ctypes.c_float, P],
+                "moe_seq_balance": [S, P, P, i64, ctypes.c_float, P, P, P, P, sz, P],
                 "moe_quantize_1x128": [i64, i32, i32, P, P, P, P],
                 "moe_quantize_weights_128x128": [i64, i32, i32, i32, P, P, P, P],
             }
@@ -89,6 +90,8 @@ def lib():
             L.moe_workspace_bytes.restype = sz
             L.moe_ffn_workspace_bytes.argtypes = [S, i64]
             L.moe_ffn_workspace_bytes.restype = sz
+            L.moe_seq_balance_workspace_bytes.argtypes = [S, i64]
+            L.moe_seq_balance_workspace_bytes.restype = sz
             L.moe_last_error.argtypes = []
             L.moe_last_error.restype = ctypes.c_char_p
             L.moe_version.argtypes = []
@@ -215,6 +218,15 @@ def moe_forward_timed(shape, u, gate_w, bias, routed_w, routed_s, shared_w, shar
 
 def moe_bias_update(shape, counts, bias, gamma, stream=None):
     return _check(lib().moe_bias_update(ctypes.byref(shape), _ptr(counts), _ptr(bias), gamma, _stream(stream)))
+
+
+def moe_seq_balance_workspace_bytes(shape: MoeShape, seq_len: int) -> int:
+    return lib().moe_seq_balance_workspace_bytes(ctypes.byref(shape), seq_len)
+
+
+def moe_seq_balance(shape, scores, topk_idx, seq_len, alpha, loss, counts=None, share=None, ws=None, stream=None):
+    return _check(lib().moe_seq_balance(ctypes.byref(shape), _ptr(scores), _ptr(topk_idx), seq_len, alpha, _ptr(loss),
+                                        _ptr(counts), _ptr(share), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
 def moe_quantize_1x128(rows, cols, x_dtype, x, q, s, stream=None):

@@ -465,6 +465,35 @@ int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, con
     return MOE_OK;
 }
 
+size_t moe_seq_balance_workspace_bytes(const moe_shape *s, int64_t seq_len) {
+    if (check_shape(s, "moe_seq_balance_workspace_bytes") != MOE_OK) return 0;
+    if (seq_len < 1) { fail(MOE_ERR_INVALID_ARG, "moe_seq_balance_workspace_bytes: seq_len < 1"); return 0; }
+    const int64_t n_seq = (s->T + seq_len - 1) / seq_len;
+    const size_t rows = (size_t)(n_seq * balance_blocks_per_seq(s->T, seq_len));
+    return align256(rows * s->n_routed * 4) * 2;
+}
+
+int moe_seq_balance(const moe_shape *s, const float *scores, const int32_t *topk_idx, int64_t seq_len, float alpha,
+                    float *loss, int32_t *counts, float *share, void *ws, size_t ws_bytes, void *stream) {
+    const char *fn = "moe_seq_balance";
+    int rc = check_shape(s, fn);
+    if (rc) return rc;
+    if (seq_len < 1) return fail(MOE_ERR_INVALID_ARG, "%s: seq_len = %lld must be >= 1", fn, (long long)seq_len);
+    if (s->T == 0) return MOE_OK;
+    NEED(scores);
+    NEED(topk_idx);
+    NEED(loss);
+    rc = ws_check(ws, ws_bytes, moe_seq_balance_workspace_bytes(s, seq_len), fn);
+    if (rc) return rc;
+    const int64_t n_seq = (s->T + seq_len - 1) / seq_len;
+    const size_t rows = (size_t)(n_seq * balance_blocks_per_seq(s->T, seq_len));
+    float *ps = (float *)ws;
+    int32_t *pc = (int32_t *)((char *)ws + align256(rows * s->n_routed * 4));
+    HIPCHK(launch_seq_balance(scores, topk_idx, s->T, s->n_routed, s->topk, seq_len, alpha, loss, counts, share, ps, pc,
+                              (hipStream_t)stream));
+    return MOE_OK;
+}
+
 int moe_bias_update(const moe_shape *s, const int32_t *counts, float *bias, float gamma, void *stream) {
     const char *fn = "moe_bias_update";
     int rc = check_shape(s, fn);

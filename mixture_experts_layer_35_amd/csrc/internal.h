@@ -70,6 +70,12 @@ hipError_t launch_ffn(int dt, bool gateup, const FfnArgs &a, hipStream_t s);
 hipError_t launch_combine(int dt_out, int dt_res, const void *y_perm, const int32_t *inv_perm, const float *topk_w,
                           const void *y_shared, int Ns, const void *residual, void *out, int64_t T, int d, int K,
                           hipStream_t s);
+// Sequence-wise balance statistic; part_share / part_count hold
+// n_seq * balance_blocks_per_seq(T, seq_len) rows of Nr partials each.
+int64_t balance_blocks_per_seq(int64_t T, int64_t seq_len);
+hipError_t launch_seq_balance(const float *scores, const int32_t *idx, int64_t T, int Nr, int K, int64_t seq_len,
+                              float alpha, float *loss, int32_t *counts, float *share, float *part_share,
+                              int32_t *part_count, hipStream_t s);
 hipError_t launch_bias_update(const int32_t *counts, float *bias, int64_t T, int K, int Nr, float gamma,
                               hipStream_t s);
 hipError_t launch_set_offsets(int32_t *offsets, int n, int64_t step, hipStream_t s);

@@ -123,6 +123,23 @@ def test_empty_batch_is_a_noop(lib):
                          need, None)
     assert rc == moe.MOE_OK, moe.moe_last_error()
     assert lib.moe_route(ctypes.byref(s), FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, 0, None) == moe.MOE_OK
+    assert lib.moe_seq_balance(ctypes.byref(s), FAKE, FAKE, 4096, 1e-4, FAKE, None, None, None, 0, None) == moe.MOE_OK
+
+
+def test_seq_balance_rejections(lib):
+    s = tiny()
+    assert lib.moe_seq_balance(ctypes.byref(s), FAKE, FAKE, 0, 1e-4, FAKE, None, None, FAKE, 1 << 20,
+                               None) == moe.MOE_ERR_INVALID_ARG
+    assert "seq_len" in moe.moe_last_error()
+    assert lib.moe_seq_balance(ctypes.byref(s), None, FAKE, 64, 1e-4, FAKE, None, None, FAKE, 1 << 20,
+                               None) == moe.MOE_ERR_INVALID_ARG
+    need = lib.moe_seq_balance_workspace_bytes(ctypes.byref(s), 64)
+    assert need > 0
+    assert lib.moe_seq_balance(ctypes.byref(s), FAKE, FAKE, 64, 1e-4, FAKE, None, None, FAKE, need - 1,
+                               None) == moe.MOE_ERR_WORKSPACE
+    # partials: one row of N_r per 64-token block of every sequence
+    T = s.T
+    assert need >= 2 * ((T + 63) // 64) * s.n_routed * 4
 
 
 def test_workspace_grows_with_tokens(lib):

@@ -389,3 +389,32 @@ def test_bias_update_replay(moe, orc):
         assert (host(idx) == ir).all() and (host(counts) == cr).all()
         assert (host(bias_d).view(np.uint32) == bias_h.view(np.uint32)).all()
     assert (bias_h != 0).any()
+
+
+# ---------------------------------------------------------------------------
+# complementary sequence-wise balance statistic
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,Nr,K,seq_len", [(1000, 256, 8, 300), (4096, 256, 8, 4096), (777, 64, 6, 5000),
+                                             (130, 16, 2, 1), (2048, 1024, 8, 512), (200, 48, 4, 64)])
+def test_seq_balance(moe, orc, T, Nr, K, seq_len):
+    """Given identical scores and selections: slot counts bit-exact, shares and
+    loss within fp32 summation error of the oracle's fp64 sums."""
+    rng = np.random.default_rng(T + Nr + seq_len)
+    scores = rng.uniform(0.01, 1.0, (T, Nr)).astype(np.float32)
+    idx = np.argsort(rng.random((T, Nr)), axis=1)[:, :K].astype(np.int32)
+    cfg = small_cfg("fp32", T, d=128, Nr=Nr, G=1, Mg=1, K=K)
+    shape = shape_of(cfg)
+    n_seq = (T + seq_len - 1) // seq_len
+    loss, counts, share = empty(n_seq, torch.float32), empty((n_seq, Nr), torch.int32), empty((n_seq, Nr), torch.float32)
+    ws = empty(moe.moe_seq_balance_workspace_bytes(shape, seq_len), torch.uint8)
+    print("seq balance", T, Nr, K, seq_len, flush=True)
+    moe.moe_seq_balance(shape, dev(scores), dev(idx), seq_len, 1e-4, loss, counts, share, ws)
+    lr, cr, sr = orc.seq_balance(scores, idx, seq_len, 1e-4)
+    assert (host(counts) == cr).all()
+    assert np.allclose(host(share), sr, rtol=1e-5, atol=1e-9)
+    assert np.allclose(host(loss), lr, rtol=1e-5, atol=0)
+    # the loss alone (optional outputs omitted) is the same, bit for bit (fixed reduction order)
+    loss2 = empty(n_seq, torch.float32)
+    moe.moe_seq_balance(shape, dev(scores), dev(idx), seq_len, 1e-4, loss2, None, None, ws)
+    assert (host(loss2).view(np.uint32) == host(loss).view(np.uint32)).all()

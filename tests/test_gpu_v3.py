@@ -88,6 +88,19 @@ def test_v3_prefill_bf16(moe, orc, v3):
                           (inp["swg"], inp["swu"], inp["swd"]), G=cfg.G, Mg=cfg.Mg, K=cfg.K, w_code=wcode,
                           out_code=ocode, tokens=tokens)
     check(cfg, cfg.T, got, ref, tokens, inp["bias"], 2e-2)
+    # sequence-wise balance statistic of this batch's real routing (4K-token sequences, §4.2)
+    for seq_len in (4096, 1024):
+        n_seq = cfg.T // seq_len
+        shape = shape_of(cfg)
+        loss = torch.empty(n_seq, dtype=torch.float32, device="cuda")
+        counts = torch.empty((n_seq, cfg.Nr), dtype=torch.int32, device="cuda")
+        ws = torch.empty(moe.moe_seq_balance_workspace_bytes(shape, seq_len), dtype=torch.uint8, device="cuda")
+        moe.moe_seq_balance(shape, torch.from_numpy(got["scores"]).cuda(), torch.from_numpy(got["idx"]).cuda(), seq_len,
+                            1e-4, loss, counts, None, ws)
+        lr, cr, _ = orc.seq_balance(got["scores"], got["idx"], seq_len, 1e-4)
+        print("seq balance loss (seq_len %d):" % seq_len, loss.cpu().numpy(), flush=True)
+        assert (counts.cpu().numpy() == cr).all()
+        assert np.allclose(loss.cpu().numpy(), lr, rtol=1e-5, atol=0)
     # the permutation of the same batch is a bijection with increasing tokens per expert
     shape = shape_of(cfg)
     T, K = cfg.T, cfg.K
