@@ -174,6 +174,23 @@ __device__ __forceinline__ void compute_step(const char *st, const float *sc, f3
 template <int DT, bool GATEUP>
 __host__ __device__ constexpr int red_bytes() { return (DT == DT_E4M3 && GATEUP) ? WF * BM * 4 : 0; }
 
+// Stores two adjacent 16-feature blocks of one token's bf16 results (block i
+// from a[], block i+1 from b[]; lane group g = lane/16 holds features 4g..4g+3
+// of each) with one 16-byte store per lane: lanes of even groups keep block i
+// and take their partner's (lane ^ 16) four block-i values, odd groups do the
+// same for block i+1.  A token's 32 features then leave as two 32-byte runs
+// instead of four 16-byte ones.  Both partners hold the same token, so they are
+// active together.
+__device__ __forceinline__ void store_pair_bf16(uint16_t *row, int f_block, const float a[4], const float b[4],
+                                                int lane, int F) {
+    const bool odd = (lane >> 4) & 1;
+    const uint32_t a01 = pack_bf16x2(a[0], a[1]), a23 = pack_bf16x2(a[2], a[3]);
+    const uint32_t b01 = pack_bf16x2(b[0], b[1]), b23 = pack_bf16x2(b[2], b[3]);
+    const uint32_t r0 = __shfl_xor(odd ? a01 : b01, 16, 64), r1 = __shfl_xor(odd ? a23 : b23, 16, 64);
+    const int f = f_block + (odd ? 16 : 0) + 4 * ((lane >> 4) & ~1);
+    if (f < F) *(u32x4 *)(row + f) = odd ? u32x4{r0, r1, b01, b23} : u32x4{a01, a23, r0, r1};
+}
+
 template <int DT, bool GATEUP>
 __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_bytes) {
     constexpr int esz = FTraits<DT>::esz;
@@ -482,14 +499,21 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                     const int tok = (j * WM + wm) * 16 + (lane & 15);
                     if (tok >= valid) continue;
                     const int64_t R = rbase + tok;
+                    if (DT == DT_F32) {
 #pragma unroll
-                    for (int i = 0; i < RB / 2; ++i) {
-                        const int f = n0 + wf * (BF / WF) + i * 16 + 4 * (lane >> 4);
-                        const float h0 = hval(i, j, 0), h1 = hval(i, j, 1), h2 = hval(i, j, 2), h3 = hval(i, j, 3);
-                        if (DT == DT_F32) {
-                            *(f32x4 *)((float *)P.out + R * F + f) = f32x4{h0, h1, h2, h3};
-                        } else {
-                            *(u32x2 *)((uint16_t *)P.out + R * F + f) = u32x2{pack_bf16x2(h0, h1), pack_bf16x2(h2, h3)};
+                        for (int i = 0; i < RB / 2; ++i) {
+                            const int f = n0 + wf * (BF / WF) + i * 16 + 4 * (lane >> 4);
+                            *(f32x4 *)((float *)P.out + R * F + f) =
+                                f32x4{hval(i, j, 0), hval(i, j, 1), hval(i, j, 2), hval(i, j, 3)};
+                        }
+                    } else {
+                        static_assert(RB % 4 == 0, "bf16 H stores pair blocks");
+#pragma unroll
+                        for (int i = 0; i < RB / 2; i += 2) {
+                            const float ha[4] = {hval(i, j, 0), hval(i, j, 1), hval(i, j, 2), hval(i, j, 3)};
+                            const float hb[4] = {hval(i + 1, j, 0), hval(i + 1, j, 1), hval(i + 1, j, 2),
+                                                 hval(i + 1, j, 3)};
+                            store_pair_bf16((uint16_t *)P.out + R * F, n0 + wf * (BF / WF) + i * 16, ha, hb, lane, F);
                         }
                     }
                 }
@@ -500,15 +524,18 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                 const int tok = (j * WM + wm) * 16 + (lane & 15);
                 if (tok >= valid) continue;
                 const int64_t R = rbase + tok;
+                if (DT == DT_F32) {
 #pragma unroll
-                for (int i = 0; i < RB; ++i) {
-                    const int f = n0 + wf * WRW + i * 16 + 4 * (lane >> 4);
-                    if (f >= F) continue;
-                    if (DT == DT_F32) {
-                        *(f32x4 *)((float *)P.out + R * F + f) = acc[i][j];
-                    } else {
-                        *(u32x2 *)((uint16_t *)P.out + R * F + f) =
-                            u32x2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+                    for (int i = 0; i < RB; ++i) {
+                        const int f = n0 + wf * WRW + i * 16 + 4 * (lane >> 4);
+                        if (f < F) *(f32x4 *)((float *)P.out + R * F + f) = acc[i][j];
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < RB; i += 2) {
+                        const float ya[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                        const float yb[4] = {acc[i + 1][j][0], acc[i + 1][j][1], acc[i + 1][j][2], acc[i + 1][j][3]};
+                        store_pair_bf16((uint16_t *)P.out + R * F, n0 + wf * WRW + i * 16, ya, yb, lane, F);
                     }
                 }
             }
