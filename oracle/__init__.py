@@ -22,7 +22,7 @@ import threading
 
 import numpy as np
 
-F32, BF16, E4M3 = 0, 1, 2
+F32, BF16, E4M3, F64 = 0, 1, 2, 3
 ADD_RESIDUAL = 1
 NC = 128
 
@@ -83,6 +83,11 @@ def _load():
                                                + [P] * 4 + [P] * 6 + [P] * 6 + [P] * 4)
             lib.oracle_bias_update.restype = None
             lib.oracle_bias_update.argtypes = [i32, i64, i32, P, P, f32]
+            lib.oracle_layer_f64.restype = i32
+            lib.oracle_layer_f64.argtypes = [i64, i32, i32, i32, i32, i32, i32, P, P, P, i32] + [P] * 6 + [P, P]
+            lib.oracle_moe_backward_f64.restype = i32
+            lib.oracle_moe_backward_f64.argtypes = ([i64, i32, i32, i32, i32, i32, i32, P, P, P, i32] + [P] * 6
+                                                    + [P, i64, P, i32, P] + [P] * 9)
             lib.oracle_seq_balance.restype = None
             lib.oracle_seq_balance.argtypes = [i64, i32, i32, P, P, i64, f32, P, P, P]
             lib.oracle_num_threads.restype = i32
@@ -113,7 +118,9 @@ def _storage(a):
         return F32, a
     if a.dtype == np.uint16:
         return BF16, a
-    raise TypeError("oracle inputs are float32 or bf16 bit patterns (uint16), got %s" % a.dtype)
+    if a.dtype == np.float64:
+        return F64, a
+    raise TypeError("oracle inputs are float32, float64 or bf16 bit patterns (uint16), got %s" % a.dtype)
 
 
 def _empty_like_code(code, shape):
@@ -338,6 +345,66 @@ def bias_update(counts, bias, T, K, gamma=0.001):
     b = np.array(bias, dtype=np.float32, copy=True)
     _load().oracle_bias_update(b.shape[0], T, K, _p(counts), _p(b), gamma)
     return b
+
+
+def _layer_args(u, gate_w, topk_idx, routed, shared):
+    au, u = _storage(u)
+    ag, gate_w = _storage(gate_w)
+    if au != ag:
+        raise TypeError("u and gate_w must share a storage format")
+    topk_idx = _c(topk_idx, np.int32)
+    ws = [_storage(w) for w in routed] + ([_storage(w) for w in shared] if shared is not None else [])
+    codes = {c for c, _ in ws}
+    if len(codes) != 1:
+        raise TypeError("expert weights must share a storage format")
+    T, d = u.shape
+    Nr = gate_w.shape[0]
+    I = routed[0].shape[1]
+    Ns = shared[0].shape[0] if shared is not None else 0
+    K = topk_idx.shape[1]
+    arrs = [w for _, w in ws] + [None] * (6 - len(ws))
+    return T, d, Nr, Ns, K, I, au, u, gate_w, topk_idx, codes.pop(), arrs
+
+
+def layer_f64(u, gate_w, topk_idx, routed, shared):
+    """The layer with nothing rounded after decoding the inputs, for a fixed
+    selection topk_idx (§2.1.2): returns (out [T, d] float64, gates [T, K]
+    float64).  Inputs in float32, bf16 bits or float64."""
+    T, d, Nr, Ns, K, I, au, u, gate_w, idx, wc, arrs = _layer_args(u, gate_w, topk_idx, routed, shared)
+    out = np.empty((T, d), np.float64)
+    g = np.empty((T, K), np.float64)
+    rc = _load().oracle_layer_f64(T, d, Nr, Ns, K, I, au, _p(u), _p(gate_w), _p(idx), wc, *[_p(a) for a in arrs],
+                                  _p(out), _p(g))
+    if rc:
+        raise ValueError("oracle_layer_f64 rc=%d" % rc)
+    return out, g
+
+
+def moe_backward(u, gate_w, topk_idx, routed, shared, dout, tokens=None, experts=None, dgate=True, dshared=True):
+    """Gradient of sum(dout * layer(...)) by the chain rule in fp64 for a fixed
+    selection (see layer_f64).  Returns a dict with
+      du [T, d] and dg [T, K] (rows of the listed tokens; others zero),
+      dgate_w [Nr, d] (if dgate), dwg/dwu/dwd [len(experts) or Nr, ...] for the
+      listed routed experts, dswg/dswu/dswd [Ns, ...] (if dshared)."""
+    T, d, Nr, Ns, K, I, au, u, gate_w, idx, wc, arrs = _layer_args(u, gate_w, topk_idx, routed, shared)
+    dout = _c(dout, np.float64)
+    tok = None if tokens is None else _c(tokens, np.int64)
+    exps = None if experts is None else _c(experts, np.int32)
+    ne = Nr if exps is None else exps.shape[0]
+    r = dict(du=np.zeros((T, d)), dg=np.zeros((T, K)),
+             dgate_w=np.empty((Nr, d)) if dgate else None,
+             dwg=np.empty((ne, I, d)), dwu=np.empty((ne, I, d)), dwd=np.empty((ne, d, I)),
+             dswg=np.empty((Ns, I, d)) if dshared and Ns else None,
+             dswu=np.empty((Ns, I, d)) if dshared and Ns else None,
+             dswd=np.empty((Ns, d, I)) if dshared and Ns else None)
+    rc = _load().oracle_moe_backward_f64(T, d, Nr, Ns, K, I, au, _p(u), _p(gate_w), _p(idx), wc,
+                                         *[_p(a) for a in arrs], _p(dout), 0 if tok is None else tok.shape[0],
+                                         _p(tok), 0 if exps is None else exps.shape[0], _p(exps),
+                                         _p(r["du"]), _p(r["dg"]), _p(r["dgate_w"]), _p(r["dwg"]), _p(r["dwu"]),
+                                         _p(r["dwd"]), _p(r["dswg"]), _p(r["dswu"]), _p(r["dswd"]))
+    if rc:
+        raise ValueError("oracle_moe_backward_f64 rc=%d" % rc)
+    return r
 
 
 def seq_balance(scores, topk_idx, seq_len, alpha=1e-4):

@@ -40,7 +40,7 @@
 #include <omp.h>
 #endif
 
-enum { OR_F32 = 0, OR_BF16 = 1, OR_E4M3 = 2 };
+enum { OR_F32 = 0, OR_BF16 = 1, OR_E4M3 = 2, OR_F64 = 3 };   /* F64: exact storage, for gradient checks */
 enum { OR_ADD_RESIDUAL = 1u };
 
 #define OR_NC 128          /* quantisation group size N_c (§3.3) */
@@ -131,6 +131,7 @@ static void init_tables(void)
 /* Value of element i of a row stored in dtype (fp32, bf16).  */
 static inline double load_plain(int dtype, const void *p, int64_t i)
 {
+    if (dtype == OR_F64) return ((const double *)p)[i];
     if (dtype == OR_F32) return (double)((const float *)p)[i];
     return dec_bf16(((const uint16_t *)p)[i]);
 }
@@ -611,6 +612,308 @@ void oracle_seq_balance(int64_t T, int Nr, int K, const float *scores, const int
         free(cnt);
         free(share);
     }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exact layer and its gradient for a fixed selection (backward reference)   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The layer of §2.1.2 evaluated in fp64 with nothing rounded after the inputs
+ * are decoded, for a given selection topk_idx [T][K] (held fixed: the
+ * selection is piecewise constant, so the layer is smooth in u, the centroids
+ * and the weights wherever the selection does not change):
+ *   s_{t,i} = sigmoid(u_t . e_i),  g_{t,j} = s_{t,e_j} / sum_k s_{t,e_k},
+ *   out_t = sum_j g_{t,j} FFN_{e_j}(u_t) + sum_s FFN^shared_s(u_t),
+ *   FFN(x) = W_down (SiLU(W_gate x) * (W_up x)).
+ * u [T][d] and gate_w [Nr][d] are stored in a_code, the weights in w_code
+ * (OR_F32, OR_BF16 or OR_F64): routed [Nr][I][d], [Nr][I][d], [Nr][d][I],
+ * shared [Ns][...].  out [T][d] and topk_w [T][K] (may be NULL) are fp64.
+ */
+typedef struct { int code; const void *p; } omat;
+
+static void orow(omat m, int64_t r, int n, double *out)
+{
+    for (int c = 0; c < n; ++c) out[c] = load_plain(m.code, m.p, r * n + c);
+}
+
+static omat osub(omat m, int64_t e, size_t elems)
+{
+    const size_t esz = m.code == OR_F64 ? 8 : m.code == OR_F32 ? 4 : 2;
+    omat r = {m.code, (const char *)m.p + (size_t)e * elems * esz};
+    return r;
+}
+
+/* a = W_gate x, b = W_up x, h = SiLU(a) b, y = W_down h (all fp64); row: d+I scratch */
+static void ffn64(int d, int I, omat wg, omat wu, omat wd, const double *x, double *a, double *b, double *h,
+                  double *y, double *row)
+{
+    for (int k = 0; k < I; ++k) {
+        orow(wg, k, d, row);
+        a[k] = dot(x, row, d);
+        orow(wu, k, d, row);
+        b[k] = dot(x, row, d);
+        h[k] = a[k] / (1.0 + exp(-a[k])) * b[k];
+    }
+    for (int i = 0; i < d; ++i) {
+        orow(wd, i, I, row);
+        y[i] = dot(h, row, I);
+    }
+}
+
+static void gates64(int d, int K, const double *x, omat gate_w, const int32_t *sel, double *s_sel, double *g,
+                    double *row)
+{
+    double den = 0.0;
+    for (int j = 0; j < K; ++j) {
+        orow(gate_w, sel[j], d, row);
+        s_sel[j] = 1.0 / (1.0 + exp(-dot(x, row, d)));
+        den += s_sel[j];
+    }
+    for (int j = 0; j < K; ++j) g[j] = s_sel[j] / den;
+}
+
+/* dh = W_down^T dy (sum over the d rows of W_down in order); row: I scratch */
+static void down_t(int d, int I, omat wd, const double *dy, double *dh, double *row)
+{
+    for (int k = 0; k < I; ++k) dh[k] = 0.0;
+    for (int c = 0; c < d; ++c) {
+        orow(wd, c, I, row);
+        for (int k = 0; k < I; ++k) dh[k] += row[k] * dy[c];
+    }
+}
+
+int oracle_layer_f64(int64_t T, int d, int Nr, int Ns, int K, int I, int a_code, const void *u, const void *gate_w,
+                     const int32_t *topk_idx, int w_code, const void *rwg, const void *rwu, const void *rwd,
+                     const void *swg, const void *swu, const void *swd, double *out, double *topk_w)
+{
+    const size_t wm = (size_t)I * d;
+    const omat U = {a_code, u}, E = {a_code, gate_w};
+    const omat RG = {w_code, rwg}, RU = {w_code, rwu}, RD = {w_code, rwd};
+    const omat SG = {w_code, swg}, SU = {w_code, swu}, SD = {w_code, swd};
+    if (K > 32) return -2;
+    (void)Nr;
+#pragma omp parallel
+    {
+        double *a = malloc(sizeof(double) * (size_t)I), *b = malloc(sizeof(double) * (size_t)I);
+        double *h = malloc(sizeof(double) * (size_t)I), *y = malloc(sizeof(double) * (size_t)d);
+        double *x = malloc(sizeof(double) * (size_t)d), *row = malloc(sizeof(double) * (size_t)(d + I));
+        double s_sel[32], g[32];
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < T; ++t) {
+            double *o = out + (size_t)t * d;
+            orow(U, t, d, x);
+            gates64(d, K, x, E, topk_idx + t * K, s_sel, g, row);
+            if (topk_w)
+                for (int j = 0; j < K; ++j) topk_w[t * K + j] = g[j];
+            for (int i = 0; i < d; ++i) o[i] = 0.0;
+            for (int j = 0; j < K + Ns; ++j) {
+                const int routed = j < K, e = routed ? topk_idx[t * K + j] : j - K;
+                ffn64(d, I, osub(routed ? RG : SG, e, wm), osub(routed ? RU : SU, e, wm), osub(routed ? RD : SD, e, wm),
+                      x, a, b, h, y, row);
+                const double gj = routed ? g[j] : 1.0;
+                for (int i = 0; i < d; ++i) o[i] += gj * y[i];
+            }
+        }
+        free(a); free(b); free(h); free(y); free(x); free(row);
+    }
+    return 0;
+}
+
+/*
+ * Gradient of sum(dout * out) for the layer above (dout [T][d] fp64), by the
+ * chain rule written out in fp64:
+ *   dy_{t,j} = g_{t,j} dout_t,   dg_{t,j} = dout_t . y_{t,j}
+ *   per expert row: dh = W_down^T dy,  dW_down += dy h^T,
+ *     da = dh * b * SiLU'(a) with SiLU'(a) = sigma(a) (1 + a (1 - sigma(a))),
+ *     db = dh * SiLU(a),  dx = W_gate^T da + W_up^T db,
+ *     dW_gate += da x^T,  dW_up += db x^T
+ *   gates g_j = s_j / D (D = sum of the selected s):
+ *     ds_k = dg_k / D - (sum_j dg_j s_j) / D^2 for selected k (no other expert
+ *     receives gate gradient; the bias receives none),
+ *   dz = ds * s (1 - s),  du_t += sum_j dx_{t,j} + dx_shared + sum_k dz_k e_k,
+ *   de_k += dz_k u_t.
+ * Subsets: du [T][d] and dtopk_w [T][K] rows are written for the listed tokens
+ * only (tok = NULL: all T).  Routed weight gradients are written for the listed
+ * experts (exps = NULL: all Nr), the q-th listed expert's into slot q of
+ * drwg/drwu/drwd ([n][I][d], [n][I][d], [n][d][I]); each sums over every token
+ * routed to it, in token order.  Shared weight gradients ([Ns][...]) and
+ * dgate_w ([Nr][d], every token) only when their pointers are non-NULL.
+ */
+int oracle_moe_backward_f64(int64_t T, int d, int Nr, int Ns, int K, int I, int a_code, const void *u,
+                            const void *gate_w, const int32_t *topk_idx, int w_code, const void *rwg, const void *rwu,
+                            const void *rwd, const void *swg, const void *swu, const void *swd, const double *dout,
+                            int64_t n_tok, const int64_t *tok, int n_exp, const int32_t *exps,
+                            double *du, double *dtopk_w, double *dgate_w,
+                            double *drwg, double *drwu, double *drwd,
+                            double *dswg, double *dswu, double *dswd)
+{
+    const size_t wm = (size_t)I * d;
+    const omat U = {a_code, u}, E = {a_code, gate_w};
+    const omat RG = {w_code, rwg}, RU = {w_code, rwu}, RD = {w_code, rwd};
+    const omat SG = {w_code, swg}, SU = {w_code, swu}, SD = {w_code, swd};
+    if (K > 32) return -2;
+    /* per-token input gradient (and gate gradient) for the listed tokens */
+    if (du || dtopk_w) {
+#pragma omp parallel
+        {
+            double *a = malloc(sizeof(double) * (size_t)I), *b = malloc(sizeof(double) * (size_t)I);
+            double *h = malloc(sizeof(double) * (size_t)I), *y = malloc(sizeof(double) * (size_t)d);
+            double *dh = malloc(sizeof(double) * (size_t)I), *dx = malloc(sizeof(double) * (size_t)d);
+            double *x = malloc(sizeof(double) * (size_t)d), *row = malloc(sizeof(double) * (size_t)(d + I));
+            double *da = malloc(sizeof(double) * (size_t)I), *db = malloc(sizeof(double) * (size_t)I);
+            double *dy = malloc(sizeof(double) * (size_t)d);
+            double s_sel[32], g[32], dg[32];
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t n = 0; n < (tok ? n_tok : T); ++n) {
+                const int64_t t = tok ? tok[n] : n;
+                const double *dO = dout + (size_t)t * d;
+                const int32_t *sel = topk_idx + t * K;
+                orow(U, t, d, x);
+                gates64(d, K, x, E, sel, s_sel, g, row);
+                for (int c = 0; c < d; ++c) dx[c] = 0.0;
+                for (int j = 0; j < K + Ns; ++j) {
+                    const int routed = j < K, e = routed ? sel[j] : j - K;
+                    const omat wg = osub(routed ? RG : SG, e, wm), wu = osub(routed ? RU : SU, e, wm);
+                    const omat wd = osub(routed ? RD : SD, e, wm);
+                    ffn64(d, I, wg, wu, wd, x, a, b, h, y, row);
+                    const double gj = routed ? g[j] : 1.0;
+                    if (routed) dg[j] = dot(dO, y, d);
+                    for (int c = 0; c < d; ++c) dy[c] = gj * dO[c];
+                    down_t(d, I, wd, dy, dh, row);
+                    for (int k = 0; k < I; ++k) {
+                        const double sg = 1.0 / (1.0 + exp(-a[k]));
+                        da[k] = dh[k] * b[k] * sg * (1.0 + a[k] * (1.0 - sg));
+                        db[k] = dh[k] * a[k] * sg;
+                    }
+                    for (int k = 0; k < I; ++k) {
+                        orow(wg, k, d, row);
+                        for (int c = 0; c < d; ++c) dx[c] += row[c] * da[k];
+                        orow(wu, k, d, row);
+                        for (int c = 0; c < d; ++c) dx[c] += row[c] * db[k];
+                    }
+                }
+                double den = 0.0, sdg = 0.0;
+                for (int j = 0; j < K; ++j) { den += s_sel[j]; sdg += dg[j] * s_sel[j]; }
+                for (int j = 0; j < K; ++j) {
+                    const double dz = (dg[j] / den - sdg / (den * den)) * s_sel[j] * (1.0 - s_sel[j]);
+                    orow(E, sel[j], d, row);
+                    for (int c = 0; c < d; ++c) dx[c] += dz * row[c];
+                }
+                if (du)
+                    for (int c = 0; c < d; ++c) du[(size_t)t * d + c] = dx[c];
+                if (dtopk_w)
+                    for (int j = 0; j < K; ++j) dtopk_w[t * K + j] = dg[j];
+            }
+            free(a); free(b); free(h); free(y); free(dh); free(dx); free(x); free(row); free(da); free(db); free(dy);
+        }
+    }
+    /* centroid gradient: every token contributes dz_k u_t to its selected experts */
+    if (dgate_w) {
+        for (size_t q = 0; q < (size_t)Nr * d; ++q) dgate_w[q] = 0.0;
+        double *dzall = malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * K);
+#pragma omp parallel
+        {
+            double *a = malloc(sizeof(double) * (size_t)I), *b = malloc(sizeof(double) * (size_t)I);
+            double *h = malloc(sizeof(double) * (size_t)I), *y = malloc(sizeof(double) * (size_t)d);
+            double *x = malloc(sizeof(double) * (size_t)d), *row = malloc(sizeof(double) * (size_t)(d + I));
+            double s_sel[32], g[32], dg[32];
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t t = 0; t < T; ++t) {
+                const double *dO = dout + (size_t)t * d;
+                const int32_t *sel = topk_idx + t * K;
+                orow(U, t, d, x);
+                gates64(d, K, x, E, sel, s_sel, g, row);
+                double den = 0.0, sdg = 0.0;
+                for (int j = 0; j < K; ++j) {
+                    ffn64(d, I, osub(RG, sel[j], wm), osub(RU, sel[j], wm), osub(RD, sel[j], wm), x, a, b, h, y, row);
+                    dg[j] = dot(dO, y, d);
+                    den += s_sel[j];
+                    sdg += dg[j] * s_sel[j];
+                }
+                for (int j = 0; j < K; ++j)
+                    dzall[t * K + j] = (dg[j] / den - sdg / (den * den)) * s_sel[j] * (1.0 - s_sel[j]);
+            }
+            free(a); free(b); free(h); free(y); free(x); free(row);
+        }
+        for (int64_t t = 0; t < T; ++t)          /* tokens in order: fixed summation order */
+            for (int j = 0; j < K; ++j) {
+                double *de = dgate_w + (size_t)topk_idx[t * K + j] * d;
+                for (int c = 0; c < d; ++c) de[c] += dzall[t * K + j] * load_plain(a_code, u, t * d + c);
+            }
+        free(dzall);
+    }
+    /* weight gradients: routed experts (listed) over the tokens routed to them, then shared.
+     * Phase 1 (parallel over the expert's tokens): x, dy, h, da, db of each token.
+     * Phase 2 (parallel over output rows): the outer products summed over the tokens in order. */
+    for (int pass = 0; pass < 2; ++pass) {
+        const int nE = pass == 0 ? (exps ? n_exp : (drwg ? Nr : 0)) : (dswg ? Ns : 0);
+        for (int q = 0; q < nE; ++q) {
+            const int e = pass == 0 ? (exps ? exps[q] : q) : q;
+            const omat wg = osub(pass ? SG : RG, e, wm), wu = osub(pass ? SU : RU, e, wm);
+            const omat wd = osub(pass ? SD : RD, e, wm);
+            double *gwg = (pass ? dswg : drwg) + q * wm, *gwu = (pass ? dswu : drwu) + q * wm;
+            double *gwd = (pass ? dswd : drwd) + q * wm;
+            int64_t nt = 0;
+            int64_t *tl = malloc(sizeof(int64_t) * (size_t)(T > 0 ? T : 1));
+            int *jl = malloc(sizeof(int) * (size_t)(T > 0 ? T : 1));
+            for (int64_t t = 0; t < T; ++t) {
+                if (pass) { tl[nt] = t; jl[nt++] = -1; continue; }
+                for (int j = 0; j < K; ++j)
+                    if (topk_idx[t * K + j] == e) { tl[nt] = t; jl[nt++] = j; }
+            }
+            const size_t per = 2 * (size_t)d + 3 * (size_t)I;   /* x[d], dy[d], h[I], da[I], db[I] */
+            double *buf = malloc(sizeof(double) * per * (size_t)(nt > 0 ? nt : 1));
+#pragma omp parallel
+            {
+                double *a = malloc(sizeof(double) * (size_t)I), *b = malloc(sizeof(double) * (size_t)I);
+                double *y = malloc(sizeof(double) * (size_t)d), *row = malloc(sizeof(double) * (size_t)(d + I));
+                double *dh = malloc(sizeof(double) * (size_t)I);
+                double s_sel[32], g[32];
+#pragma omp for schedule(dynamic, 1)
+                for (int64_t n = 0; n < nt; ++n) {
+                    const int64_t t = tl[n];
+                    double *x = buf + per * n, *dy = x + d, *h = dy + d, *da = h + I, *db = da + I;
+                    orow(U, t, d, x);
+                    double gj = 1.0;
+                    if (!pass) {
+                        gates64(d, K, x, E, topk_idx + t * K, s_sel, g, row);
+                        gj = g[jl[n]];
+                    }
+                    ffn64(d, I, wg, wu, wd, x, a, b, h, y, row);
+                    for (int c = 0; c < d; ++c) dy[c] = gj * dout[(size_t)t * d + c];
+                    down_t(d, I, wd, dy, dh, row);
+                    for (int k = 0; k < I; ++k) {
+                        const double sg = 1.0 / (1.0 + exp(-a[k]));
+                        da[k] = dh[k] * b[k] * sg * (1.0 + a[k] * (1.0 - sg));
+                        db[k] = dh[k] * a[k] * sg;
+                    }
+                }
+                free(a); free(b); free(y); free(row); free(dh);
+            }
+#pragma omp parallel for schedule(static)
+            for (int c = 0; c < d; ++c)
+                for (int k = 0; k < I; ++k) {
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < nt; ++n) acc += buf[per * n + d + c] * buf[per * n + 2 * d + k];
+                    gwd[(size_t)c * I + k] = acc;
+                }
+#pragma omp parallel for schedule(static)
+            for (int k = 0; k < I; ++k)
+                for (int c = 0; c < d; ++c) {
+                    double ag = 0.0, au = 0.0;
+                    for (int64_t n = 0; n < nt; ++n) {
+                        const double xc = buf[per * n + c];
+                        ag += buf[per * n + 2 * d + I + k] * xc;
+                        au += buf[per * n + 2 * d + 2 * I + k] * xc;
+                    }
+                    gwg[(size_t)k * d + c] = ag;
+                    gwu[(size_t)k * d + c] = au;
+                }
+            free(buf); free(tl); free(jl);
+        }
+    }
+    return 0;
 }
 
 int oracle_num_threads(void)

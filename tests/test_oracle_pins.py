@@ -517,3 +517,103 @@ def test_seq_balance_invariants_and_sequence_split(orc):
     perm = np.concatenate([rng.permutation(L), np.arange(L, T)])
     lp, cp, _ = orc.seq_balance(scores[perm], idx[perm], L)
     assert (cp == counts).all() and abs(float(lp[0]) - float(loss[0])) <= 1e-6 * float(loss[0])
+
+
+# ---------------------------------------------------------------------------
+# backward of the layer (fixed selection): exact forward + chain-rule gradient
+# ---------------------------------------------------------------------------
+
+def _tiny_f64(seed, T=5, d=16, Nr=8, Ns=1, K=3, I=8):
+    rng = np.random.default_rng(seed)
+    u = rng.standard_normal((T, d))
+    e = rng.standard_normal((Nr, d)) / np.sqrt(d)
+    rw = (rng.standard_normal((Nr, I, d)) / np.sqrt(d), rng.standard_normal((Nr, I, d)) / np.sqrt(d),
+          rng.standard_normal((Nr, d, I)) / np.sqrt(I))
+    sw = (rng.standard_normal((Ns, I, d)) / np.sqrt(d), rng.standard_normal((Ns, I, d)) / np.sqrt(d),
+          rng.standard_normal((Ns, d, I)) / np.sqrt(I))
+    idx = np.stack([rng.permutation(Nr)[:K] for _ in range(T)]).astype(np.int32)
+    dout = rng.standard_normal((T, d))
+    return u, e, idx, rw, sw, dout
+
+
+def test_exact_layer_matches_the_rounding_forward(orc):
+    """layer_f64 on fp32 inputs equals the fp32-storage forward oracle (same
+    selection) to fp32 rounding: two independent codings of one layer."""
+    cfg = syn.CONFIGS["tiny"]
+    inp = syn.layer_inputs(cfg)
+    out_r, idx, w, _ = orc.moe_forward(inp["u"], inp["gate_w"], inp["bias"], (inp["wg"], inp["wu"], inp["wd"]),
+                                       (inp["swg"], inp["swu"], inp["swd"]), G=cfg.G, Mg=cfg.Mg, K=cfg.K,
+                                       w_code=orc.F32, out_code=orc.F32)
+    out_x, g = orc.layer_f64(inp["u"], inp["gate_w"], idx, (inp["wg"], inp["wu"], inp["wd"]),
+                             (inp["swg"], inp["swu"], inp["swd"]))
+    assert np.abs(g - w).max() <= 4e-7
+    assert np.abs(out_x - out_r).max() <= 2e-5 * np.abs(out_x).max()
+
+
+def test_backward_matches_finite_differences(orc):
+    """Central differences of sum(dout * layer) agree with the chain-rule
+    gradient for u, the centroids and all six weight tensors."""
+    u, e, idx, rw, sw, dout = _tiny_f64(11)
+    g = orc.moe_backward(u, e, idx, rw, sw, dout)
+
+    def loss(u_, e_, rw_, sw_):
+        return float((orc.layer_f64(u_, e_, idx, rw_, sw_)[0] * dout).sum())
+
+    rng = np.random.default_rng(3)
+    h = 1e-6
+    checks = 0
+    for name in ("u", "e", "rwg", "rwu", "rwd", "swg", "swu", "swd"):
+        for _ in range(6):
+            arrs = dict(u=u.copy(), e=e.copy(), rwg=rw[0].copy(), rwu=rw[1].copy(), rwd=rw[2].copy(),
+                        swg=sw[0].copy(), swu=sw[1].copy(), swd=sw[2].copy())
+            a = arrs[name]
+            pos = tuple(rng.integers(0, n) for n in a.shape)
+            if name == "e":   # a centroid that some token selected (others have zero gradient)
+                pos = (int(idx[rng.integers(0, idx.shape[0]), rng.integers(0, idx.shape[1])]),) + pos[1:]
+            grads = dict(u=g["du"], e=g["dgate_w"], rwg=g["dwg"], rwu=g["dwu"], rwd=g["dwd"],
+                         swg=g["dswg"], swu=g["dswu"], swd=g["dswd"])
+            v0 = a[pos]
+            a[pos] = v0 + h
+            lp = loss(arrs["u"], arrs["e"], (arrs["rwg"], arrs["rwu"], arrs["rwd"]), (arrs["swg"], arrs["swu"], arrs["swd"]))
+            a[pos] = v0 - h
+            lm = loss(arrs["u"], arrs["e"], (arrs["rwg"], arrs["rwu"], arrs["rwd"]), (arrs["swg"], arrs["swu"], arrs["swd"]))
+            fd = (lp - lm) / (2 * h)
+            an = grads[name][pos]
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (name, pos, fd, an)
+            checks += 1
+    assert checks == 48
+    # unselected centroids get no gradient
+    unused = sorted(set(range(e.shape[0])) - set(idx.ravel().tolist()))
+    assert all((g["dgate_w"][i] == 0).all() for i in unused)
+
+
+def test_backward_single_expert_is_dense_swiglu_autograd(orc):
+    """N_r = K = 1: the gate is s/s = 1, so the centroid gets no gradient and
+    the rest is the gradient of two dense SwiGLU FFNs, here taken from torch
+    autograd in float64."""
+    u, e, _, rw, sw, dout = _tiny_f64(5, T=7, Nr=1, K=1)
+    idx = np.zeros((7, 1), np.int32)
+    g = orc.moe_backward(u, e, idx, rw, sw, dout)
+    assert np.abs(g["dgate_w"]).max() <= 1e-15
+    tu = torch.tensor(u, requires_grad=True)
+    ws = [torch.tensor(w[0], requires_grad=True) for w in rw + sw]
+
+    def ffn(x, wg, wu, wd):
+        return torch.nn.functional.silu(x @ wg.T) * (x @ wu.T) @ wd.T
+
+    out = ffn(tu, *ws[:3]) + ffn(tu, *ws[3:])
+    (out * torch.tensor(dout)).sum().backward()
+    assert np.allclose(g["du"], tu.grad.numpy(), rtol=1e-12, atol=1e-12)
+    for mine, ref in zip((g["dwg"][0], g["dwu"][0], g["dwd"][0], g["dswg"][0], g["dswu"][0], g["dswd"][0]), ws):
+        assert np.allclose(mine, ref.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_backward_token_and_expert_subsets(orc):
+    """Listing tokens or experts gives the same rows as the full computation."""
+    u, e, idx, rw, sw, dout = _tiny_f64(8, T=9, Nr=6, K=2)
+    full = orc.moe_backward(u, e, idx, rw, sw, dout)
+    sub = orc.moe_backward(u, e, idx, rw, sw, dout, tokens=[2, 7], experts=[4, 1], dgate=False, dshared=False)
+    assert (sub["du"][[2, 7]] == full["du"][[2, 7]]).all() and (sub["du"][[0, 1, 3]] == 0).all()
+    assert (sub["dg"][[2, 7]] == full["dg"][[2, 7]]).all()
+    for k in ("dwg", "dwu", "dwd"):
+        assert (sub[k][0] == full[k][4]).all() and (sub[k][1] == full[k][1]).all()
