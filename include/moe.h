@@ -186,7 +186,10 @@ int moe_combine(const moe_shape *shape, const void *y_perm, const int32_t *inv_p
  * memory; their elements are device pointers.)
  * Optional outputs (NULL to skip): topk_idx_out [T][K], topk_w_out [T][K],
  * counts_out [N_r], scores_out [T][N_r].
- * ws: moe_workspace_bytes(shape, MOE_WS_FORWARD).
+ * ws: moe_workspace_bytes(shape, MOE_WS_FORWARD).  After the call it holds the
+ * layer's saved activations (affinities, selection, gates, dispatch, H and the
+ * expert outputs) that moe_backward reads; scores_out, topk_idx_out and
+ * topk_w_out receive copies.
  */
 int moe_forward(const moe_shape *shape, const void *u, const void *gate_w, const float *bias,
                 const void *const *routed_w, const float *const *routed_s,
@@ -210,6 +213,63 @@ int moe_forward_timed(const moe_shape *shape, const void *u, const void *gate_w,
                       const void *const *shared_w, const float *const *shared_s,
                       void *out, int32_t *topk_idx_out, float *topk_w_out, int32_t *counts_out,
                       float *scores_out, void *ws, size_t ws_bytes, void *stream, void *const *stage_events);
+
+/* ------------------------------------------------------------------------ */
+/* backward                                                                 */
+
+/*
+ * moe_transpose_expert_weights -- the transposed weight copies moe_backward
+ * reads (input gradients run through the same grouped expert kernel as the
+ * forward, which wants the reduction dimension contiguous):
+ *   w_down_t    [n][I][d]  = W_down^T per expert,
+ *   w_gate_up_t [n][d][2I] = [W_gate^T | W_up^T] per expert.
+ * w_gate, w_up [n][I][d], w_down [n][d][I] in shape->w_dtype (MOE_F32 or
+ * MOE_BF16); the copies are bit-exact.  Rebuild them whenever the weights
+ * change.  n = N_r for the routed and N_s for the shared experts.
+ * Errors: MOE_ERR_UNSUPPORTED for E4M3 shapes.
+ */
+int moe_transpose_expert_weights(const moe_shape *shape, int32_t n, const void *w_gate, const void *w_up,
+                                 const void *w_down, void *w_down_t, void *w_gate_up_t, void *stream);
+
+/*
+ * moe_backward -- gradient of the layer (§2.1.2) for the selection that
+ * moe_forward made, given dout = dL/dh'_t [T][d]; the selection and the bias
+ * are piecewise constant and take no gradient (reading: the balancing bias
+ * moves only by the moe_bias_update rule).  For output row t,
+ *   dy_{t,j} = g_{t,j} dout_t,   dg_{t,j} = dout_t . y_{t,j}   (y = expert output)
+ *   expert (SwiGLU h = SiLU(a) * b, a = W_gate x, b = W_up x, y = W_down h):
+ *     dh = W_down^T dy,  da = dh b SiLU'(a),  db = dh SiLU(a),
+ *     dx = W_gate^T da + W_up^T db,
+ *     dW_down = sum dy h^T,  dW_gate = sum da x^T,  dW_up = sum db x^T
+ *   gate g_j = rs s_j / D, D = sum_k s_k over the selected k (rs = routed_scale):
+ *     ds_j = rs (dg_j / D - (sum_k dg_k s_k) / D^2),  dz_j = ds_j s_j (1 - s_j)
+ *     (z = u . e, s = sigmoid(z)),
+ *   du_t = sum_j dx_{t,j} + sum_shared dx + sum_j dz_j e_{sel_j},
+ *   de_i = sum over slots routed to i of dz u_t.
+ * (With MOE_ADD_RESIDUAL the residual's own gradient, dout, is the caller's
+ * to add: du holds the layer's part only.)
+ * Inputs: u, gate_w and the weights exactly as passed to moe_forward;
+ * routed_wt = {w_down_t, w_gate_up_t} from moe_transpose_expert_weights,
+ * shared_wt likewise (NULL when N_s == 0); fwd_ws/fwd_ws_bytes: the forward
+ * workspace of the moe_forward call whose output dout refers to, untouched
+ * since (it holds the scores, selection, dispatch, H and Y, which are the saved
+ * activations).  Storage: dout, du and the weight gradients in act_dtype.
+ * Outputs: du [T][d]; optional (NULL to skip): dgate_w [N_r][d] fp32,
+ * d_routed_w = {dW_gate, dW_up, dW_down} (layout of routed_w), d_shared_w
+ * likewise, dtopk_w [T][K] fp32 = dL/dg.  Gradients are written, not
+ * accumulated.  Sums run in fp32 in a fixed order (deterministic).
+ * ws: moe_backward_workspace_bytes(shape).
+ * Errors: MOE_ERR_UNSUPPORTED for E4M3 shapes; MOE_ERR_WORKSPACE when
+ * fwd_ws_bytes is smaller than moe_workspace_bytes(shape, MOE_WS_FORWARD).
+ */
+int moe_backward(const moe_shape *shape, const void *u, const void *gate_w, const void *const *routed_w,
+                 const void *const *routed_wt, const void *const *shared_w, const void *const *shared_wt,
+                 const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du, float *dgate_w,
+                 void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/* Workspace bytes for moe_backward (0 when rejected). */
+size_t moe_backward_workspace_bytes(const moe_shape *shape);
 
 /* ------------------------------------------------------------------------ */
 /* helpers                                                                  */

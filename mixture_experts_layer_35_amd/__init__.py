@@ -27,6 +27,7 @@ MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_FORWARD = 0, 1, 2
 EXPORTED = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_timed",
             "moe_workspace_bytes",
             "moe_ffn_workspace_bytes", "moe_bias_update", "moe_seq_balance", "moe_seq_balance_workspace_bytes",
+            "moe_transpose_expert_weights", "moe_backward", "moe_backward_workspace_bytes",
             "moe_quantize_1x128", "moe_quantize_weights_128x128", "moe_last_error", "moe_version")
 
 
@@ -79,6 +80,8 @@ def lib():
                 "moe_forward_timed": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P, P],
                 "moe_bias_update": [S, P, P, ctypes.c_float, P],
                 "moe_seq_balance": [S, P, P, i64, ctypes.c_float, P, P, P, P, sz, P],
+                "moe_transpose_expert_weights": [S, i32, P, P, P, P, P, P],
+                "moe_backward": [S, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, sz, P],
                 "moe_quantize_1x128": [i64, i32, i32, P, P, P, P],
                 "moe_quantize_weights_128x128": [i64, i32, i32, i32, P, P, P, P],
             }
@@ -92,6 +95,8 @@ def lib():
             L.moe_ffn_workspace_bytes.restype = sz
             L.moe_seq_balance_workspace_bytes.argtypes = [S, i64]
             L.moe_seq_balance_workspace_bytes.restype = sz
+            L.moe_backward_workspace_bytes.argtypes = [S]
+            L.moe_backward_workspace_bytes.restype = sz
             L.moe_last_error.argtypes = []
             L.moe_last_error.restype = ctypes.c_char_p
             L.moe_version.argtypes = []
@@ -227,6 +232,28 @@ def moe_seq_balance_workspace_bytes(shape: MoeShape, seq_len: int) -> int:
 def moe_seq_balance(shape, scores, topk_idx, seq_len, alpha, loss, counts=None, share=None, ws=None, stream=None):
     return _check(lib().moe_seq_balance(ctypes.byref(shape), _ptr(scores), _ptr(topk_idx), seq_len, alpha, _ptr(loss),
                                         _ptr(counts), _ptr(share), _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_transpose_expert_weights(shape, n, w_gate, w_up, w_down, w_down_t, w_gate_up_t, stream=None):
+    return _check(lib().moe_transpose_expert_weights(ctypes.byref(shape), n, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
+                                                     _ptr(w_down_t), _ptr(w_gate_up_t), _stream(stream)))
+
+
+def moe_backward_workspace_bytes(shape: MoeShape) -> int:
+    return lib().moe_backward_workspace_bytes(ctypes.byref(shape))
+
+
+def moe_backward(shape, u, gate_w, routed_w, routed_wt, shared_w, shared_wt, fwd_ws, dout, du, dgate_w=None,
+                 d_routed_w=None, d_shared_w=None, dtopk_w=None, ws=None, stream=None):
+    """routed_w / shared_w: (W_gate, W_up, W_down); *_wt: (W_down^T, [W_gate^T | W_up^T]); fwd_ws: the
+    workspace tensor of the forward call whose output dout refers to."""
+    rw, rt, sw, st, dr, ds = (_ptr_array(x) for x in (routed_w, routed_wt, shared_w, shared_wt, d_routed_w,
+                                                       d_shared_w))
+    return _check(lib().moe_backward(ctypes.byref(shape), _ptr(u), _ptr(gate_w), rw[0] if rw else None,
+                                     rt[0] if rt else None, sw[0] if sw else None, st[0] if st else None,
+                                     _ptr(fwd_ws), _nbytes(fwd_ws), _ptr(dout), _ptr(du), _ptr(dgate_w),
+                                     dr[0] if dr else None, ds[0] if ds else None, _ptr(dtopk_w), _ptr(ws),
+                                     _nbytes(ws), _stream(stream)))
 
 
 def moe_quantize_1x128(rows, cols, x_dtype, x, q, s, stream=None):

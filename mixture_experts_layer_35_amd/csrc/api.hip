@@ -159,11 +159,11 @@ int run_ffn_pair(const moe_shape *s, const FfnProblem *gu, const FfnProblem *dn,
     a.K = s->d;
     a.F = s->inter;
     for (int i = 0; i < nprob; ++i) a.p[i] = gu[i];
-    HIPCHK(launch_ffn(dt_of(s->w_dtype), true, a, st));
+    HIPCHK(launch_ffn(dt_of(s->w_dtype), FFN_GATEUP, a, st));
     a.K = s->inter;
     a.F = s->d;
     for (int i = 0; i < nprob; ++i) a.p[i] = dn[i];
-    HIPCHK(launch_ffn(dt_of(s->w_dtype), false, a, st));
+    HIPCHK(launch_ffn(dt_of(s->w_dtype), FFN_DOWN, a, st));
     return MOE_OK;
 }
 
@@ -369,9 +369,11 @@ int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, con
     hipStream_t st = (hipStream_t)stream;
     char *W = (char *)ws;
     const int64_t T = s->T, TK = T * s->topk;
-    float *scores = scores_out ? scores_out : (float *)(W + L.scores);
-    int32_t *idx = topk_idx_out ? topk_idx_out : (int32_t *)(W + L.idx);
-    float *tw = topk_w_out ? topk_w_out : (float *)(W + L.w);
+    // the workspace keeps the affinities, selection and gates (moe_backward reads them);
+    // the optional outputs get copies
+    float *scores = (float *)(W + L.scores);
+    int32_t *idx = (int32_t *)(W + L.idx);
+    float *tw = (float *)(W + L.w);
     int32_t *counts = counts_out ? counts_out : (int32_t *)(W + L.counts);
     int32_t *offsets = (int32_t *)(W + L.offsets);
     int32_t *bc = (int32_t *)(W + L.bc);
@@ -386,6 +388,10 @@ int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, con
     HIPCHK(launch_router_gemm(dt_of(s->act_dtype), u, gate_w, scores, T, s->d, s->n_routed, st));
     HIPCHK(launch_router_select(scores, bias, T, s->n_routed, s->n_groups, s->topk_groups, s->topk, s->routed_scale,
                                 idx, tw, st));
+    if (scores_out)
+        HIPCHK(hipMemcpyAsync(scores_out, scores, (size_t)T * s->n_routed * 4, hipMemcpyDeviceToDevice, st));
+    if (topk_idx_out) HIPCHK(hipMemcpyAsync(topk_idx_out, idx, (size_t)TK * 4, hipMemcpyDeviceToDevice, st));
+    if (topk_w_out) HIPCHK(hipMemcpyAsync(topk_w_out, tw, (size_t)TK * 4, hipMemcpyDeviceToDevice, st));
     HIPCHK(mark(1));
     // 2. dispatch bookkeeping (rows are gathered inside the expert GEMM)
     HIPCHK(launch_perm_hist(idx, T, s->topk, s->n_routed, bc, st));
@@ -448,12 +454,12 @@ int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, con
         // the shared experts' tiles go first: every workgroup starts at the same time, so the
         // row blocks of one shared weight block run together and share it through L2
         for (int i = 0; i < nprob; ++i) a.p[i] = gu[nprob - 1 - i];
-        HIPCHK(launch_ffn(dt_of(s->w_dtype), true, a, st));
+        HIPCHK(launch_ffn(dt_of(s->w_dtype), FFN_GATEUP, a, st));
         HIPCHK(mark(3));
         a.K = s->inter;
         a.F = s->d;
         for (int i = 0; i < nprob; ++i) a.p[i] = dn[nprob - 1 - i];
-        HIPCHK(launch_ffn(dt_of(s->w_dtype), false, a, st));
+        HIPCHK(launch_ffn(dt_of(s->w_dtype), FFN_DOWN, a, st));
         HIPCHK(mark(4));
     }
     // 5. gate-weighted combine plus shared experts
@@ -461,7 +467,254 @@ int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, con
                           s->n_shared ? W + L.ysh : nullptr, s->n_shared,
                           (s->flags & MOE_ADD_RESIDUAL) ? u : nullptr, out, T, s->d, s->topk, st));
     HIPCHK(mark(5));
-    (void)TK;
+    return MOE_OK;
+}
+
+// backward workspace: dy [TK][d], dg [TK], dz [TK], dh [R][I], dab [R][2I], dx [R][d] (R = TK + T*Ns)
+struct BwdLayout {
+    size_t dy, dg, dz, dh, dab, dx, total;
+};
+
+static BwdLayout bwd_layout(const moe_shape *s) {
+    BwdLayout L{};
+    const int64_t T = s->T, TK = T * s->topk, R = TK + T * s->n_shared;
+    const int a = esize(s->act_dtype);
+    size_t o = 0;
+    auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
+    L.dy = take((size_t)TK * s->d * a);
+    L.dg = take((size_t)TK * 4);
+    L.dz = take((size_t)TK * 4);
+    L.dh = take((size_t)R * s->inter * a);
+    L.dab = take((size_t)R * 2 * s->inter * a);
+    L.dx = take((size_t)R * s->d * a);
+    L.total = o;
+    return L;
+}
+
+static int check_bwd_shape(const moe_shape *s, const char *fn) {
+    int rc = check_shape(s, fn);
+    if (rc) return rc;
+    if (s->w_dtype == MOE_E4M3) return fail(MOE_ERR_UNSUPPORTED, "%s: the backward runs on fp32 / bf16 layers", fn);
+    return MOE_OK;
+}
+
+size_t moe_backward_workspace_bytes(const moe_shape *s) {
+    if (check_bwd_shape(s, "moe_backward_workspace_bytes") != MOE_OK) return 0;
+    return bwd_layout(s).total;
+}
+
+int moe_transpose_expert_weights(const moe_shape *s, int32_t n, const void *w_gate, const void *w_up,
+                                 const void *w_down, void *w_down_t, void *w_gate_up_t, void *stream) {
+    const char *fn = "moe_transpose_expert_weights";
+    int rc = check_bwd_shape(s, fn);
+    if (rc) return rc;
+    if (n < 0) return fail(MOE_ERR_INVALID_ARG, "%s: n < 0", fn);
+    if (n == 0) return MOE_OK;
+    NEED(w_gate);
+    NEED(w_up);
+    NEED(w_down);
+    NEED(w_down_t);
+    NEED(w_gate_up_t);
+    const int dt = dt_of(s->w_dtype), d = s->d, I = s->inter;
+    hipStream_t st = (hipStream_t)stream;
+    HIPCHK(launch_transpose(dt, w_down, n, d, I, w_down_t, d, 0, st));        // [n][d][I] -> [n][I][d]
+    HIPCHK(launch_transpose(dt, w_gate, n, I, d, w_gate_up_t, 2 * I, 0, st)); // [n][I][d] -> [n][d][0:I]
+    HIPCHK(launch_transpose(dt, w_up, n, I, d, w_gate_up_t, 2 * I, I, st));   // [n][I][d] -> [n][d][I:2I]
+    return MOE_OK;
+}
+
+int moe_backward(const moe_shape *s, const void *u, const void *gate_w, const void *const *routed_w,
+                 const void *const *routed_wt, const void *const *shared_w, const void *const *shared_wt,
+                 const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du, float *dgate_w,
+                 void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes,
+                 void *stream) {
+    const char *fn = "moe_backward";
+    int rc = check_bwd_shape(s, fn);
+    if (rc) return rc;
+    if (s->T == 0) return MOE_OK;
+    NEED(u);
+    NEED(gate_w);
+    NEED(routed_w);
+    NEED(routed_wt);
+    NEED(fwd_ws);
+    NEED(dout);
+    NEED(du);
+    if (!routed_w[0] || !routed_w[1] || !routed_w[2] || !routed_wt[0] || !routed_wt[1])
+        return fail(MOE_ERR_INVALID_ARG, "%s: routed weight entries must not be NULL", fn);
+    if (s->n_shared > 0) {
+        NEED(shared_w);
+        NEED(shared_wt);
+        if (!shared_w[0] || !shared_w[1] || !shared_w[2] || !shared_wt[0] || !shared_wt[1])
+            return fail(MOE_ERR_INVALID_ARG, "%s: shared weight entries must not be NULL", fn);
+    }
+    if (d_routed_w && (!d_routed_w[0] || !d_routed_w[1] || !d_routed_w[2]))
+        return fail(MOE_ERR_INVALID_ARG, "%s: d_routed_w entries must not be NULL", fn);
+    if (s->n_shared > 0 && d_shared_w && (!d_shared_w[0] || !d_shared_w[1] || !d_shared_w[2]))
+        return fail(MOE_ERR_INVALID_ARG, "%s: d_shared_w entries must not be NULL", fn);
+    const FwdLayout F = fwd_layout(s);
+    if ((uintptr_t)fwd_ws & 255) return fail(MOE_ERR_INVALID_ARG, "%s: forward workspace must be 256-byte aligned", fn);
+    if (fwd_ws_bytes < F.total)
+        return fail(MOE_ERR_WORKSPACE, "%s: forward workspace of %zu bytes expected, got %zu", fn, F.total,
+                    fwd_ws_bytes);
+    const BwdLayout L = bwd_layout(s);
+    rc = ws_check(ws, ws_bytes, L.total, fn);
+    if (rc) return rc;
+
+    hipStream_t st = (hipStream_t)stream;
+    const int dt = dt_of(s->act_dtype);
+    const int64_t T = s->T, TK = T * s->topk;
+    const int d = s->d, I = s->inter, Ns = s->n_shared, a_sz = esize(s->act_dtype);
+    const char *Fw = (const char *)fwd_ws;
+    char *W = (char *)ws;
+    const float *scores = (const float *)(Fw + F.scores);
+    const int32_t *idx = (const int32_t *)(Fw + F.idx);
+    const float *tw = (const float *)(Fw + F.w);
+    const int32_t *offsets = (const int32_t *)(Fw + F.offsets);
+    const int32_t *perm = (const int32_t *)(Fw + F.perm);
+    const int32_t *inv = (const int32_t *)(Fw + F.inv);
+    char *dy = W + L.dy, *dh = W + L.dh, *dab = W + L.dab, *dx = W + L.dx;
+    float *dg = dtopk_w ? dtopk_w : (float *)(W + L.dg);
+    float *dz = (float *)(W + L.dz);
+    char *dh_s = dh + (size_t)TK * I * a_sz, *dab_s = dab + (size_t)TK * 2 * I * a_sz, *dx_s = dx + (size_t)TK * d * a_sz;
+
+    // 1. combine: dY rows and gate gradients
+    HIPCHK(launch_bwd_combine(dt, dout, Fw + F.yperm, inv, tw, T, d, s->topk, dy, dg, st));
+    // 2. dH = dY . W_down (transposed copies [n][I][d])
+    FfnProblem p[2] = {}, q[2] = {};
+    p[0].n_exp = s->n_routed;
+    p[0].offsets = offsets;
+    p[0].x = dy;
+    p[0].w0 = routed_wt[0];
+    p[0].out = dh;
+    if (Ns) {
+        p[1].n_exp = Ns;
+        p[1].rows_fixed = T;
+        p[1].x_local = 1;
+        p[1].x = dout;
+        p[1].w0 = shared_wt[0];
+        p[1].out = dh_s;
+    }
+    FfnArgs fa{};
+    fa.nprob = Ns ? 2 : 1;
+    fa.K = d;
+    fa.F = I;
+    for (int i = 0; i < fa.nprob; ++i) fa.p[i] = p[fa.nprob - 1 - i];
+    HIPCHK(launch_ffn(dt, FFN_DOWN, fa, st));
+    // 3. gate/up recomputed from u; SwiGLU gradient against dH -> [dA | dB]
+    q[0].n_exp = s->n_routed;
+    q[0].offsets = offsets;
+    q[0].gather = perm;
+    q[0].x = u;
+    q[0].w0 = routed_w[0];
+    q[0].w1 = routed_w[1];
+    q[0].dh = dh;
+    q[0].out = dab;
+    q[0].out_ld = 2 * I;
+    if (Ns) {
+        q[1].n_exp = Ns;
+        q[1].rows_fixed = T;
+        q[1].x_local = 1;
+        q[1].x = u;
+        q[1].w0 = shared_w[0];
+        q[1].w1 = shared_w[1];
+        q[1].dh = dh_s;
+        q[1].out = dab_s;
+        q[1].out_ld = 2 * I;
+    }
+    for (int i = 0; i < fa.nprob; ++i) fa.p[i] = q[fa.nprob - 1 - i];
+    HIPCHK(launch_ffn(dt, FFN_GATEUP_BWD, fa, st));
+    // 4. dX = [dA | dB] . [W_gate ; W_up] (transposed copies [n][d][2I])
+    FfnProblem r[2] = {};
+    r[0].n_exp = s->n_routed;
+    r[0].offsets = offsets;
+    r[0].x = dab;
+    r[0].w0 = routed_wt[1];
+    r[0].out = dx;
+    if (Ns) {
+        r[1].n_exp = Ns;
+        r[1].rows_fixed = T;
+        r[1].x = dab_s;
+        r[1].w0 = shared_wt[1];
+        r[1].out = dx_s;
+    }
+    fa.K = 2 * I;
+    fa.F = d;
+    for (int i = 0; i < fa.nprob; ++i) fa.p[i] = r[fa.nprob - 1 - i];
+    HIPCHK(launch_ffn(dt, FFN_DOWN, fa, st));
+    // 5. du: dispatch sum and router chain; dz per row
+    HIPCHK(launch_bwd_token(dt, dx, dx_s, Ns, inv, idx, scores, dg, gate_w, T, d, s->n_routed, s->topk,
+                            s->routed_scale, du, dz, st));
+    // 6. centroid gradient
+    if (dgate_w) HIPCHK(launch_dgate(dt, u, perm, offsets, dz, s->n_routed, d, dgate_w, st));
+    // 7. weight gradients: down (dY rows x H rows), then gate/up ([dA | dB] rows x gathered u rows)
+    if (d_routed_w || (Ns && d_shared_w)) {
+        WgradArgs wa{};
+        int np = 0;
+        if (d_routed_w) {
+            WgradProblem &w = wa.p[np++];
+            w.n_exp = s->n_routed;
+            w.offsets = offsets;
+            w.P = dy;
+            w.P_ld = d;
+            w.Q = Fw + F.h;
+            w.Q_ld = I;
+            w.Pdim = d;
+            w.Qdim = I;
+            w.split = d;
+            w.out0 = d_routed_w[2];
+        }
+        if (Ns && d_shared_w) {
+            WgradProblem &w = wa.p[np++];
+            w.n_exp = Ns;
+            w.rows_fixed = T;
+            w.p_local = 1;
+            w.P = dout;
+            w.P_ld = d;
+            w.Q = Fw + F.hsh;
+            w.Q_ld = I;
+            w.Pdim = d;
+            w.Qdim = I;
+            w.split = d;
+            w.out0 = d_shared_w[2];
+        }
+        wa.nprob = np;
+        HIPCHK(launch_wgrad(dt, wa, st));
+        np = 0;
+        if (d_routed_w) {
+            WgradProblem &w = wa.p[np++];
+            w = WgradProblem{};
+            w.n_exp = s->n_routed;
+            w.offsets = offsets;
+            w.P = dab;
+            w.P_ld = 2 * I;
+            w.Q = u;
+            w.Q_ld = d;
+            w.q_gather = perm;
+            w.Pdim = 2 * I;
+            w.Qdim = d;
+            w.split = I;
+            w.out0 = d_routed_w[0];
+            w.out1 = d_routed_w[1];
+        }
+        if (Ns && d_shared_w) {
+            WgradProblem &w = wa.p[np++];
+            w = WgradProblem{};
+            w.n_exp = Ns;
+            w.rows_fixed = T;
+            w.q_local = 1;
+            w.P = dab_s;
+            w.P_ld = 2 * I;
+            w.Q = u;
+            w.Q_ld = d;
+            w.Pdim = 2 * I;
+            w.Qdim = d;
+            w.split = I;
+            w.out0 = d_shared_w[0];
+            w.out1 = d_shared_w[1];
+        }
+        wa.nprob = np;
+        HIPCHK(launch_wgrad(dt, wa, st));
+    }
     return MOE_OK;
 }
 

@@ -171,8 +171,8 @@ __device__ __forceinline__ void compute_step(const char *st, const float *sc, f3
 
 // LDS bytes of the fp8 H-quantisation scratch (per-wave row maxima), kept
 // apart from the ring so the next tile's loads can land during the epilogue.
-template <int DT, bool GATEUP>
-__host__ __device__ constexpr int red_bytes() { return (DT == DT_E4M3 && GATEUP) ? WF * BM * 4 : 0; }
+template <int DT, int MODE>
+__host__ __device__ constexpr int red_bytes() { return (DT == DT_E4M3 && MODE == FFN_GATEUP) ? WF * BM * 4 : 0; }
 
 // Stores two adjacent 16-feature blocks of one token's bf16 results (block i
 // from a[], block i+1 from b[]; lane group g = lane/16 holds features 4g..4g+3
@@ -191,8 +191,10 @@ __device__ __forceinline__ void store_pair_bf16(uint16_t *row, int f_block, cons
     if (f < F) *(u32x4 *)(row + f) = odd ? u32x4{r0, r1, b01, b23} : u32x4{a01, a23, r0, r1};
 }
 
-template <int DT, bool GATEUP>
+template <int DT, int MODE>
 __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_bytes) {
+    constexpr bool GATEUP = MODE != FFN_DOWN;           // two weight matrices, SwiGLU epilogue
+    constexpr bool SWBWD = MODE == FFN_GATEUP_BWD;      // epilogue: SwiGLU gradient from dH
     constexpr int esz = FTraits<DT>::esz;
     constexpr int CB = Frag<DT>::CB;              // staged bytes per row per reduction step
     constexpr int RPI = 1024 / CB;                // rows per 1 KB DMA instruction
@@ -203,12 +205,13 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
     constexpr bool FP8 = DT == DT_E4M3;
     static_assert(!FP8 || !GATEUP || BF == 128, "fp8 H quantisation needs whole 128-feature groups per tile");
     static_assert(!FP8 || 128 % (GATEUP ? WRW / 2 : WRW) == 0, "fp8: a wave's rows sit in one weight block");
+    static_assert(!(FP8 && SWBWD), "the SwiGLU gradient pass is bf16 / fp32 only");
 
     extern __shared__ __align__(1024) char smem[];
     const int pbytes = prefix_bytes(a.p[0].n_exp, a.nprob > 1 ? a.p[1].n_exp : 0);
     int *pre = (int *)smem;                                            // [n0 + 1] then [n1 + 1]
     float *red = (float *)(smem + pbytes);                             // fp8 gate/up: [WF][BM]
-    char *ring = smem + pbytes + red_bytes<DT, GATEUP>();
+    char *ring = smem + pbytes + red_bytes<DT, MODE>();
     int *scan = (int *)ring;                                           // start-up scratch, aliases the ring
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -456,7 +459,48 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
             const float g = acc[i][j][q], u = acc[i + RB / 2][j][q];
             return __fdividef(g, 1.0f + __expf(-g)) * u;
         };
-        if (GATEUP) {
+        const int64_t ld = P.out_ld ? P.out_ld : F;
+        if (SWBWD) {
+            // a, b recomputed in the accumulators; dH of the same features from the forward's
+            // gradient: da = dh * b * SiLU'(a), db = dh * SiLU(a), SiLU'(a) = s (1 + a (1 - s))
+#pragma unroll
+            for (int j = 0; j < TB; ++j) {
+                const int tok = (j * WM + wm) * 16 + (lane & 15);
+                if (tok >= valid) continue;
+                const int64_t R = rbase + tok;
+#pragma unroll
+                for (int i = 0; i < RB / 2; ++i) {
+                    const int f = n0 + wf * (BF / WF) + i * 16 + 4 * (lane >> 4);
+                    float dh[4], da[4], db[4];
+                    if (DT == DT_F32) {
+                        const f32x4 v = *(const f32x4 *)((const float *)P.dh + R * F + f);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) dh[q] = v[q];
+                    } else {
+                        const u32x2 v = *(const u32x2 *)((const uint16_t *)P.dh + R * F + f);
+                        dh[0] = __uint_as_float(v[0] << 16);
+                        dh[1] = __uint_as_float(v[0] & 0xFFFF0000u);
+                        dh[2] = __uint_as_float(v[1] << 16);
+                        dh[3] = __uint_as_float(v[1] & 0xFFFF0000u);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float av = acc[i][j][q], bv = acc[i + RB / 2][j][q];
+                        const float sg = 1.0f / (1.0f + __expf(-av));
+                        da[q] = dh[q] * bv * sg * (1.0f + av * (1.0f - sg));
+                        db[q] = dh[q] * av * sg;
+                    }
+                    if (DT == DT_F32) {
+                        *(f32x4 *)((float *)P.out + R * ld + f) = f32x4{da[0], da[1], da[2], da[3]};
+                        *(f32x4 *)((float *)P.out + R * ld + F + f) = f32x4{db[0], db[1], db[2], db[3]};
+                    } else {
+                        *(u32x2 *)((uint16_t *)P.out + R * ld + f) = u32x2{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
+                        *(u32x2 *)((uint16_t *)P.out + R * ld + F + f) =
+                            u32x2{pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3])};
+                    }
+                }
+            }
+        } else if (GATEUP) {
             if (FP8) {
                 // 1 x 128 groups of H along features: the tile's 128 features of a token live in
                 // 4 lanes x (RB/2) blocks x 4 values in each of the WF waves of its token column
@@ -483,7 +527,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                     const float scale = quant_scale(amax);
                     if (tok >= valid) continue;
                     const int64_t R = rbase + tok;
-                    uint8_t *orow = (uint8_t *)P.out + R * F;
+                    uint8_t *orow = (uint8_t *)P.out + R * ld;
 #pragma unroll
                     for (int i = 0; i < RB / 2; ++i) {
                         const int f = n0 + wf * (BF / WF) + i * 16 + 4 * (lane >> 4);
@@ -503,7 +547,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
 #pragma unroll
                         for (int i = 0; i < RB / 2; ++i) {
                             const int f = n0 + wf * (BF / WF) + i * 16 + 4 * (lane >> 4);
-                            *(f32x4 *)((float *)P.out + R * F + f) =
+                            *(f32x4 *)((float *)P.out + R * ld + f) =
                                 f32x4{hval(i, j, 0), hval(i, j, 1), hval(i, j, 2), hval(i, j, 3)};
                         }
                     } else {
@@ -513,7 +557,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                             const float ha[4] = {hval(i, j, 0), hval(i, j, 1), hval(i, j, 2), hval(i, j, 3)};
                             const float hb[4] = {hval(i + 1, j, 0), hval(i + 1, j, 1), hval(i + 1, j, 2),
                                                  hval(i + 1, j, 3)};
-                            store_pair_bf16((uint16_t *)P.out + R * F, n0 + wf * (BF / WF) + i * 16, ha, hb, lane, F);
+                            store_pair_bf16((uint16_t *)P.out + R * ld, n0 + wf * (BF / WF) + i * 16, ha, hb, lane, F);
                         }
                     }
                 }
@@ -528,14 +572,14 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
 #pragma unroll
                     for (int i = 0; i < RB; ++i) {
                         const int f = n0 + wf * WRW + i * 16 + 4 * (lane >> 4);
-                        if (f < F) *(f32x4 *)((float *)P.out + R * F + f) = acc[i][j];
+                        if (f < F) *(f32x4 *)((float *)P.out + R * ld + f) = acc[i][j];
                     }
                 } else {
 #pragma unroll
                     for (int i = 0; i < RB; i += 2) {
                         const float ya[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
                         const float yb[4] = {acc[i + 1][j][0], acc[i + 1][j][1], acc[i + 1][j][2], acc[i + 1][j][3]};
-                        store_pair_bf16((uint16_t *)P.out + R * F, n0 + wf * WRW + i * 16, ya, yb, lane, F);
+                        store_pair_bf16((uint16_t *)P.out + R * ld, n0 + wf * WRW + i * 16, ya, yb, lane, F);
                     }
                 }
             }
@@ -544,32 +588,38 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
     }
 }
 
-template <int DT, bool GATEUP>
+template <int DT, int MODE>
 hipError_t run(const FfnArgs &a, hipStream_t s) {
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(once, [&] {
-        attr_err = hipFuncSetAttribute((const void *)ffn_kernel<DT, GATEUP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+        attr_err = hipFuncSetAttribute((const void *)ffn_kernel<DT, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                        LDS_TOTAL);
     });
     if (attr_err != hipSuccess) return attr_err;
     const int pb = prefix_bytes(a.p[0].n_exp, a.nprob > 1 ? a.p[1].n_exp : 0);
-    const int ring = LDS_TOTAL - pb - red_bytes<DT, GATEUP>();
+    const int ring = LDS_TOTAL - pb - red_bytes<DT, MODE>();
     // the ring must hold two stages of any tile
     constexpr int CB = Frag<DT>::CB;
     if (ring < 2 * ((WR + BM) * CB + (DT == DT_E4M3 ? SCL_BYTES : 0))) return hipErrorInvalidValue;
     int grid = device_cus();
     grid = (grid + 7) / 8 * 8;
-    ffn_kernel<DT, GATEUP><<<grid, NT, LDS_TOTAL, s>>>(a, ring);
+    ffn_kernel<DT, MODE><<<grid, NT, LDS_TOTAL, s>>>(a, ring);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_ffn(int dt, bool gateup, const FfnArgs &a, hipStream_t s) {
-    if (dt == DT_F32) return gateup ? run<DT_F32, true>(a, s) : run<DT_F32, false>(a, s);
-    if (dt == DT_BF16) return gateup ? run<DT_BF16, true>(a, s) : run<DT_BF16, false>(a, s);
-    return gateup ? run<DT_E4M3, true>(a, s) : run<DT_E4M3, false>(a, s);
+hipError_t launch_ffn(int dt, int mode, const FfnArgs &a, hipStream_t s) {
+    if (mode == FFN_GATEUP_BWD) {
+        if (dt == DT_F32) return run<DT_F32, FFN_GATEUP_BWD>(a, s);
+        if (dt == DT_BF16) return run<DT_BF16, FFN_GATEUP_BWD>(a, s);
+        return hipErrorInvalidValue;
+    }
+    const bool gateup = mode == FFN_GATEUP;
+    if (dt == DT_F32) return gateup ? run<DT_F32, FFN_GATEUP>(a, s) : run<DT_F32, FFN_DOWN>(a, s);
+    if (dt == DT_BF16) return gateup ? run<DT_BF16, FFN_GATEUP>(a, s) : run<DT_BF16, FFN_DOWN>(a, s);
+    return gateup ? run<DT_E4M3, FFN_GATEUP>(a, s) : run<DT_E4M3, FFN_DOWN>(a, s);
 }
 
 }  // namespace moe

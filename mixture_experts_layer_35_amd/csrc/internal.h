@@ -56,6 +56,8 @@ struct FfnProblem {
     const float *s0, *s1;   // E4M3 block scales [n_exp][F/128][K/128]
     void *out;              // gate/up: H [rows][F]; down: y [rows][F]
     float *out_s;           // E4M3 gate/up: H scales [rows][F/128]
+    int64_t out_ld;         // elements between output rows (0: F)
+    const void *dh;         // gate/up gradient pass: dH [rows][F] (act dtype)
 };
 struct FfnArgs {
     FfnProblem p[2];
@@ -64,7 +66,45 @@ struct FfnArgs {
     int F;   // output features (I for gate/up, d for down)
 };
 constexpr int kMaxExperts = 1024;
-hipError_t launch_ffn(int dt, bool gateup, const FfnArgs &a, hipStream_t s);
+// mode: FFN_DOWN (out = x . w^T), FFN_GATEUP (out = SiLU(x . w0^T) * (x . w1^T)),
+// FFN_GATEUP_BWD (a = x . w0^T, b = x . w1^T recomputed; with dh read from P.dh,
+// out[:, 0:F] = dh * b * SiLU'(a) and out[:, F:2F] = dh * SiLU(a); out_ld = 2F).
+enum { FFN_DOWN = 0, FFN_GATEUP = 1, FFN_GATEUP_BWD = 2 };
+hipError_t launch_ffn(int dt, int mode, const FfnArgs &a, hipStream_t s);
+
+// ---- backward ----------------------------------------------------------------
+// Weight-gradient problem: for each expert e with rows r (offsets, or rows_fixed
+// each), C_e[p][q] = sum_r P[prow(r)][p] * Q[qrow(r)][q] over the expert's rows r:
+// qrow(r) = q_gather[r], else r within the expert when q_local, else the global
+// row (prow likewise with p_local).  Rows p < split go to out0 [n][split][Qdim],
+// the rest to out1 [n][Pdim - split][Qdim].
+struct WgradProblem {
+    int n_exp;
+    const int32_t *offsets;
+    int64_t rows_fixed;
+    const void *P;
+    int64_t P_ld;
+    const void *Q;
+    int64_t Q_ld;
+    const int32_t *q_gather;
+    int p_local, q_local;   // row r of the expert reads P / Q row r (not base + r): an input shared by experts
+    int Pdim, Qdim, split;
+    void *out0, *out1;
+};
+struct WgradArgs {
+    WgradProblem p[2];
+    int nprob;
+};
+hipError_t launch_transpose(int dt, const void *src, int64_t nmat, int rows, int cols, void *dst, int dst_ld, int col0,
+                            hipStream_t s);
+hipError_t launch_bwd_combine(int dt, const void *dout, const void *y, const int32_t *inv, const float *topk_w, int64_t T,
+                              int d, int K, void *dy, float *dg, hipStream_t s);
+hipError_t launch_bwd_token(int dt, const void *dxr, const void *dxs, int Ns, const int32_t *inv, const int32_t *idx,
+                            const float *scores, const float *dg, const void *gate_w, int64_t T, int d, int Nr, int K,
+                            float rs, void *du, float *dz_row, hipStream_t s);
+hipError_t launch_dgate(int dt, const void *u, const int32_t *perm, const int32_t *offsets, const float *dz_row, int Nr,
+                        int d, float *dgate, hipStream_t s);
+hipError_t launch_wgrad(int dt, const WgradArgs &a, hipStream_t s);
 
 // ---- combine / bias ----------------------------------------------------------
 hipError_t launch_combine(int dt_out, int dt_res, const void *y_perm, const int32_t *inv_perm, const float *topk_w,

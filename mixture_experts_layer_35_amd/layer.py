@@ -1,6 +1,6 @@
-"""Device-resident DeepSeekMoE layer: uploads weights once, owns the workspace,
-and calls ``moe_forward`` on each batch.  Memory management only; the layer's
-arithmetic is entirely in libmoe's kernels.
+"""Device-resident DeepSeekMoE layer: uploads weights once, owns the workspaces,
+and calls ``moe_forward`` on each batch and ``moe_backward`` for its gradient.
+Memory management only; the layer's arithmetic is entirely in libmoe's kernels.
 
 For an e4m3 layer the bf16 master weights are uploaded and block-quantised on
 the device by ``moe_quantize_weights_128x128`` (128 x 128 blocks, §3.3 of the
@@ -11,8 +11,9 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_WS_FORWARD, MoeShape, moe_forward, moe_quantize_weights_128x128,
-               moe_workspace_bytes)
+from . import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_WS_FORWARD, MoeError, MoeShape, MOE_ERR_UNSUPPORTED, moe_backward,
+               moe_backward_workspace_bytes, moe_forward, moe_quantize_weights_128x128,
+               moe_transpose_expert_weights, moe_workspace_bytes)
 
 
 def to_device(a: np.ndarray, device="cuda") -> torch.Tensor:
@@ -53,6 +54,9 @@ class MoeLayer:
         self.shared_s = tuple(shared_s) if shared_s is not None else None
         self._ws = None
         self._ws_T = -1
+        self._bws = None
+        self._bws_T = -1
+        self._wt = None
 
     @classmethod
     def from_host(cls, shape: MoeShape, gate_w, bias, wg, wu, wd, swg=None, swu=None, swd=None, device="cuda"):
@@ -99,3 +103,50 @@ class MoeLayer:
         moe_forward(self.shape, u, self.gate_w, self.bias, self.routed_w, self.routed_s, self.shared_w,
                     self.shared_s, out, topk_idx, topk_w, counts, scores, ws, stream)
         return out
+
+    # ---- backward -----------------------------------------------------------
+
+    def transposed_weights(self, stream=None):
+        """(routed, shared) pairs (W_down^T [n, I, d], [W_gate^T | W_up^T] [n, d, 2I]) that the
+        backward reads; built on first use.  Call drop_transposed() after changing the weights."""
+        if self.shape.w_dtype == MOE_E4M3:
+            raise MoeError(MOE_ERR_UNSUPPORTED, "the backward runs on fp32 / bf16 layers")
+        if self._wt is None:
+            d, I = self.shape.d, self.shape.inter
+
+            def tr(ws):
+                if ws is None:
+                    return None
+                wg, wu, wd = ws
+                n = wg.shape[0]
+                wdt = torch.empty((n, I, d), dtype=wd.dtype, device=wd.device)
+                wgut = torch.empty((n, d, 2 * I), dtype=wg.dtype, device=wg.device)
+                moe_transpose_expert_weights(self.shape, n, wg, wu, wd, wdt, wgut, stream)
+                return wdt, wgut
+
+            self._wt = (tr(self.routed_w), tr(self.shared_w))
+        return self._wt
+
+    def drop_transposed(self):
+        self._wt = None
+
+    def backward(self, u: torch.Tensor, dout: torch.Tensor, du: torch.Tensor = None, dgate_w=None, d_routed_w=None,
+                 d_shared_w=None, dtopk_w=None, stream=None) -> torch.Tensor:
+        """Gradients for the most recent forward(u) (its workspace holds the saved
+        activations, so no other forward may run in between).  du is returned;
+        dgate_w [N_r, d] fp32, d_routed_w / d_shared_w (dW_gate, dW_up, dW_down) and
+        dtopk_w [T, K] fp32 are filled when given."""
+        T = u.shape[0]
+        if self._ws is None or self._ws_T != T:
+            raise ValueError("backward needs the workspace of a forward call on the same batch")
+        rt, st = self.transposed_weights(stream)
+        self.shape.T = T
+        if self._bws is None or self._bws_T != T:
+            n = moe_backward_workspace_bytes(self.shape)
+            self._bws = torch.empty(max(n, 256), dtype=torch.uint8, device=u.device)
+            self._bws_T = T
+        if du is None:
+            du = torch.empty((T, self.shape.d), dtype=u.dtype, device=u.device)
+        moe_backward(self.shape, u, self.gate_w, self.routed_w, rt, self.shared_w, st, self._ws, dout, du, dgate_w,
+                     d_routed_w, d_shared_w, dtopk_w, self._bws, stream)
+        return du

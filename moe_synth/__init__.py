@@ -31,7 +31,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
-TAG_U, TAG_GATE, TAG_BIAS, TAG_WG, TAG_WU, TAG_WD, TAG_SWG, TAG_SWU, TAG_SWD, TAG_SCORES = range(1, 11)
+TAG_U, TAG_GATE, TAG_BIAS, TAG_WG, TAG_WU, TAG_WD, TAG_SWG, TAG_SWU, TAG_SWD, TAG_SCORES, TAG_DOUT = range(1, 12)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -165,6 +165,14 @@ def expert_weights(cfg: LayerConfig, n=None, shared=False, seed=None, threads=No
     wu = _stack((cfg.I, cfg.d), n, 1.0 / np.sqrt(cfg.d), seed, tu, st, threads)
     wd = _stack((cfg.d, cfg.I), n, 1.0 / np.sqrt(cfg.I), seed, td, st, threads)
     return wg, wu, wd
+
+
+def grad_output(cfg: LayerConfig, seed=None, T=None):
+    """Upstream gradient dL/d(layer output) [T, d]: unit normal, in the
+    activation storage (the backward takes it in the layer's own format)."""
+    seed = cfg.seed if seed is None else seed
+    T = cfg.T if T is None else T
+    return normal((T, cfg.d), 1.0, seed, TAG_DOUT, 0, store_of(cfg))
 
 
 def random_scores(T, Nr, seed, tag_index=0):

@@ -84,10 +84,11 @@ def _load():
             lib.oracle_bias_update.restype = None
             lib.oracle_bias_update.argtypes = [i32, i64, i32, P, P, f32]
             lib.oracle_layer_f64.restype = i32
-            lib.oracle_layer_f64.argtypes = [i64, i32, i32, i32, i32, i32, i32, P, P, P, i32] + [P] * 6 + [P, P]
+            f64 = ctypes.c_double
+            lib.oracle_layer_f64.argtypes = [i64, i32, i32, i32, i32, i32, i32, P, P, P, i32] + [P] * 6 + [f64, P, P]
             lib.oracle_moe_backward_f64.restype = i32
             lib.oracle_moe_backward_f64.argtypes = ([i64, i32, i32, i32, i32, i32, i32, P, P, P, i32] + [P] * 6
-                                                    + [P, i64, P, i32, P] + [P] * 9)
+                                                    + [f64, P, i64, P, i32, P] + [P] * 9)
             lib.oracle_seq_balance.restype = None
             lib.oracle_seq_balance.argtypes = [i64, i32, i32, P, P, i64, f32, P, P, P]
             lib.oracle_num_threads.restype = i32
@@ -366,7 +367,7 @@ def _layer_args(u, gate_w, topk_idx, routed, shared):
     return T, d, Nr, Ns, K, I, au, u, gate_w, topk_idx, codes.pop(), arrs
 
 
-def layer_f64(u, gate_w, topk_idx, routed, shared):
+def layer_f64(u, gate_w, topk_idx, routed, shared, routed_scale=1.0):
     """The layer with nothing rounded after decoding the inputs, for a fixed
     selection topk_idx (§2.1.2): returns (out [T, d] float64, gates [T, K]
     float64).  Inputs in float32, bf16 bits or float64."""
@@ -374,13 +375,15 @@ def layer_f64(u, gate_w, topk_idx, routed, shared):
     out = np.empty((T, d), np.float64)
     g = np.empty((T, K), np.float64)
     rc = _load().oracle_layer_f64(T, d, Nr, Ns, K, I, au, _p(u), _p(gate_w), _p(idx), wc, *[_p(a) for a in arrs],
+                                  routed_scale,
                                   _p(out), _p(g))
     if rc:
         raise ValueError("oracle_layer_f64 rc=%d" % rc)
     return out, g
 
 
-def moe_backward(u, gate_w, topk_idx, routed, shared, dout, tokens=None, experts=None, dgate=True, dshared=True):
+def moe_backward(u, gate_w, topk_idx, routed, shared, dout, tokens=None, experts=None, dgate=True, dshared=True,
+                 routed_scale=1.0):
     """Gradient of sum(dout * layer(...)) by the chain rule in fp64 for a fixed
     selection (see layer_f64).  Returns a dict with
       du [T, d] and dg [T, K] (rows of the listed tokens; others zero),
@@ -398,7 +401,7 @@ def moe_backward(u, gate_w, topk_idx, routed, shared, dout, tokens=None, experts
              dswu=np.empty((Ns, I, d)) if dshared and Ns else None,
              dswd=np.empty((Ns, d, I)) if dshared and Ns else None)
     rc = _load().oracle_moe_backward_f64(T, d, Nr, Ns, K, I, au, _p(u), _p(gate_w), _p(idx), wc,
-                                         *[_p(a) for a in arrs], _p(dout), 0 if tok is None else tok.shape[0],
+                                         *[_p(a) for a in arrs], routed_scale, _p(dout), 0 if tok is None else tok.shape[0],
                                          _p(tok), 0 if exps is None else exps.shape[0], _p(exps),
                                          _p(r["du"]), _p(r["dg"]), _p(r["dgate_w"]), _p(r["dwg"]), _p(r["dwu"]),
                                          _p(r["dwd"]), _p(r["dswg"]), _p(r["dswu"]), _p(r["dswd"]))

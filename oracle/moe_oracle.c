@@ -623,7 +623,8 @@ void oracle_seq_balance(int64_t T, int Nr, int K, const float *scores, const int
  * are decoded, for a given selection topk_idx [T][K] (held fixed: the
  * selection is piecewise constant, so the layer is smooth in u, the centroids
  * and the weights wherever the selection does not change):
- *   s_{t,i} = sigmoid(u_t . e_i),  g_{t,j} = s_{t,e_j} / sum_k s_{t,e_k},
+ *   s_{t,i} = sigmoid(u_t . e_i),  g_{t,j} = rs * s_{t,e_j} / sum_k s_{t,e_k}
+ *   (rs: the routed scaling factor, 1 in the pages' formula),
  *   out_t = sum_j g_{t,j} FFN_{e_j}(u_t) + sum_s FFN^shared_s(u_t),
  *   FFN(x) = W_down (SiLU(W_gate x) * (W_up x)).
  * u [T][d] and gate_w [Nr][d] are stored in a_code, the weights in w_code
@@ -661,8 +662,8 @@ static void ffn64(int d, int I, omat wg, omat wu, omat wd, const double *x, doub
     }
 }
 
-static void gates64(int d, int K, const double *x, omat gate_w, const int32_t *sel, double *s_sel, double *g,
-                    double *row)
+static void gates64(int d, int K, const double *x, omat gate_w, const int32_t *sel, double rs, double *s_sel,
+                    double *g, double *row)
 {
     double den = 0.0;
     for (int j = 0; j < K; ++j) {
@@ -670,7 +671,7 @@ static void gates64(int d, int K, const double *x, omat gate_w, const int32_t *s
         s_sel[j] = 1.0 / (1.0 + exp(-dot(x, row, d)));
         den += s_sel[j];
     }
-    for (int j = 0; j < K; ++j) g[j] = s_sel[j] / den;
+    for (int j = 0; j < K; ++j) g[j] = rs * s_sel[j] / den;
 }
 
 /* dh = W_down^T dy (sum over the d rows of W_down in order); row: I scratch */
@@ -685,7 +686,7 @@ static void down_t(int d, int I, omat wd, const double *dy, double *dh, double *
 
 int oracle_layer_f64(int64_t T, int d, int Nr, int Ns, int K, int I, int a_code, const void *u, const void *gate_w,
                      const int32_t *topk_idx, int w_code, const void *rwg, const void *rwu, const void *rwd,
-                     const void *swg, const void *swu, const void *swd, double *out, double *topk_w)
+                     const void *swg, const void *swu, const void *swd, double rs, double *out, double *topk_w)
 {
     const size_t wm = (size_t)I * d;
     const omat U = {a_code, u}, E = {a_code, gate_w};
@@ -703,7 +704,7 @@ int oracle_layer_f64(int64_t T, int d, int Nr, int Ns, int K, int I, int a_code,
         for (int64_t t = 0; t < T; ++t) {
             double *o = out + (size_t)t * d;
             orow(U, t, d, x);
-            gates64(d, K, x, E, topk_idx + t * K, s_sel, g, row);
+            gates64(d, K, x, E, topk_idx + t * K, rs, s_sel, g, row);
             if (topk_w)
                 for (int j = 0; j < K; ++j) topk_w[t * K + j] = g[j];
             for (int i = 0; i < d; ++i) o[i] = 0.0;
@@ -728,9 +729,9 @@ int oracle_layer_f64(int64_t T, int d, int Nr, int Ns, int K, int I, int a_code,
  *     da = dh * b * SiLU'(a) with SiLU'(a) = sigma(a) (1 + a (1 - sigma(a))),
  *     db = dh * SiLU(a),  dx = W_gate^T da + W_up^T db,
  *     dW_gate += da x^T,  dW_up += db x^T
- *   gates g_j = s_j / D (D = sum of the selected s):
- *     ds_k = dg_k / D - (sum_j dg_j s_j) / D^2 for selected k (no other expert
- *     receives gate gradient; the bias receives none),
+ *   gates g_j = rs s_j / D (D = sum of the selected s):
+ *     ds_k = rs (dg_k / D - (sum_j dg_j s_j) / D^2) for selected k (no other
+ *     expert receives gate gradient; the bias receives none),
  *   dz = ds * s (1 - s),  du_t += sum_j dx_{t,j} + dx_shared + sum_k dz_k e_k,
  *   de_k += dz_k u_t.
  * Subsets: du [T][d] and dtopk_w [T][K] rows are written for the listed tokens
@@ -742,8 +743,8 @@ int oracle_layer_f64(int64_t T, int d, int Nr, int Ns, int K, int I, int a_code,
  */
 int oracle_moe_backward_f64(int64_t T, int d, int Nr, int Ns, int K, int I, int a_code, const void *u,
                             const void *gate_w, const int32_t *topk_idx, int w_code, const void *rwg, const void *rwu,
-                            const void *rwd, const void *swg, const void *swu, const void *swd, const double *dout,
-                            int64_t n_tok, const int64_t *tok, int n_exp, const int32_t *exps,
+                            const void *rwd, const void *swg, const void *swu, const void *swd, double rs,
+                            const double *dout, int64_t n_tok, const int64_t *tok, int n_exp, const int32_t *exps,
                             double *du, double *dtopk_w, double *dgate_w,
                             double *drwg, double *drwu, double *drwd,
                             double *dswg, double *dswu, double *dswd)
@@ -770,7 +771,7 @@ int oracle_moe_backward_f64(int64_t T, int d, int Nr, int Ns, int K, int I, int 
                 const double *dO = dout + (size_t)t * d;
                 const int32_t *sel = topk_idx + t * K;
                 orow(U, t, d, x);
-                gates64(d, K, x, E, sel, s_sel, g, row);
+                gates64(d, K, x, E, sel, rs, s_sel, g, row);
                 for (int c = 0; c < d; ++c) dx[c] = 0.0;
                 for (int j = 0; j < K + Ns; ++j) {
                     const int routed = j < K, e = routed ? sel[j] : j - K;
@@ -796,7 +797,7 @@ int oracle_moe_backward_f64(int64_t T, int d, int Nr, int Ns, int K, int I, int 
                 double den = 0.0, sdg = 0.0;
                 for (int j = 0; j < K; ++j) { den += s_sel[j]; sdg += dg[j] * s_sel[j]; }
                 for (int j = 0; j < K; ++j) {
-                    const double dz = (dg[j] / den - sdg / (den * den)) * s_sel[j] * (1.0 - s_sel[j]);
+                    const double dz = rs * (dg[j] / den - sdg / (den * den)) * s_sel[j] * (1.0 - s_sel[j]);
                     orow(E, sel[j], d, row);
                     for (int c = 0; c < d; ++c) dx[c] += dz * row[c];
                 }
@@ -823,7 +824,7 @@ int oracle_moe_backward_f64(int64_t T, int d, int Nr, int Ns, int K, int I, int 
                 const double *dO = dout + (size_t)t * d;
                 const int32_t *sel = topk_idx + t * K;
                 orow(U, t, d, x);
-                gates64(d, K, x, E, sel, s_sel, g, row);
+                gates64(d, K, x, E, sel, rs, s_sel, g, row);
                 double den = 0.0, sdg = 0.0;
                 for (int j = 0; j < K; ++j) {
                     ffn64(d, I, osub(RG, sel[j], wm), osub(RU, sel[j], wm), osub(RD, sel[j], wm), x, a, b, h, y, row);
@@ -832,7 +833,7 @@ int oracle_moe_backward_f64(int64_t T, int d, int Nr, int Ns, int K, int I, int 
                     sdg += dg[j] * s_sel[j];
                 }
                 for (int j = 0; j < K; ++j)
-                    dzall[t * K + j] = (dg[j] / den - sdg / (den * den)) * s_sel[j] * (1.0 - s_sel[j]);
+                    dzall[t * K + j] = rs * (dg[j] / den - sdg / (den * den)) * s_sel[j] * (1.0 - s_sel[j]);
             }
             free(a); free(b); free(h); free(y); free(x); free(row);
         }
@@ -877,7 +878,7 @@ int oracle_moe_backward_f64(int64_t T, int d, int Nr, int Ns, int K, int I, int 
                     orow(U, t, d, x);
                     double gj = 1.0;
                     if (!pass) {
-                        gates64(d, K, x, E, topk_idx + t * K, s_sel, g, row);
+                        gates64(d, K, x, E, topk_idx + t * K, rs, s_sel, g, row);
                         gj = g[jl[n]];
                     }
                     ffn64(d, I, wg, wu, wd, x, a, b, h, y, row);

@@ -155,3 +155,44 @@ def test_binding_raises_with_message(lib):
     with pytest.raises(moe.MoeError) as e:
         moe.moe_route(s, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, stream=0)
     assert "multiples of 128" in str(e.value) and e.value.code == moe.MOE_ERR_UNSUPPORTED
+
+
+def _parr(*ptrs):
+    arr = (ctypes.c_void_p * 3)(*ptrs)
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def test_backward_rejections(lib):
+    s = tiny()
+    S = ctypes.byref(s)
+    fwd = lib.moe_workspace_bytes(S, moe.MOE_WS_FORWARD)
+    need = lib.moe_backward_workspace_bytes(S)
+    # dY, dH, [dA|dB], dX per routed and shared row, at least
+    R = s.T * (s.topk + s.n_shared)
+    assert need >= 4 * (s.T * s.topk * s.d + R * (s.inter * 3 + s.d))
+    w, wa = _parr(FAKE, FAKE, FAKE)
+    wt, wta = _parr(FAKE, FAKE, None)
+
+    def call(shape=S, fwd_bytes=fwd, ws_bytes=need, routed_wt=wt, du=FAKE, fwd_ws=FAKE):
+        return lib.moe_backward(shape, FAKE, FAKE, w, routed_wt, w, wt, fwd_ws, fwd_bytes, FAKE, du, None, None,
+                                None, None, FAKE, ws_bytes, None)
+
+    assert call(ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
+    assert call(fwd_bytes=fwd - 1) == moe.MOE_ERR_WORKSPACE
+    assert "forward workspace" in moe.moe_last_error()
+    assert call(du=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(fwd_ws=FAKE + 16) == moe.MOE_ERR_INVALID_ARG
+    bad_t, bad_ta = _parr(FAKE, None, None)
+    assert call(routed_wt=bad_t) == moe.MOE_ERR_INVALID_ARG
+    s8 = moe.make_shape(256, 256, 16, 1, 4, 2, 2, 128, "fp8")
+    assert call(shape=ctypes.byref(s8)) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_backward_workspace_bytes(ctypes.byref(s8)) == 0
+    assert lib.moe_transpose_expert_weights(ctypes.byref(s8), 4, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                            None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_transpose_expert_weights(S, -1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_transpose_expert_weights(S, 4, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    # nothing to do: no device access
+    assert lib.moe_transpose_expert_weights(S, 0, None, None, None, None, None, None) == moe.MOE_OK
+    s0 = tiny(T=0)
+    assert lib.moe_backward(ctypes.byref(s0), None, None, None, None, None, None, None, 0, None, None, None, None,
+                            None, None, None, 0, None) == moe.MOE_OK

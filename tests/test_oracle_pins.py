@@ -550,14 +550,17 @@ def test_exact_layer_matches_the_rounding_forward(orc):
     assert np.abs(out_x - out_r).max() <= 2e-5 * np.abs(out_x).max()
 
 
-def test_backward_matches_finite_differences(orc):
+@pytest.mark.parametrize("rs", [1.0, 2.5])
+def test_backward_matches_finite_differences(orc, rs):
     """Central differences of sum(dout * layer) agree with the chain-rule
-    gradient for u, the centroids and all six weight tensors."""
+    gradient for u, the centroids and all six weight tensors, with and
+    without a routed scaling factor on the gates."""
     u, e, idx, rw, sw, dout = _tiny_f64(11)
-    g = orc.moe_backward(u, e, idx, rw, sw, dout)
+    g = orc.moe_backward(u, e, idx, rw, sw, dout, routed_scale=rs)
+    assert np.allclose(orc.layer_f64(u, e, idx, rw, sw, routed_scale=rs)[1].sum(1), rs, rtol=1e-14)
 
     def loss(u_, e_, rw_, sw_):
-        return float((orc.layer_f64(u_, e_, idx, rw_, sw_)[0] * dout).sum())
+        return float((orc.layer_f64(u_, e_, idx, rw_, sw_, routed_scale=rs)[0] * dout).sum())
 
     rng = np.random.default_rng(3)
     h = 1e-6
