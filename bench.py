@@ -11,7 +11,12 @@ measured with HIP events on the launch stream, a `roofline` object for the
 dominant kernel and a `cpu_baseline` object (the CPU oracle on a bounded
 sample of the same workload, timed on this host).
 
-  python bench.py [--steps K] [--warmup W] [--config v3_prefill|v3_decode|v3_fp8|v3_skew|tiny]
+With --backward a step is one forward and one backward (moe_backward: input,
+centroid and expert-weight gradients for an upstream gradient of the layer
+output) of the same batch; the roofline then names the dominant backward
+kernel and the CPU baseline times the oracle's input-gradient chain rule.
+
+  python bench.py [--steps K] [--warmup W] [--config v3_prefill|v3_decode|v3_fp8|v3_skew|tiny] [--backward]
 """
 import argparse
 import json
@@ -68,8 +73,38 @@ def stage_bytes(cfg):
     return dict(router=router, dispatch=dispatch, combine=combine)
 
 
-def profile_path(cfg):
-    return os.path.join(ROOT, "profiles", "moe_forward_%s_pmc.md" % cfg.name)
+BWD_STAGES = ("bwd_combine", "bwd_dh", "bwd_swiglu", "bwd_dx", "bwd_token", "bwd_dgate", "wgrad_down",
+              "wgrad_gate_up")
+
+
+def algorithmic_bwd(cfg, n_touched):
+    """Algorithmic (FLOPs, HBM bytes) per launch of each backward stage: every
+    operand read or written once (weights of touched experts once, u once,
+    activations per expert row once), no padding rows."""
+    T, d, I, K, Ns, Nr = cfg.T, cfg.d, cfg.I, cfg.K, cfg.Ns, cfg.Nr
+    a = esz(cfg.dtype)
+    rr, rs = T * K, T * Ns
+    rows = rr + rs
+    ex = n_touched + Ns
+    gemm = 2.0 * rows * I * d
+    return dict(
+        bwd_combine=(2.0 * rr * d, T * d * a + 2 * rr * d * a + rr * 12),
+        bwd_dh=(gemm, ex * I * d * a + (rr + T) * d * a + rows * I * a),
+        bwd_swiglu=(2 * gemm, ex * 2 * I * d * a + T * d * a + rows * I * a + rows * 2 * I * a),
+        bwd_dx=(2 * gemm, ex * 2 * I * d * a + rows * 2 * I * a + rows * d * a),
+        bwd_token=(2.0 * rows * d, rows * d * a + Nr * d * a + T * d * a + rr * 16 + T * Nr * 0),
+        bwd_dgate=(2.0 * rr * d, T * d * a + Nr * d * 4 + rr * 8),
+        wgrad_down=(gemm, (rr + T) * d * a + rows * I * a + ex * I * d * a),
+        wgrad_gate_up=(2 * gemm, rows * 2 * I * a + T * d * a + ex * 2 * I * d * a))
+
+
+BWD_KERNELS = {"bwd_combine": "bwd_combine_kernel", "bwd_dh": "bwd_dh", "bwd_swiglu": "bwd_swiglu",
+               "bwd_dx": "bwd_dx", "bwd_token": "bwd_token_kernel", "bwd_dgate": "dgate_kernel",
+               "wgrad_down": "wgrad_down", "wgrad_gate_up": "wgrad_gate_up"}
+
+
+def profile_path(cfg, backward=False):
+    return os.path.join(ROOT, "profiles", "moe_%s_%s_pmc.md" % ("backward" if backward else "forward", cfg.name))
 
 
 STAGE_KERNELS = {"router": ("router_gemm_kernel", "router_select_kernel"),
@@ -77,16 +112,16 @@ STAGE_KERNELS = {"router": ("router_gemm_kernel", "router_select_kernel"),
                  "combine": ("combine_kernel",)}
 
 
-def traffic_from_profile(cfg, kernel):
+def traffic_from_profile(cfg, kernel, backward=False):
     """HBM bytes per launch of `kernel` (a name or a tuple of names, summed)
     from the committed rocprofv3 PMC summary, or None when there is none for
     this workload or the kernel sources changed since it was taken."""
     if isinstance(kernel, tuple):
-        parts = [traffic_from_profile(cfg, k) for k in kernel]
+        parts = [traffic_from_profile(cfg, k, backward) for k in kernel]
         parts = [p for p in parts if p is not None]
         return sum(parts) if parts else None
     from mixture_experts_layer_35_amd.profsum import source_hash
-    path = profile_path(cfg)
+    path = profile_path(cfg, backward)
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -134,6 +169,28 @@ def cpu_baseline(cfg, inp, n_tokens):
                                                                dt)}
 
 
+def cpu_baseline_backward(cfg, inp, n_tokens):
+    """The oracle's chain rule for the input gradient (du, dL/dg) of the first
+    n_tokens tokens taken as a batch of their own, at the oracle's routing."""
+    import oracle
+    import moe_synth as syn
+    import numpy as np
+    n = min(n_tokens, cfg.T)
+    u = inp["u"][:n]
+    dout = syn.grad_output(cfg)[:n]
+    dout = (dout.astype(np.uint32) << 16).view(np.float32) if dout.dtype == np.uint16 else dout
+    _, idx, _ = oracle.route(u, inp["gate_w"], inp["bias"], G=cfg.G, Mg=cfg.Mg, K=cfg.K)
+    shared = (inp["swg"], inp["swu"], inp["swd"]) if cfg.Ns else None
+    t0 = time.perf_counter()
+    oracle.moe_backward(u, inp["gate_w"], idx, (inp["wg"], inp["wu"], inp["wd"]), shared, dout,
+                        experts=np.zeros(0, np.int32), dgate=False, dshared=False)
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "input-gradient chain rule (du and dL/dg: %d routed + %d shared SwiGLU experts recomputed "
+                      "and differentiated per token, fp64) for the first %d tokens of the %d-token batch; weight "
+                      "and centroid gradients not in the sample; %.1f s" % (cfg.K, cfg.Ns, n, cfg.T, dt)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +199,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", default="v3_prefill")
     ap.add_argument("--cpu-tokens", type=int, default=640, help="tokens in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time forward + backward (input, centroid and expert-weight gradients) per step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counter scaling)")
     args = ap.parse_args()
@@ -159,6 +218,9 @@ def main():
     from mixture_experts_layer_35_amd.layer import MoeLayer, to_device
 
     cfg = syn.CONFIGS[args.config]
+    if args.backward and cfg.dtype == "fp8":
+        print("bench.py: the backward runs on fp32 / bf16 layers", file=sys.stderr)
+        sys.exit(2)
     if args.steps is None:
         args.steps = syn.SKEW_STEPS if cfg.skew else 20
     torch.cuda.set_device(0)
@@ -185,9 +247,29 @@ def main():
     stream = torch.cuda.current_stream()
     bias0 = layer.bias.clone()
 
-    def step(k, events=None):
+    bw = None
+    if args.backward:
+        # weight transposes are weight preparation (once per weight update), timed apart
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        rt, st = layer.transposed_weights(stream)
+        e1.record()
+        torch.cuda.synchronize()
+        bw = dict(rt=rt, st=st, transpose_ms=e0.elapsed_time(e1),
+                  dout=to_device(syn.grad_output(cfg)), du=torch.empty_like(us[0]),
+                  dgate=torch.empty((cfg.Nr, cfg.d), dtype=torch.float32, device="cuda"),
+                  dr=tuple(torch.empty_like(w) for w in layer.routed_w),
+                  ds=tuple(torch.empty_like(w) for w in layer.shared_w) if cfg.Ns else None,
+                  ws=torch.empty(max(moe.moe_backward_workspace_bytes(shape), 256), dtype=torch.uint8,
+                                 device="cuda"))
+
+    def step(k, events=None, bevents=None):
         moe.moe_forward_timed(shape, us[k % len(us)], layer.gate_w, layer.bias, layer.routed_w, layer.routed_s,
                               layer.shared_w, layer.shared_s, out, None, None, counts[k], None, ws, stream, events)
+        if bw is not None:
+            moe.moe_backward_timed(shape, us[k % len(us)], layer.gate_w, layer.routed_w, bw["rt"], layer.shared_w,
+                                   bw["st"], ws, bw["dout"], bw["du"], bw["dgate"], bw["dr"], bw["ds"], None,
+                                   bw["ws"], stream, bevents)
         if cfg.skew:
             moe.moe_bias_update(shape, counts[k], layer.bias, syn.SKEW_GAMMA, stream)
 
@@ -195,24 +277,35 @@ def main():
         step(0)
     layer.bias.copy_(bias0)
     # events: created and recorded once so that their handles exist
-    evs = []
-    for _ in range(args.steps):
-        row = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        for e in row:
-            e.record()
-        evs.append(row)
+
+    def event_rows(n):
+        rows = []
+        for _ in range(args.steps):
+            row = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+            for e in row:
+                e.record()
+            rows.append(row)
+        return rows
+
+    evs = event_rows(6)
+    bevs = event_rows(9) if bw is not None else None
     torch.cuda.synchronize()
     handles = [[e.cuda_event for e in row] for row in evs]
+    bhandles = [[e.cuda_event for e in row] for row in bevs] if bevs else [None] * args.steps
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(k, handles[k])
+        step(k, handles[k], bhandles[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1000.0 / args.steps
     stage_ms = {name: float(np.mean([evs[k][i].elapsed_time(evs[k][i + 1]) for k in range(args.steps)]))
                 for i, name in enumerate(STAGES)}
+    bstage_ms = None
+    if bevs:
+        bstage_ms = {name: float(np.mean([bevs[k][i].elapsed_time(bevs[k][i + 1]) for k in range(args.steps)]))
+                     for i, name in enumerate(BWD_STAGES)}
 
     cnt = counts.cpu().numpy()
     n_touched = int(np.mean([(c > 0).sum() for c in cnt]))
@@ -224,10 +317,15 @@ def main():
                 "min_over_mean": [round(float(c.min() / mean), 3) for c in cnt],
                 "step_ms": [round(float(evs[k][0].elapsed_time(evs[k][5])), 4) for k in range(args.steps)],
                 "bias_range_after": [round(float(layer.bias.min()), 4), round(float(layer.bias.max()), 4)]}
-    alg = algorithmic(cfg, n_touched)
-    dom = max(("ffn_gate_up", "ffn_down"), key=lambda k: stage_ms[k])
+    if bw is None:
+        alg = algorithmic(cfg, n_touched)
+        dom = max(("ffn_gate_up", "ffn_down"), key=lambda k: stage_ms[k])
+        t_dom = stage_ms[dom] / 1000.0
+    else:
+        alg = algorithmic_bwd(cfg, n_touched)
+        dom = max(BWD_STAGES, key=lambda k: bstage_ms[k])
+        t_dom = bstage_ms[dom] / 1000.0
     flops, nbytes = alg[dom]
-    t_dom = stage_ms[dom] / 1000.0
     peak_f = PEAK_TFLOPS[cfg.dtype]
     ridge = peak_f * 1e12 / (PEAK_HBM_GBS * 1e9)
     if flops / nbytes < ridge:
@@ -235,12 +333,23 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(flops / t_dom / 1e12, 1), "peak": peak_f, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    tr = traffic_from_profile(cfg, dom)
+    tr = traffic_from_profile(cfg, dom) if bw is None else traffic_from_profile(cfg, BWD_KERNELS[dom], True)
     roof["traffic"] = tr
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
-    roof["kernel_ms"] = round(stage_ms[dom], 4)
+    roof["kernel_ms"] = round(t_dom * 1000.0, 4)
+    bwd_stages = None
+    if bw is not None:
+        bwd_stages = {}
+        for name in BWD_STAGES:
+            f, nb = alg[name]
+            t = bstage_ms[name] / 1000.0
+            bwd_stages[name] = {"ms": round(bstage_ms[name], 4), "algorithmic_bytes": int(nb),
+                                "algorithmic_flops": f,
+                                "GB/s": round(nb / t / 1e9, 1) if t > 0 else None,
+                                "TFLOP/s": round(f / t / 1e12, 1) if t > 0 else None,
+                                "traffic": traffic_from_profile(cfg, BWD_KERNELS[name], True)}
 
     hbm_stages = {}
     for name, nb in stage_bytes(cfg).items():
@@ -249,6 +358,9 @@ def main():
                             "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "traffic": traffic_from_profile(cfg, STAGE_KERNELS[name])}
     layer_flops = T * cfg.flops_per_token
+    if bw is not None:
+        layer_flops += sum(f for name, (f, _) in alg.items() if name in ("bwd_dh", "bwd_swiglu", "bwd_dx",
+                                                                         "wgrad_down", "wgrad_gate_up"))
     tflops = layer_flops / (ms / 1000.0) / 1e12
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -259,16 +371,20 @@ def main():
 
     cpu = None
     if args.cpu_tokens > 0:
-        cpu = cpu_baseline(cfg, inp, args.cpu_tokens)
+        cpu = cpu_baseline(cfg, inp, args.cpu_tokens) if bw is None else \
+            cpu_baseline_backward(cfg, inp, max(1, args.cpu_tokens // 8))
 
-    wl = ("%s: DeepSeekMoE layer forward, T=%d tokens, d=%d, %d routed + %d shared SwiGLU experts (I=%d), "
-          "%d groups / top-%d groups / top-%d experts, %s" % (cfg.name, T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.G, cfg.Mg,
+    wl = ("%s: DeepSeekMoE layer %s, T=%d tokens, d=%d, %d routed + %d shared SwiGLU experts (I=%d), "
+          "%d groups / top-%d groups / top-%d experts, %s" % (cfg.name, "forward" if bw is None else
+                                                           "forward + backward (input, centroid and "
+                                                           "expert-weight gradients)", T, cfg.d, cfg.Nr, cfg.Ns, cfg.I, cfg.G, cfg.Mg,
                                                            cfg.K, {"bf16": "bf16 storage, fp32 accumulation",
                                                                    "fp8": "e4m3 expert GEMMs (1x128 / 128x128 fp32 "
                                                                           "scales), bf16 in/out",
                                                                    "fp32": "fp32"}[cfg.dtype]))
     line = {
-        "metric": "MoE layer tokens/s + achieved TFLOP/s (% MFMA peak), V3 shape bf16/fp8",
+        "metric": "MoE layer tokens/s + achieved TFLOP/s (% MFMA peak), V3 shape bf16/fp8" if bw is None else
+                  "MoE layer forward+backward tokens/s + achieved TFLOP/s, V3 shape bf16",
         "value": round(T / (ms / 1000.0), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -285,6 +401,9 @@ def main():
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / peak_f, 4),
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "backward_stages": bwd_stages,
+        "backward_ms": round(sum(bstage_ms.values()), 4) if bstage_ms else None,
+        "weight_transpose_ms": round(bw["transpose_ms"], 4) if bw is not None else None,
         "experts_touched": n_touched,
         "roofline": roof,
         "hbm_stages": hbm_stages,

@@ -268,6 +268,24 @@ int moe_backward(const moe_shape *shape, const void *u, const void *gate_w, cons
                  void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes,
                  void *stream);
 
+/*
+ * moe_backward_timed -- moe_backward that also records caller-created HIP
+ * events on `stream` at its stage boundaries:
+ *   stage_events[0] before the combine gradient   [1] after it (dY, dg)
+ *   [2] after dH = dY W_down                      [3] after the SwiGLU gradient pass ([dA | dB])
+ *   [4] after dX = [dA | dB] [W_gate ; W_up]      [5] after the token pass (du, dz)
+ *   [6] after the centroid gradient               [7] after dW_down
+ *   [8] after dW_gate / dW_up
+ * NULL entries (or a NULL array, 9 entries otherwise) are skipped; skipped
+ * optional outputs leave their stage empty.  Results are identical to
+ * moe_backward.
+ */
+int moe_backward_timed(const moe_shape *shape, const void *u, const void *gate_w, const void *const *routed_w,
+                       const void *const *routed_wt, const void *const *shared_w, const void *const *shared_wt,
+                       const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du, float *dgate_w,
+                       void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes,
+                       void *stream, void *const *stage_events);
+
 /* Workspace bytes for moe_backward (0 when rejected). */
 size_t moe_backward_workspace_bytes(const moe_shape *shape);
 

@@ -27,7 +27,7 @@ MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_FORWARD = 0, 1, 2
 EXPORTED = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_timed",
             "moe_workspace_bytes",
             "moe_ffn_workspace_bytes", "moe_bias_update", "moe_seq_balance", "moe_seq_balance_workspace_bytes",
-            "moe_transpose_expert_weights", "moe_backward", "moe_backward_workspace_bytes",
+            "moe_transpose_expert_weights", "moe_backward", "moe_backward_timed", "moe_backward_workspace_bytes",
             "moe_quantize_1x128", "moe_quantize_weights_128x128", "moe_last_error", "moe_version")
 
 
@@ -82,6 +82,7 @@ def lib():
                 "moe_seq_balance": [S, P, P, i64, ctypes.c_float, P, P, P, P, sz, P],
                 "moe_transpose_expert_weights": [S, i32, P, P, P, P, P, P],
                 "moe_backward": [S, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, sz, P],
+                "moe_backward_timed": [S, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, sz, P, P],
                 "moe_quantize_1x128": [i64, i32, i32, P, P, P, P],
                 "moe_quantize_weights_128x128": [i64, i32, i32, i32, P, P, P, P],
             }
@@ -254,6 +255,22 @@ def moe_backward(shape, u, gate_w, routed_w, routed_wt, shared_w, shared_wt, fwd
                                      _ptr(fwd_ws), _nbytes(fwd_ws), _ptr(dout), _ptr(du), _ptr(dgate_w),
                                      dr[0] if dr else None, ds[0] if ds else None, _ptr(dtopk_w), _ptr(ws),
                                      _nbytes(ws), _stream(stream)))
+
+
+def moe_backward_timed(shape, u, gate_w, routed_w, routed_wt, shared_w, shared_wt, fwd_ws, dout, du, dgate_w=None,
+                       d_routed_w=None, d_shared_w=None, dtopk_w=None, ws=None, stream=None, stage_events=None):
+    """stage_events: 9 raw hipEvent_t handles (ints) or None."""
+    rw, rt, sw, st, dr, ds = (_ptr_array(x) for x in (routed_w, routed_wt, shared_w, shared_wt, d_routed_w,
+                                                       d_shared_w))
+    ev = None
+    if stage_events is not None:
+        arr = (ctypes.c_void_p * 9)(*stage_events)
+        ev = ctypes.cast(arr, ctypes.c_void_p)
+    return _check(lib().moe_backward_timed(ctypes.byref(shape), _ptr(u), _ptr(gate_w), rw[0] if rw else None,
+                                           rt[0] if rt else None, sw[0] if sw else None, st[0] if st else None,
+                                           _ptr(fwd_ws), _nbytes(fwd_ws), _ptr(dout), _ptr(du), _ptr(dgate_w),
+                                           dr[0] if dr else None, ds[0] if ds else None, _ptr(dtopk_w), _ptr(ws),
+                                           _nbytes(ws), _stream(stream), ev))
 
 
 def moe_quantize_1x128(rows, cols, x_dtype, x, q, s, stream=None):

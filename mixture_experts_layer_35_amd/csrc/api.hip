@@ -523,11 +523,11 @@ int moe_transpose_expert_weights(const moe_shape *s, int32_t n, const void *w_ga
     return MOE_OK;
 }
 
-int moe_backward(const moe_shape *s, const void *u, const void *gate_w, const void *const *routed_w,
-                 const void *const *routed_wt, const void *const *shared_w, const void *const *shared_wt,
-                 const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du, float *dgate_w,
-                 void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes,
-                 void *stream) {
+static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, const void *const *routed_w,
+                         const void *const *routed_wt, const void *const *shared_w, const void *const *shared_wt,
+                         const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du, float *dgate_w,
+                         void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes,
+                         void *stream, void *const *ev) {
     const char *fn = "moe_backward";
     int rc = check_bwd_shape(s, fn);
     if (rc) return rc;
@@ -577,8 +577,13 @@ int moe_backward(const moe_shape *s, const void *u, const void *gate_w, const vo
     float *dz = (float *)(W + L.dz);
     char *dh_s = dh + (size_t)TK * I * a_sz, *dab_s = dab + (size_t)TK * 2 * I * a_sz, *dx_s = dx + (size_t)TK * d * a_sz;
 
+    auto mark = [&](int i) -> hipError_t {
+        return (ev && ev[i]) ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
+    };
+    HIPCHK(mark(0));
     // 1. combine: dY rows and gate gradients
     HIPCHK(launch_bwd_combine(dt, dout, Fw + F.yperm, inv, tw, T, d, s->topk, dy, dg, st));
+    HIPCHK(mark(1));
     // 2. dH = dY . W_down (transposed copies [n][I][d])
     FfnProblem p[2] = {}, q[2] = {};
     p[0].n_exp = s->n_routed;
@@ -599,7 +604,8 @@ int moe_backward(const moe_shape *s, const void *u, const void *gate_w, const vo
     fa.K = d;
     fa.F = I;
     for (int i = 0; i < fa.nprob; ++i) fa.p[i] = p[fa.nprob - 1 - i];
-    HIPCHK(launch_ffn(dt, FFN_DOWN, fa, st));
+    HIPCHK(launch_ffn(dt, FFN_BWD_DH, fa, st));
+    HIPCHK(mark(2));
     // 3. gate/up recomputed from u; SwiGLU gradient against dH -> [dA | dB]
     q[0].n_exp = s->n_routed;
     q[0].offsets = offsets;
@@ -623,6 +629,7 @@ int moe_backward(const moe_shape *s, const void *u, const void *gate_w, const vo
     }
     for (int i = 0; i < fa.nprob; ++i) fa.p[i] = q[fa.nprob - 1 - i];
     HIPCHK(launch_ffn(dt, FFN_GATEUP_BWD, fa, st));
+    HIPCHK(mark(3));
     // 4. dX = [dA | dB] . [W_gate ; W_up] (transposed copies [n][d][2I])
     FfnProblem r[2] = {};
     r[0].n_exp = s->n_routed;
@@ -640,33 +647,26 @@ int moe_backward(const moe_shape *s, const void *u, const void *gate_w, const vo
     fa.K = 2 * I;
     fa.F = d;
     for (int i = 0; i < fa.nprob; ++i) fa.p[i] = r[fa.nprob - 1 - i];
-    HIPCHK(launch_ffn(dt, FFN_DOWN, fa, st));
+    HIPCHK(launch_ffn(dt, FFN_BWD_DX, fa, st));
+    HIPCHK(mark(4));
     // 5. du: dispatch sum and router chain; dz per row
     HIPCHK(launch_bwd_token(dt, dx, dx_s, Ns, inv, idx, scores, dg, gate_w, T, d, s->n_routed, s->topk,
                             s->routed_scale, du, dz, st));
+    HIPCHK(mark(5));
     // 6. centroid gradient
     if (dgate_w) HIPCHK(launch_dgate(dt, u, perm, offsets, dz, s->n_routed, d, dgate_w, st));
+    HIPCHK(mark(6));
     // 7. weight gradients: down (dY rows x H rows), then gate/up ([dA | dB] rows x gathered u rows)
     if (d_routed_w || (Ns && d_shared_w)) {
+        // shared experts first: their long reductions start early, spread over every XCD
+        const int64_t hint = (TK + s->n_routed - 1) / s->n_routed;
         WgradArgs wa{};
         int np = 0;
-        if (d_routed_w) {
-            WgradProblem &w = wa.p[np++];
-            w.n_exp = s->n_routed;
-            w.offsets = offsets;
-            w.P = dy;
-            w.P_ld = d;
-            w.Q = Fw + F.h;
-            w.Q_ld = I;
-            w.Pdim = d;
-            w.Qdim = I;
-            w.split = d;
-            w.out0 = d_routed_w[2];
-        }
         if (Ns && d_shared_w) {
             WgradProblem &w = wa.p[np++];
             w.n_exp = Ns;
             w.rows_fixed = T;
+            w.rows_hint = T;
             w.p_local = 1;
             w.P = dout;
             w.P_ld = d;
@@ -677,30 +677,30 @@ int moe_backward(const moe_shape *s, const void *u, const void *gate_w, const vo
             w.split = d;
             w.out0 = d_shared_w[2];
         }
-        wa.nprob = np;
-        HIPCHK(launch_wgrad(dt, wa, st));
-        np = 0;
         if (d_routed_w) {
             WgradProblem &w = wa.p[np++];
-            w = WgradProblem{};
             w.n_exp = s->n_routed;
             w.offsets = offsets;
-            w.P = dab;
-            w.P_ld = 2 * I;
-            w.Q = u;
-            w.Q_ld = d;
-            w.q_gather = perm;
-            w.Pdim = 2 * I;
-            w.Qdim = d;
-            w.split = I;
-            w.out0 = d_routed_w[0];
-            w.out1 = d_routed_w[1];
+            w.rows_hint = hint;
+            w.P = dy;
+            w.P_ld = d;
+            w.Q = Fw + F.h;
+            w.Q_ld = I;
+            w.Pdim = d;
+            w.Qdim = I;
+            w.split = d;
+            w.out0 = d_routed_w[2];
         }
+        wa.nprob = np;
+        HIPCHK(launch_wgrad(dt, 0, wa, st));
+        HIPCHK(mark(7));
+        np = 0;
         if (Ns && d_shared_w) {
             WgradProblem &w = wa.p[np++];
             w = WgradProblem{};
             w.n_exp = Ns;
             w.rows_fixed = T;
+            w.rows_hint = T;
             w.q_local = 1;
             w.P = dab_s;
             w.P_ld = 2 * I;
@@ -712,10 +712,48 @@ int moe_backward(const moe_shape *s, const void *u, const void *gate_w, const vo
             w.out0 = d_shared_w[0];
             w.out1 = d_shared_w[1];
         }
+        if (d_routed_w) {
+            WgradProblem &w = wa.p[np++];
+            w = WgradProblem{};
+            w.n_exp = s->n_routed;
+            w.offsets = offsets;
+            w.rows_hint = hint;
+            w.P = dab;
+            w.P_ld = 2 * I;
+            w.Q = u;
+            w.Q_ld = d;
+            w.q_gather = perm;
+            w.Pdim = 2 * I;
+            w.Qdim = d;
+            w.split = I;
+            w.out0 = d_routed_w[0];
+            w.out1 = d_routed_w[1];
+        }
         wa.nprob = np;
-        HIPCHK(launch_wgrad(dt, wa, st));
+        HIPCHK(launch_wgrad(dt, 1, wa, st));
+    } else {
+        HIPCHK(mark(7));
     }
+    HIPCHK(mark(8));
     return MOE_OK;
+}
+
+int moe_backward(const moe_shape *s, const void *u, const void *gate_w, const void *const *routed_w,
+                 const void *const *routed_wt, const void *const *shared_w, const void *const *shared_wt,
+                 const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du, float *dgate_w,
+                 void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes,
+                 void *stream) {
+    return backward_impl(s, u, gate_w, routed_w, routed_wt, shared_w, shared_wt, fwd_ws, fwd_ws_bytes, dout, du,
+                         dgate_w, d_routed_w, d_shared_w, dtopk_w, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_backward_timed(const moe_shape *s, const void *u, const void *gate_w, const void *const *routed_w,
+                       const void *const *routed_wt, const void *const *shared_w, const void *const *shared_wt,
+                       const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du, float *dgate_w,
+                       void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes,
+                       void *stream, void *const *stage_events) {
+    return backward_impl(s, u, gate_w, routed_w, routed_wt, shared_w, shared_wt, fwd_ws, fwd_ws_bytes, dout, du,
+                         dgate_w, d_routed_w, d_shared_w, dtopk_w, ws, ws_bytes, stream, stage_events);
 }
 
 size_t moe_seq_balance_workspace_bytes(const moe_shape *s, int64_t seq_len) {

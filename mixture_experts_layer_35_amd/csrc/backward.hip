@@ -13,6 +13,10 @@
 // the centroid gradient, the weight-gradient GEMM and the weight transpose.
 #include "common.h"
 #include "internal.h"
+#include "lds_ring.h"
+
+#include <mutex>
+#include <type_traits>
 
 namespace moe {
 
@@ -202,113 +206,477 @@ __global__ __launch_bounds__(BW_NT) void dgate_kernel(const void *__restrict__ u
     *(f32x4 *)(dgate + (int64_t)i * d + c + 4) = f32x4{acc[4], acc[5], acc[6], acc[7]};
 }
 
+// ---- weight-gradient tile order ---------------------------------------------
+// A tile is (problem, expert, 128-wide p tile, group of 128-wide q tiles); the
+// group size wg_qgroup keeps roughly 32 reduction steps per workgroup.  Tiles
+// of a fixed-rows problem (the shared experts: every token, long reductions)
+// come first, one per workgroup in launch order so they spread over all XCDs
+// and start early; the routed experts' tiles follow in contiguous ranges per
+// XCD (workgroup b runs on XCD b % 8), so an expert's activations are read
+// into one or two L2s rather than all eight.
+__host__ __device__ inline int wg_qgroup(const WgradProblem &P) {
+    const int nqt = P.Qdim / 128;
+    const int64_t steps = (P.rows_hint + 31) / 32;
+    const int g = steps >= 32 ? 1 : (int)(32 / (steps > 0 ? steps : 1));
+    return g < nqt ? g : nqt;
+}
+__host__ __device__ inline int64_t wg_tiles(const WgradProblem &P) {
+    const int nqt = P.Qdim / 128, g = wg_qgroup(P);
+    return (int64_t)P.n_exp * (P.Pdim / 128) * ((nqt + g - 1) / g);
+}
+
+struct WgTile {
+    int pi, e, p0, qt0, nq;
+};
+
+// workgroup b -> tile; false for a workgroup with no tile
+__device__ inline bool wg_decode(const WgradArgs &a, int64_t nlead, int64_t ntiles, int64_t b, WgTile &T) {
+    int64_t t;
+    const int64_t nlead8 = (nlead + 7) / 8 * 8;
+    if (b < nlead) {
+        t = b;
+    } else if (b < nlead8) {
+        return false;
+    } else {
+        const int64_t c = b - nlead8, per_xcd = (ntiles - nlead + 7) / 8;
+        t = nlead + (c & 7) * per_xcd + (c >> 3);
+        if (t >= ntiles) return false;
+    }
+    T.pi = 0;
+    const int64_t t0 = wg_tiles(a.p[0]);
+    if (a.nprob > 1 && t >= t0) {
+        t -= t0;
+        T.pi = 1;
+    }
+    const WgradProblem &P = T.pi ? a.p[1] : a.p[0];
+    const int ptiles = P.Pdim / 128, nqt = P.Qdim / 128, g = wg_qgroup(P);
+    const int ngroups = (nqt + g - 1) / g;
+    T.e = (int)(t / ((int64_t)ptiles * ngroups));
+    const int r = (int)(t - (int64_t)T.e * ptiles * ngroups);
+    T.p0 = (r / ngroups) * 128;
+    T.qt0 = (r % ngroups) * g;
+    T.nq = min(g, nqt - T.qt0);
+    return true;
+}
+
 // ---- weight gradient: C[p][q] = sum over an expert's rows r of P[r][p] Q[qrow(r)][q] ----
-// Tile 128 (p) x 128 (q) per 256-thread workgroup (2 x 2 waves of 64 x 64).  Each
-// 32-row step stages P and Q transposed in LDS ([p][r], [q][r], rows padded), so
-// MFMA fragments (8 consecutive r per lane) are single 16-byte reads.  Q is the
-// MFMA row operand: a lane's four results are four consecutive q of one p, one
-// store into C's row p.  All of an expert's rows are reduced in one tile, in
-// order: no cross-tile reduction, deterministic.
-constexpr int WG_T = 128, WG_R = 32, WG_LD = WG_R + 8;   // LDS row: 32 values + pad
+// fp32 layers.  A workgroup (4 waves, 2 x 2 of 64 x 64) owns one tile of the
+// order above, walked in 32-row reduction steps per q tile.
+// Every step stages 32 rows x 128 values of P and of Q transposed in LDS
+// ([value][row], rows contiguous), so MFMA fragments (8 consecutive rows per
+// lane) are two 8-byte reads.  Half the threads stage P and half Q: a thread
+// loads a 4-row x 8-value patch (four 16-byte loads, coalesced along the row)
+// and writes its eight 4-row columns as 8-byte stores; the 4-row group's slot
+// inside an LDS row is XOR-swizzled by the row index so that neither the
+// stores nor the fragment reads pile onto a few banks.  Two LDS buffers: the
+// global loads of step i+1 are in flight while step i runs its MFMAs.  Q is
+// the MFMA row operand (a lane's four results are four consecutive q of one
+// p).  All of an expert's rows are reduced in one tile, in order: no
+// cross-tile reduction, deterministic.
+constexpr int WG_T = 128, WG_R = 32;
 
 template <int DT>
-__global__ __launch_bounds__(BW_NT) void wgrad_kernel(const WgradArgs a) {
-    typedef typename std::conditional<DT == DT_BF16, uint16_t, float>::type E;
-    __shared__ E Pt[WG_T][WG_LD];
-    __shared__ E Qt[WG_T][WG_LD];
+struct WgLds {
+    static constexpr int LDW = DT == DT_BF16 ? 20 : 36;   // dwords per LDS row (32 rows of the step + pad)
+    static constexpr int GW = DT == DT_BF16 ? 2 : 4;      // dwords per 4-row group
+};
+
+__device__ __forceinline__ int wg_swz(int p) { return (p ^ (p >> 4)) & 7; }
+
+template <int DT>
+struct WgPatch {
+    // 4 rows x 8 values as raw bits: bf16 in v[k][0], fp32 in v[k][0..1]
+    u32x4 v[4][DT == DT_BF16 ? 1 : 2];
+};
+
+// PASS only separates the down and gate/up instantiations in profiles.
+template <int DT, int PASS>
+__global__ __launch_bounds__(BW_NT) void wgrad_kernel(const WgradArgs a, int64_t nlead, int64_t ntiles) {
+    constexpr int LDW = WgLds<DT>::LDW, GW = WgLds<DT>::GW;
+    __shared__ __align__(16) uint32_t lds[2][2][WG_T * LDW];   // [buffer][P, Q][value][row]
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int wp = wid >> 1, wq = wid & 1;
 
-    // tile -> (problem, expert, p-tile, q-tile)
-    int64_t t = blockIdx.x;
-    int pi = 0;
-    const int64_t per0 = (int64_t)(a.p[0].Pdim / WG_T) * (a.p[0].Qdim / WG_T);
-    if (a.nprob > 1 && t >= (int64_t)a.p[0].n_exp * per0) { t -= (int64_t)a.p[0].n_exp * per0; pi = 1; }
-    const WgradProblem &P = pi ? a.p[1] : a.p[0];
-    const int ptiles = P.Pdim / WG_T, qtiles = P.Qdim / WG_T;
-    const int e = (int)(t / ((int64_t)ptiles * qtiles));
-    const int64_t tt = t % ((int64_t)ptiles * qtiles);
-    const int p0 = (int)(tt / qtiles) * WG_T, q0 = (int)(tt % qtiles) * WG_T;
+    WgTile T;
+    if (!wg_decode(a, nlead, ntiles, blockIdx.x, T)) return;
+    const WgradProblem &P = T.pi ? a.p[1] : a.p[0];
+    const int e = T.e, p0 = T.p0, qt0 = T.qt0, nq = T.nq;
     const int64_t rb = P.offsets ? (int64_t)P.offsets[e] : (int64_t)e * P.rows_fixed;
     const int64_t M = P.offsets ? (int64_t)P.offsets[e + 1] - rb : P.rows_fixed;
+    const int nsteps = (int)((M + WG_R - 1) / WG_R);
+    const int total = nq * nsteps;
+
+    // output rows of this lane: p = p0 + wp*64 + j*16 + (lane&15); columns q = q0 + wq*64 + i*16 + 4*(lane>>4)
+    const int split_rows = P.split < P.Pdim ? P.split : P.Pdim;
+    auto store_tile = [&](int q0, const f32x4 (&acc)[4][4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int p = p0 + wp * 64 + j * 16 + (lane & 15);
+            void *out = p < P.split ? P.out0 : P.out1;
+            const int prow = p < P.split ? p : p - P.split;
+            const int64_t base = ((int64_t)e * split_rows + prow) * P.Qdim;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = q0 + wq * 64 + i * 16 + 4 * (lane >> 4);
+                if (DT == DT_BF16) {
+                    *(u32x2 *)((uint16_t *)out + base + q) =
+                        u32x2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+                } else {
+                    *(f32x4 *)((float *)out + base + q) = acc[i][j];
+                }
+            }
+        }
+    };
 
     f32x4 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    if (total == 0) {   // an expert without rows: its gradient is zero
+        for (int q = 0; q < nq; ++q) store_tile((qt0 + q) * WG_T, acc);
+        return;
+    }
 
-    for (int64_t r0 = 0; r0 < M; r0 += WG_R) {
-        // stage: 32 rows x 128 values of P and of Q; thread takes 16 values of each (2 x 8)
+    // staging role: threads 0..127 stage P, 128..255 stage Q; patch (rg, cg) = rows 4rg..4rg+3, values 8cg..8cg+7
+    const int op = tid >> 7, pt = tid & 127, cg = pt & 15, rg = pt >> 4;
+    auto load = [&](int it, WgPatch<DT> &x) {
+        const int q0 = (qt0 + it / nsteps) * WG_T;
+        const int64_t r0 = (int64_t)(it % nsteps) * WG_R + rg * 4;
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int id = tid + BW_NT * h;         // 0..511: row id / 16, 8 values at (id % 16) * 8
-            const int rr = id >> 4, cc = (id & 15) * 8;
-            const int64_t r = r0 + rr;
-            float pv[8], qv[8];
+        for (int k = 0; k < 4; ++k) {
+            const int64_t r = r0 + k;
             if (r < M) {
                 const int64_t R = rb + r;
-                ld8v<DT>(P.P, (P.p_local ? r : R) * P.P_ld + p0 + cc, pv);
-                const int64_t QR = P.q_gather ? (int64_t)P.q_gather[R] : (P.q_local ? r : R);
-                ld8v<DT>(P.Q, QR * P.Q_ld + q0 + cc, qv);
-            } else {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) { pv[q] = 0.0f; qv[q] = 0.0f; }
-            }
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                if (DT == DT_BF16) {
-                    Pt[cc + q][rr] = (E)(__float_as_uint(pv[q]) >> 16);   // exact: the values are bf16
-                    Qt[cc + q][rr] = (E)(__float_as_uint(qv[q]) >> 16);
+                const char *src;
+                if (op == 0) {
+                    src = (const char *)P.P + ((P.p_local ? r : R) * P.P_ld + p0 + cg * 8) * (DT == DT_BF16 ? 2 : 4);
                 } else {
-                    Pt[cc + q][rr] = pv[q];
-                    Qt[cc + q][rr] = qv[q];
+                    const int64_t QR = P.q_gather ? (int64_t)P.q_gather[R] : (P.q_local ? r : R);
+                    src = (const char *)P.Q + (QR * P.Q_ld + q0 + cg * 8) * (DT == DT_BF16 ? 2 : 4);
                 }
+                x.v[k][0] = *(const u32x4 *)src;
+                if (DT != DT_BF16) x.v[k][DT == DT_BF16 ? 0 : 1] = *(const u32x4 *)(src + 16);
+            } else {
+                x.v[k][0] = {};
+                x.v[k][DT == DT_BF16 ? 0 : 1] = {};
             }
         }
-        __syncthreads();
+    };
+    auto stage = [&](int buf, const WgPatch<DT> &x) {
+        uint32_t *dst = lds[buf][op];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const int v = cg * 8 + c;
+            uint32_t *d = dst + v * LDW + GW * (rg ^ wg_swz(v));
+            if (DT == DT_BF16) {
+                const int w = c >> 1;
+                uint32_t r4[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) r4[k] = x.v[k][0][w];
+                const uint32_t lo = (c & 1) ? ((r4[0] >> 16) | (r4[1] & 0xFFFF0000u))
+                                            : ((r4[0] & 0xFFFFu) | (r4[1] << 16));
+                const uint32_t hi = (c & 1) ? ((r4[2] >> 16) | (r4[3] & 0xFFFF0000u))
+                                            : ((r4[2] & 0xFFFFu) | (r4[3] << 16));
+                *(u32x2 *)d = u32x2{lo, hi};
+            } else {
+                uint32_t f4[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) f4[k] = x.v[k][(c >> 2) & (DT == DT_BF16 ? 0 : 1)][c & 3];
+                *(u32x4 *)d = u32x4{f4[0], f4[1], f4[2], f4[3]};
+            }
+        }
+    };
+    auto compute = [&](int buf) {
+        const uint32_t *Ps = lds[buf][0], *Qs = lds[buf][1];
         if (DT == DT_BF16) {
+            // 16x16x32: lane supplies rows 8*(lane>>4) .. +7 = 4-row groups g0, g0 + 1
+            const int g0 = 2 * (lane >> 4);
             bf16x8 qa[4], pb[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                qa[i] = *(const bf16x8 *)&Qt[wq * 64 + i * 16 + (lane & 15)][8 * (lane >> 4)];
+            for (int i = 0; i < 4; ++i) {
+                const int v = wq * 64 + i * 16 + (lane & 15);
+                const uint32_t *row = Qs + v * LDW;
+                const u32x2 x0 = *(const u32x2 *)(row + 2 * (g0 ^ wg_swz(v)));
+                const u32x2 x1 = *(const u32x2 *)(row + 2 * ((g0 + 1) ^ wg_swz(v)));
+                const u32x4 w = u32x4{x0[0], x0[1], x1[0], x1[1]};
+                qa[i] = __builtin_bit_cast(bf16x8, w);
+            }
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                pb[j] = *(const bf16x8 *)&Pt[wp * 64 + j * 16 + (lane & 15)][8 * (lane >> 4)];
+            for (int j = 0; j < 4; ++j) {
+                const int v = wp * 64 + j * 16 + (lane & 15);
+                const uint32_t *row = Ps + v * LDW;
+                const u32x2 x0 = *(const u32x2 *)(row + 2 * (g0 ^ wg_swz(v)));
+                const u32x2 x1 = *(const u32x2 *)(row + 2 * ((g0 + 1) ^ wg_swz(v)));
+                const u32x4 w = u32x4{x0[0], x0[1], x1[0], x1[1]};
+                pb[j] = __builtin_bit_cast(bf16x8, w);
+            }
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], pb[j], acc[i][j], 0, 0, 0);
         } else {
+            // 16x16x4 f32: k step g covers rows 4g .. 4g+3 (one group), lane supplies row 4g + (lane>>4)
 #pragma unroll
-            for (int s = 0; s < WG_R / 4; ++s)
+            for (int g = 0; g < WG_R / 4; ++g) {
+                float qa[4], pb[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int v = wq * 64 + i * 16 + (lane & 15);
+                    qa[i] = __uint_as_float(Qs[v * LDW + 4 * (g ^ wg_swz(v)) + (lane >> 4)]);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int v = wp * 64 + j * 16 + (lane & 15);
+                    pb[j] = __uint_as_float(Ps[v * LDW + 4 * (g ^ wg_swz(v)) + (lane >> 4)]);
+                }
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                            (float)Qt[wq * 64 + i * 16 + (lane & 15)][4 * s + (lane >> 4)],
-                            (float)Pt[wp * 64 + j * 16 + (lane & 15)][4 * s + (lane >> 4)], acc[i][j], 0, 0, 0);
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(qa[i], pb[j], acc[i][j], 0, 0, 0);
+            }
         }
+    };
+
+    WgPatch<DT> x;
+    load(0, x);
+    stage(0, x);
+    __syncthreads();
+    for (int it = 0; it < total; ++it) {
+        const bool more = it + 1 < total;
+        if (more) load(it + 1, x);
+        compute(it & 1);
+        if (it % nsteps == nsteps - 1) {
+            store_tile((qt0 + it / nsteps) * WG_T, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+        }
+        if (more) stage((it + 1) & 1, x);
         __syncthreads();
     }
-    // lane: q = q0 + wq*64 + i*16 + 4*(lane>>4) + {0..3}, p = p0 + wp*64 + j*16 + (lane&15)
+}
+
+// ---- bf16 weight gradient through an LDS ring --------------------------------
+// One workgroup per (expert, 128-wide p tile); it walks every 128-wide q tile
+// in 32-row reduction steps.  Four MFMA waves (2 x 2 of 64 x 64) and one
+// producer wave.  The producer copies each step's operand rows into an LDS
+// ring as they lie in memory ([row][value], 256 bytes per 128 values) with
+// direct global->LDS loads, S steps ahead, and waits only for its own loads;
+// the MFMA waves never wait on the vector-memory counter, so their output
+// stores stay in flight while later steps run.  The two roles run separate
+// loops that meet at one barrier per step, which also keeps the compiler from
+// guarding the MFMA waves' LDS reads against loads they never issue.
+//
+// MFMA fragments come from the LDS transpose read: in each group of 16 lanes,
+// lane 4a+b receives value b of the 8-byte pieces addressed by lanes a, 4+a,
+// 8+a and 12+a.  When lane 4j+a of group g addresses row kb + j at values
+// c0 + 4a .. c0 + 4a + 3, lane L of the group receives rows kb .. kb+3 of
+// value c0 + L: two such reads (kb = 8g, 8g + 4) give the eight consecutive
+// rows a 16x16x32 operand lane holds.  The 16-byte chunks of a staged row sit
+// in XOR-permuted slots (wgb_h) so that the 16 rows one read touches spread
+// over all banks.  For a gathered Q operand the row indices of a step travel
+// in the ring S - 1 steps ahead of their step, so the producer reads them from
+// LDS instead of waiting on global memory.
+constexpr int WGB_S = 4;                                  // ring stages
+constexpr int WGB_PB = WG_R * WG_T * 2;                   // one operand's rows of a step (8 KB)
+constexpr int WGB_IDX = 256;                              // gather indices of a later step
+constexpr int WGB_STAGE = 2 * WGB_PB + WGB_IDX;
+constexpr int WGB_LDS = WGB_S * WGB_STAGE;
+constexpr int WGB_NT = 320;
+
+// slot permutation of a staged row's 16 chunks (an even XOR keeps chunk pairs together)
+__device__ __forceinline__ int wgb_h(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
+
+typedef short wgb_v4s __attribute__((ext_vector_type(4)));
+typedef short wgb_v8s __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ wgb_v4s lds_tr16(const char *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) wgb_v4s *)p);
+}
+
+// Eight LDS words read in an asm block that also waits for them (the producer
+// has its ring loads in flight; a compiler-placed wait would cover all of them).
+__device__ __forceinline__ void lds_u32_x8(uint32_t (&v)[8], const uint32_t (&a)[8]) {
+    asm volatile(
+        "ds_read_b32 %0, %8\n"
+        "ds_read_b32 %1, %9\n"
+        "ds_read_b32 %2, %10\n"
+        "ds_read_b32 %3, %11\n"
+        "ds_read_b32 %4, %12\n"
+        "ds_read_b32 %5, %13\n"
+        "ds_read_b32 %6, %14\n"
+        "ds_read_b32 %7, %15\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "memory");
+}
+
+// PASS only separates the down and gate/up instantiations in profiles.
+template <int PASS>
+__global__ __launch_bounds__(WGB_NT) void wgrad_bf16_kernel(const WgradArgs a, int64_t nlead, int64_t ntiles) {
+    extern __shared__ __align__(1024) char wsm[];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const bool producer = wid == 4;
+    const int wp = (wid >> 1) & 1, wq = wid & 1;
+
+    WgTile T;
+    if (!wg_decode(a, nlead, ntiles, blockIdx.x, T)) return;
+    const int pi = T.pi;
+    // the problem's fields, read once (the asm blocks below clobber memory)
+    const WgradProblem &Pr = pi ? a.p[1] : a.p[0];
+    const uint16_t *const Pp = (const uint16_t *)Pr.P, *const Qp = (const uint16_t *)Pr.Q;
+    const int64_t P_ld = Pr.P_ld, Q_ld = Pr.Q_ld;
+    const int32_t *const qg = Pr.q_gather;
+    const bool p_local = Pr.p_local != 0, q_local = Pr.q_local != 0;
+    const int Pdim = Pr.Pdim, Qdim = Pr.Qdim, split = Pr.split;
+    const int e = T.e, p0 = T.p0, qt0 = T.qt0, nq = T.nq;
+    const int64_t rb = Pr.offsets ? (int64_t)Pr.offsets[e] : (int64_t)e * Pr.rows_fixed;
+    const int M = (int)(Pr.offsets ? (int64_t)Pr.offsets[e + 1] - rb : Pr.rows_fixed);
+    const int nsteps = (M + WG_R - 1) / WG_R;
+    const int total = nq * nsteps;
+
+    if (producer) {
+        if (total == 0) return;
+        // instruction n (0..7) of an operand covers rows 4n .. 4n+3 of the step; this lane:
+        // row 4n + lane/16, chunk slot lane%16 holding data chunk (lane%16) ^ h(row)
+        const int drow = lane >> 4, pchunk = lane & 15;
+        int cofs[8];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int p = p0 + wp * 64 + j * 16 + (lane & 15);
-        void *out = p < P.split ? P.out0 : P.out1;
-        const int prow = p < P.split ? p : p - P.split;
-        const int64_t base = ((int64_t)e * (P.split < P.Pdim ? P.split : P.Pdim) + prow) * P.Qdim;
+        for (int n = 0; n < 8; ++n) cofs[n] = 8 * (pchunk ^ wgb_h(4 * n + drow));
+        const bool gather = qg != nullptr;
+        const int32_t *const qgb = gather ? qg + rb : nullptr;
+        auto nops = [&](int y) { return 16 + ((gather && y + WGB_S - 1 < total) ? 1 : 0); };
+        // step y into ring slot y % S; qrow: gathered Q rows of this lane's 8 rows (if gather)
+        int yq = 0, ys = 0;   // q tile and step of the next step to issue
+        auto issue = [&](int y, const int (&qrow)[8]) {
+            char *slot = wsm + (y % WGB_S) * WGB_STAGE;
+            const int q0 = (qt0 + yq) * WG_T, r0 = ys * WG_R;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = q0 + wq * 64 + i * 16 + 4 * (lane >> 4);
-            if (DT == DT_BF16) {
-                *(u32x2 *)((uint16_t *)out + base + q) =
-                    u32x2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
-            } else {
-                *(f32x4 *)((float *)out + base + q) = acc[i][j];
+            for (int n = 0; n < 8; ++n) {
+                const int r = min(r0 + 4 * n + drow, M - 1);   // rows past the expert repeat its last (masked)
+                const int64_t prow = p_local ? r : rb + r;
+                dma16(Pp + prow * P_ld + p0 + cofs[n], slot + n * 1024);
+                const int64_t qr = gather ? (int64_t)qrow[n] : (q_local ? (int64_t)r : rb + r);
+                dma16(Qp + qr * Q_ld + q0 + cofs[n], slot + WGB_PB + n * 1024);
             }
+            if (gather && y + WGB_S - 1 < total) {
+                // row indices of step y + S - 1 ride along (64 words, the first 32 used)
+                const int ys2 = (ys + WGB_S - 1) % nsteps;
+                dma4(qgb + min(ys2 * WG_R + (lane & 31), M - 1), slot + 2 * WGB_PB);
+            }
+            if (++ys == nsteps) { ys = 0; ++yq; }
+        };
+        int qrow[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int y = 0; y < WGB_S - 1 && y < total; ++y) {
+            if (gather)
+#pragma unroll
+                for (int n = 0; n < 8; ++n) qrow[n] = qgb[min(ys * WG_R + 4 * n + drow, M - 1)];
+            issue(y, qrow);
+        }
+        for (int x = 0; x < total; ++x) {
+            // step x has landed once at most the later steps' loads are outstanding
+            int after = 0;
+            for (int y = x + 1; y <= min(x + WGB_S - 2, total - 1); ++y) after += nops(y);
+            wait_vmcnt_dyn(after);
+            cta_barrier();                       // step x landed; every MFMA wave is done with slot (x - 1) % S
+            const int y = x + WGB_S - 1;
+            if (y < total) {
+                if (gather) {
+                    const uint32_t ib = (uint32_t)(uintptr_t)(wsm + (x % WGB_S) * WGB_STAGE + 2 * WGB_PB);
+                    uint32_t ad[8], v[8];
+#pragma unroll
+                    for (int n = 0; n < 8; ++n) ad[n] = ib + 4 * (4 * n + drow);
+                    lds_u32_x8(v, ad);
+#pragma unroll
+                    for (int n = 0; n < 8; ++n) qrow[n] = (int)v[n];
+                }
+                issue(y, qrow);
+            }
+        }
+        return;
+    }
+
+    // ---- MFMA waves ----
+    const int split_rows = split < Pdim ? split : Pdim;   // a p tile lies on one side of the split
+    uint16_t *const out = (uint16_t *)(p0 < split ? Pr.out0 : Pr.out1);
+    const int prow0 = p0 < split ? p0 : p0 - split;
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    // output rows of this lane: p = p0 + wp*64 + j*16 + (lane&15); columns q = q0 + wq*64 + i*16 + 4*(lane>>4)
+    auto store_tile = [&](int q0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int prow = prow0 + wp * 64 + j * 16 + (lane & 15);
+            uint16_t *orow = out + ((int64_t)e * split_rows + prow) * Qdim + q0 + wq * 64 + 4 * (lane >> 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *(u32x2 *)(orow + i * 16) =
+                    u32x2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+        }
+    };
+    if (total == 0) {   // an expert without rows: its gradient is zero
+        for (int q = 0; q < nq; ++q) store_tile((qt0 + q) * WG_T);
+        return;
+    }
+    // per-lane byte offsets (in a stage) of the fragment reads: rows 8g + jj and 8g + 4 + jj
+    // of values col0 + 4aa .. +3, for the 4 Q and 4 P fragments of this wave
+    const int g = lane >> 4, jj = (lane >> 2) & 3, aa = lane & 3;
+    int ofs[16];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        const int col0 = f < 4 ? wq * 64 + f * 16 : wp * 64 + (f - 4) * 16;
+        const int c = (col0 + 4 * aa) >> 3, off = 8 * (aa & 1);
+        const int k0 = 8 * g + jj, k1 = k0 + 4;
+        const int base = f < 4 ? WGB_PB : 0;
+        ofs[2 * f] = base + k0 * 256 + ((c ^ wgb_h(k0)) << 4) + off;
+        ofs[2 * f + 1] = base + k1 * 256 + ((c ^ wgb_h(k1)) << 4) + off;
+    }
+    const int vlast = M - (nsteps - 1) * WG_R;   // valid rows of an expert's last step
+    int qt = 0, st = 0, slot = 0;
+    for (int x = 0; x < total; ++x) {
+        cta_barrier();                           // step x has landed
+        const char *sb = wsm + slot * WGB_STAGE;
+        wgb_v4s r[16];
+#pragma unroll
+        for (int f = 0; f < 16; ++f) r[f] = lds_tr16(sb + ofs[f]);
+        bf16x8 qa[4], pb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            qa[i] = __builtin_bit_cast(bf16x8, (wgb_v8s)__builtin_shufflevector(r[2 * i], r[2 * i + 1], 0, 1, 2, 3,
+                                                                                 4, 5, 6, 7));
+        const bool ragged = st == nsteps - 1 && vlast < WG_R;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            wgb_v8s v = __builtin_shufflevector(r[8 + 2 * j], r[8 + 2 * j + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+            if (ragged) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    if (8 * g + q >= vlast) v[q] = 0;
+            }
+            pb[j] = __builtin_bit_cast(bf16x8, v);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], pb[j], acc[i][j], 0, 0, 0);
+        slot = slot + 1 == WGB_S ? 0 : slot + 1;
+        if (++st == nsteps) {
+            store_tile((qt0 + qt) * WG_T);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+            st = 0;
+            ++qt;
         }
     }
 }
@@ -361,14 +729,31 @@ hipError_t launch_dgate(int dt, const void *u, const int32_t *perm, const int32_
     return hipGetLastError();
 }
 
-hipError_t launch_wgrad(int dt, const WgradArgs &a, hipStream_t s) {
+hipError_t launch_wgrad(int dt, int pass, const WgradArgs &a, hipStream_t s) {
     int64_t tiles = 0;
-    for (int i = 0; i < a.nprob; ++i)
-        tiles += (int64_t)a.p[i].n_exp * (a.p[i].Pdim / WG_T) * (a.p[i].Qdim / WG_T);
+    for (int i = 0; i < a.nprob; ++i) tiles += wg_tiles(a.p[i]);
     if (tiles <= 0) return hipSuccess;
-    if (tiles >= (1ll << 31)) return hipErrorInvalidValue;
-    if (dt == DT_F32) wgrad_kernel<DT_F32><<<(unsigned)tiles, BW_NT, 0, s>>>(a);
-    else wgrad_kernel<DT_BF16><<<(unsigned)tiles, BW_NT, 0, s>>>(a);
+    // a leading fixed-rows problem is spread over all XCDs (see wg_decode)
+    const int64_t nlead = (a.nprob > 1 && !a.p[0].offsets) ? wg_tiles(a.p[0]) : 0;
+    const int64_t grid = (nlead + 7) / 8 * 8 + (tiles - nlead + 7) / 8 * 8;
+    if (grid >= (1ll << 31)) return hipErrorInvalidValue;
+    if (dt == DT_F32) {
+        if (pass) wgrad_kernel<DT_F32, 1><<<(unsigned)grid, BW_NT, 0, s>>>(a, nlead, tiles);
+        else wgrad_kernel<DT_F32, 0><<<(unsigned)grid, BW_NT, 0, s>>>(a, nlead, tiles);
+    } else {
+        static std::once_flag once;
+        static hipError_t attr = hipSuccess;
+        std::call_once(once, [] {
+            attr = hipFuncSetAttribute((const void *)wgrad_bf16_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       WGB_LDS);
+            if (attr == hipSuccess)
+                attr = hipFuncSetAttribute((const void *)wgrad_bf16_kernel<1>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, WGB_LDS);
+        });
+        if (attr != hipSuccess) return attr;
+        if (pass) wgrad_bf16_kernel<1><<<(unsigned)grid, WGB_NT, WGB_LDS, s>>>(a, nlead, tiles);
+        else wgrad_bf16_kernel<0><<<(unsigned)grid, WGB_NT, WGB_LDS, s>>>(a, nlead, tiles);
+    }
     return hipGetLastError();
 }
 

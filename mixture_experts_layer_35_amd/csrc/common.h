@@ -25,8 +25,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return (uint16_t)(u >> 16);
 }
 
+// Two fp32 -> packed bf16 pair (lo in bits 0-15), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950 (same result as f32_to_bf16 for finite inputs).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
 }
 
 // Four fp32 values (already in [-448, 448]) -> four E4M3FN codes, nearest even.

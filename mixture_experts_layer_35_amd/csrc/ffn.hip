@@ -193,7 +193,7 @@ __device__ __forceinline__ void store_pair_bf16(uint16_t *row, int f_block, cons
 
 template <int DT, int MODE>
 __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_bytes) {
-    constexpr bool GATEUP = MODE != FFN_DOWN;           // two weight matrices, SwiGLU epilogue
+    constexpr bool GATEUP = MODE == FFN_GATEUP || MODE == FFN_GATEUP_BWD;   // two weight matrices, SwiGLU epilogue
     constexpr bool SWBWD = MODE == FFN_GATEUP_BWD;      // epilogue: SwiGLU gradient from dH
     constexpr int esz = FTraits<DT>::esz;
     constexpr int CB = Frag<DT>::CB;              // staged bytes per row per reduction step
@@ -611,10 +611,12 @@ hipError_t run(const FfnArgs &a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_ffn(int dt, int mode, const FfnArgs &a, hipStream_t s) {
-    if (mode == FFN_GATEUP_BWD) {
-        if (dt == DT_F32) return run<DT_F32, FFN_GATEUP_BWD>(a, s);
-        if (dt == DT_BF16) return run<DT_BF16, FFN_GATEUP_BWD>(a, s);
-        return hipErrorInvalidValue;
+    if (mode == FFN_GATEUP_BWD || mode == FFN_BWD_DH || mode == FFN_BWD_DX) {
+        if (dt == DT_E4M3) return hipErrorInvalidValue;
+        const bool f32 = dt == DT_F32;
+        if (mode == FFN_GATEUP_BWD) return f32 ? run<DT_F32, FFN_GATEUP_BWD>(a, s) : run<DT_BF16, FFN_GATEUP_BWD>(a, s);
+        if (mode == FFN_BWD_DH) return f32 ? run<DT_F32, FFN_BWD_DH>(a, s) : run<DT_BF16, FFN_BWD_DH>(a, s);
+        return f32 ? run<DT_F32, FFN_BWD_DX>(a, s) : run<DT_BF16, FFN_BWD_DX>(a, s);
     }
     const bool gateup = mode == FFN_GATEUP;
     if (dt == DT_F32) return gateup ? run<DT_F32, FFN_GATEUP>(a, s) : run<DT_F32, FFN_DOWN>(a, s);

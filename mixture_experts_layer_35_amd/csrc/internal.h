@@ -69,7 +69,9 @@ constexpr int kMaxExperts = 1024;
 // mode: FFN_DOWN (out = x . w^T), FFN_GATEUP (out = SiLU(x . w0^T) * (x . w1^T)),
 // FFN_GATEUP_BWD (a = x . w0^T, b = x . w1^T recomputed; with dh read from P.dh,
 // out[:, 0:F] = dh * b * SiLU'(a) and out[:, F:2F] = dh * SiLU(a); out_ld = 2F).
-enum { FFN_DOWN = 0, FFN_GATEUP = 1, FFN_GATEUP_BWD = 2 };
+// FFN_BWD_DH / FFN_BWD_DX: the plain product of FFN_DOWN for the backward's dH = dY W_down and
+// dX = [dA | dB] [W_gate ; W_up] passes, instantiated apart so that profiles tell the passes apart.
+enum { FFN_DOWN = 0, FFN_GATEUP = 1, FFN_GATEUP_BWD = 2, FFN_BWD_DH = 3, FFN_BWD_DX = 4 };
 hipError_t launch_ffn(int dt, int mode, const FfnArgs &a, hipStream_t s);
 
 // ---- backward ----------------------------------------------------------------
@@ -90,6 +92,7 @@ struct WgradProblem {
     int p_local, q_local;   // row r of the expert reads P / Q row r (not base + r): an input shared by experts
     int Pdim, Qdim, split;
     void *out0, *out1;
+    int64_t rows_hint;      // typical rows per expert (sizes the work per workgroup)
 };
 struct WgradArgs {
     WgradProblem p[2];
@@ -104,7 +107,8 @@ hipError_t launch_bwd_token(int dt, const void *dxr, const void *dxs, int Ns, co
                             float rs, void *du, float *dz_row, hipStream_t s);
 hipError_t launch_dgate(int dt, const void *u, const int32_t *perm, const int32_t *offsets, const float *dz_row, int Nr,
                         int d, float *dgate, hipStream_t s);
-hipError_t launch_wgrad(int dt, const WgradArgs &a, hipStream_t s);
+// pass: 0 for dW_down, 1 for dW_gate / dW_up (separate instantiations, same code)
+hipError_t launch_wgrad(int dt, int pass, const WgradArgs &a, hipStream_t s);
 
 // ---- combine / bias ----------------------------------------------------------
 hipError_t launch_combine(int dt_out, int dt_res, const void *y_perm, const int32_t *inv_perm, const float *topk_w,

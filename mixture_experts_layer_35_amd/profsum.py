@@ -25,9 +25,12 @@ COPY_BYTES = 1 << 30
 def short_name(full: str) -> str:
     """Readable kernel name: the expert kernels by their projection, others
     by their function name."""
-    m = re.search(r"ffn_kernel<(\d+), (true|false)", full)
+    m = re.search(r"ffn_kernel<(\d+), (\d+)>", full)
     if m:
-        return "ffn_gate_up" if m.group(2) == "true" else "ffn_down"
+        return {0: "ffn_down", 1: "ffn_gate_up", 2: "bwd_swiglu", 3: "bwd_dh", 4: "bwd_dx"}[int(m.group(2))]
+    m = re.search(r"wgrad_kernel<(\d+), (\d+)>", full)
+    if m:
+        return "wgrad_gate_up" if m.group(2) == "1" else "wgrad_down"
     if "copyBuffer" in full:
         return "copy_buffer"
     head = full.replace("(anonymous namespace)", "").split("(")[0]
