@@ -462,10 +462,10 @@ __global__ __launch_bounds__(BW_NT) void wgrad_kernel(const WgradArgs a, int64_t
 
 // ---- bf16 weight gradient through an LDS ring --------------------------------
 // One workgroup per (expert, 128-wide p tile); it walks every 128-wide q tile
-// in 32-row reduction steps.  Four MFMA waves (2 x 2 of 64 x 64) and one
-// producer wave.  The producer copies each step's operand rows into an LDS
+// in 32-row reduction steps.  Four MFMA waves (2 x 2 of 64 x 64) and two
+// producer waves.  The producers copy each step's operand rows into an LDS
 // ring as they lie in memory ([row][value], 256 bytes per 128 values) with
-// direct global->LDS loads, S steps ahead, and waits only for its own loads;
+// direct global->LDS loads, S steps ahead, and each waits only for its own loads;
 // the MFMA waves never wait on the vector-memory counter, so their output
 // stores stay in flight while later steps run.  The two roles run separate
 // loops that meet at one barrier per step, which also keeps the compiler from
@@ -486,7 +486,7 @@ constexpr int WGB_PB = WG_R * WG_T * 2;                   // one operand's rows 
 constexpr int WGB_IDX = 256;                              // gather indices of a later step
 constexpr int WGB_STAGE = 2 * WGB_PB + WGB_IDX;
 constexpr int WGB_LDS = WGB_S * WGB_STAGE;
-constexpr int WGB_NT = 320;
+constexpr int WGB_NT = 384;
 
 // slot permutation of a staged row's 16 chunks (an even XOR keeps chunk pairs together)
 __device__ __forceinline__ int wgb_h(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
@@ -498,21 +498,16 @@ __device__ __forceinline__ wgb_v4s lds_tr16(const char *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) wgb_v4s *)p);
 }
 
-// Eight LDS words read in an asm block that also waits for them (the producer
-// has its ring loads in flight; a compiler-placed wait would cover all of them).
-__device__ __forceinline__ void lds_u32_x8(uint32_t (&v)[8], const uint32_t (&a)[8]) {
+// Four LDS words read in an asm block that also waits for them.
+__device__ __forceinline__ void lds_u32_x4(uint32_t (&v)[4], uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3) {
     asm volatile(
-        "ds_read_b32 %0, %8\n"
-        "ds_read_b32 %1, %9\n"
-        "ds_read_b32 %2, %10\n"
-        "ds_read_b32 %3, %11\n"
-        "ds_read_b32 %4, %12\n"
-        "ds_read_b32 %5, %13\n"
-        "ds_read_b32 %6, %14\n"
-        "ds_read_b32 %7, %15\n"
+        "ds_read_b32 %0, %4\n"
+        "ds_read_b32 %1, %5\n"
+        "ds_read_b32 %2, %6\n"
+        "ds_read_b32 %3, %7\n"
         "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
-        : "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3]), "v"(a[4]), "v"(a[5]), "v"(a[6]), "v"(a[7])
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
         : "memory");
 }
 
@@ -521,7 +516,7 @@ template <int PASS>
 __global__ __launch_bounds__(WGB_NT) void wgrad_bf16_kernel(const WgradArgs a, int64_t nlead, int64_t ntiles) {
     extern __shared__ __align__(1024) char wsm[];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const bool producer = wid == 4;
+    const bool producer = wid >= 4;
     const int wp = (wid >> 1) & 1, wq = wid & 1;
 
     WgTile T;
@@ -542,40 +537,54 @@ __global__ __launch_bounds__(WGB_NT) void wgrad_bf16_kernel(const WgradArgs a, i
 
     if (producer) {
         if (total == 0) return;
-        // instruction n (0..7) of an operand covers rows 4n .. 4n+3 of the step; this lane:
-        // row 4n + lane/16, chunk slot lane%16 holding data chunk (lane%16) ^ h(row)
-        const int drow = lane >> 4, pchunk = lane & 15;
-        int cofs[8];
-#pragma unroll
-        for (int n = 0; n < 8; ++n) cofs[n] = 8 * (pchunk ^ wgb_h(4 * n + drow));
+        // instruction n (0..7) of an operand covers rows 4n .. 4n+3 of the step; producer k issues
+        // n = 2m + k.  This lane: row 4n + lane/16, chunk slot lane%16 holding data chunk
+        // (lane%16) ^ h(row).  Row pointers are formed once and advanced by a uniform offset per step.
+        const int k = wid - 4, drow = lane >> 4, pchunk = lane & 15;
         const bool gather = qg != nullptr;
         const int32_t *const qgb = gather ? qg + rb : nullptr;
-        auto nops = [&](int y) { return 16 + ((gather && y + WGB_S - 1 < total) ? 1 : 0); };
-        // step y into ring slot y % S; qrow: gathered Q rows of this lane's 8 rows (if gather)
+        const int64_t prb = p_local ? 0 : rb, qrb = q_local ? 0 : rb;
+        int cofs[4];
+        const uint16_t *pbase[4], *qbase[4], *plast[4], *qlast[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int n = 2 * m + k, kr = 4 * n + drow;
+            cofs[m] = 8 * (pchunk ^ wgb_h(kr));
+            pbase[m] = Pp + (prb + kr) * P_ld + p0 + cofs[m];
+            qbase[m] = Qp + (qrb + kr) * Q_ld + cofs[m];
+            plast[m] = Pp + (prb + M - 1) * P_ld + p0 + cofs[m];   // rows past the expert repeat its last
+            qlast[m] = Qp + (qrb + M - 1) * Q_ld + cofs[m];
+        }
+        auto nops = [&](int y) { return 8 + ((k == 0 && gather && y + WGB_S - 1 < total) ? 1 : 0); };
         int yq = 0, ys = 0;   // q tile and step of the next step to issue
-        auto issue = [&](int y, const int (&qrow)[8]) {
+        // step y into ring slot y % S; qrow: gathered Q rows of this lane's 4 rows (if gather)
+        auto issue = [&](int y, const int (&qrow)[4]) {
             char *slot = wsm + (y % WGB_S) * WGB_STAGE;
             const int q0 = (qt0 + yq) * WG_T, r0 = ys * WG_R;
+            const bool ragged = r0 + WG_R > M;
+            const int64_t po = (int64_t)r0 * P_ld, qo = (int64_t)r0 * Q_ld + q0;
 #pragma unroll
-            for (int n = 0; n < 8; ++n) {
-                const int r = min(r0 + 4 * n + drow, M - 1);   // rows past the expert repeat its last (masked)
-                const int64_t prow = p_local ? r : rb + r;
-                dma16(Pp + prow * P_ld + p0 + cofs[n], slot + n * 1024);
-                const int64_t qr = gather ? (int64_t)qrow[n] : (q_local ? (int64_t)r : rb + r);
-                dma16(Qp + qr * Q_ld + q0 + cofs[n], slot + WGB_PB + n * 1024);
+            for (int m = 0; m < 4; ++m) {
+                const int n = 2 * m + k;
+                const bool past = ragged && r0 + 4 * n + drow >= M;
+                dma16(past ? plast[m] : pbase[m] + po, slot + n * 1024);
+                const uint16_t *qs;
+                if (gather) qs = Qp + (int64_t)qrow[m] * Q_ld + q0 + cofs[m];
+                else qs = past ? qlast[m] + q0 : qbase[m] + qo;
+                dma16(qs, slot + WGB_PB + n * 1024);
             }
-            if (gather && y + WGB_S - 1 < total) {
+            if (k == 0 && gather && y + WGB_S - 1 < total) {
                 // row indices of step y + S - 1 ride along (64 words, the first 32 used)
                 const int ys2 = (ys + WGB_S - 1) % nsteps;
                 dma4(qgb + min(ys2 * WG_R + (lane & 31), M - 1), slot + 2 * WGB_PB);
             }
             if (++ys == nsteps) { ys = 0; ++yq; }
         };
-        int qrow[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        int qrow[4] = {0, 0, 0, 0};
         for (int y = 0; y < WGB_S - 1 && y < total; ++y) {
             if (gather)
 #pragma unroll
-                for (int n = 0; n < 8; ++n) qrow[n] = qgb[min(ys * WG_R + 4 * n + drow, M - 1)];
+                for (int m = 0; m < 4; ++m) qrow[m] = qgb[min(ys * WG_R + 4 * (2 * m + k) + drow, M - 1)];
             issue(y, qrow);
         }
         for (int x = 0; x < total; ++x) {
@@ -588,12 +597,11 @@ __global__ __launch_bounds__(WGB_NT) void wgrad_bf16_kernel(const WgradArgs a, i
             if (y < total) {
                 if (gather) {
                     const uint32_t ib = (uint32_t)(uintptr_t)(wsm + (x % WGB_S) * WGB_STAGE + 2 * WGB_PB);
-                    uint32_t ad[8], v[8];
+                    uint32_t v[4];
+                    lds_u32_x4(v, ib + 4 * (4 * k + drow), ib + 4 * (4 * (2 + k) + drow), ib + 4 * (4 * (4 + k) + drow),
+                               ib + 4 * (4 * (6 + k) + drow));
 #pragma unroll
-                    for (int n = 0; n < 8; ++n) ad[n] = ib + 4 * (4 * n + drow);
-                    lds_u32_x8(v, ad);
-#pragma unroll
-                    for (int n = 0; n < 8; ++n) qrow[n] = (int)v[n];
+                    for (int m = 0; m < 4; ++m) qrow[m] = (int)v[m];
                 }
                 issue(y, qrow);
             }
@@ -611,15 +619,18 @@ __global__ __launch_bounds__(WGB_NT) void wgrad_bf16_kernel(const WgradArgs a, i
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
     // output rows of this lane: p = p0 + wp*64 + j*16 + (lane&15); columns q = q0 + wq*64 + i*16 + 4*(lane>>4)
+    // (pairs of 16-column blocks leave as one 16-byte store per lane: 128 bytes of a row per 8 lanes)
     auto store_tile = [&](int q0) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int prow = prow0 + wp * 64 + j * 16 + (lane & 15);
-            uint16_t *orow = out + ((int64_t)e * split_rows + prow) * Qdim + q0 + wq * 64 + 4 * (lane >> 4);
+            uint16_t *orow = out + ((int64_t)e * split_rows + prow) * Qdim;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                *(u32x2 *)(orow + i * 16) =
-                    u32x2{pack_bf16x2(acc[i][j][0], acc[i][j][1]), pack_bf16x2(acc[i][j][2], acc[i][j][3])};
+            for (int i = 0; i < 4; i += 2) {
+                const float ya[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                const float yb[4] = {acc[i + 1][j][0], acc[i + 1][j][1], acc[i + 1][j][2], acc[i + 1][j][3]};
+                store_pair_bf16(orow, q0 + wq * 64 + i * 16, ya, yb, lane, Qdim);
+            }
         }
     };
     if (total == 0) {   // an expert without rows: its gradient is zero

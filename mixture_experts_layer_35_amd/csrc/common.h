@@ -33,6 +33,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){lo, hi}, b2));
 }
 
+// Stores two adjacent 16-feature blocks of one token's bf16 results (block i
+// from a[], block i+1 from b[]; lane group g = lane/16 holds features 4g..4g+3
+// of each) with one 16-byte store per lane: lanes of even groups keep block i
+// and take their partner's (lane ^ 16) four block-i values, odd groups do the
+// same for block i+1.  A token's 32 features then leave as two 32-byte runs
+// instead of four 16-byte ones.  Both partners hold the same token, so they are
+// active together.
+__device__ __forceinline__ void store_pair_bf16(uint16_t *row, int f_block, const float a[4], const float b[4],
+                                                int lane, int F) {
+    const bool odd = (lane >> 4) & 1;
+    const uint32_t a01 = pack_bf16x2(a[0], a[1]), a23 = pack_bf16x2(a[2], a[3]);
+    const uint32_t b01 = pack_bf16x2(b[0], b[1]), b23 = pack_bf16x2(b[2], b[3]);
+    const uint32_t r0 = __shfl_xor(odd ? a01 : b01, 16, 64), r1 = __shfl_xor(odd ? a23 : b23, 16, 64);
+    const int f = f_block + (odd ? 16 : 0) + 4 * ((lane >> 4) & ~1);
+    if (f < F) *(u32x4 *)(row + f) = odd ? u32x4{r0, r1, b01, b23} : u32x4{a01, a23, r0, r1};
+}
+
 // Four fp32 values (already in [-448, 448]) -> four E4M3FN codes, nearest even.
 __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
     uint32_t v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
