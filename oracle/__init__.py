@@ -89,6 +89,11 @@ def _load():
             lib.oracle_moe_backward_f64.restype = i32
             lib.oracle_moe_backward_f64.argtypes = ([i64, i32, i32, i32, i32, i32, i32, P, P, P, i32] + [P] * 6
                                                     + [f64, P, i64, P, i32, P] + [P] * 9)
+            lib.oracle_quant_128x1.restype = None
+            lib.oracle_quant_128x1.argtypes = [i32, P, i32, i32, P, P, P, P, P]
+            lib.oracle_moe_backward_fp8.restype = i32
+            lib.oracle_moe_backward_fp8.argtypes = ([i64, i32, i32, i32, i32, i32, P, P, P] + [P] * 12
+                                                    + [f64, P, i64, P, i32, P] + [P] * 9)
             lib.oracle_seq_balance.restype = None
             lib.oracle_seq_balance.argtypes = [i64, i32, i32, P, P, i64, f32, P, P, P]
             lib.oracle_num_threads.restype = i32
@@ -407,6 +412,73 @@ def moe_backward(u, gate_w, topk_idx, routed, shared, dout, tokens=None, experts
                                          _p(r["dwd"]), _p(r["dswg"]), _p(r["dswu"]), _p(r["dswd"]))
     if rc:
         raise ValueError("oracle_moe_backward_f64 rc=%d" % rc)
+    return r
+
+
+def quant_128x1(x, offsets, x_scales=None, gather=None):
+    """128 x 1 tiles along the rows of segments (the backward's weight-gradient
+    operands; reading in moe_oracle.c).  x: [n, cols] float32, bf16 bits, or
+    e4m3 codes (uint8) with 1 x 128 scales x_scales [n, cols/128]; offsets
+    [n_seg + 1] int32 over the list rows; gather [rows] int32 or None.
+    Returns (codes uint8 [rows, cols], scales float32 [n_blocks, cols]) with
+    n_blocks = sum over segments of ceil(len / 128)."""
+    offsets = _c(offsets, np.int32)
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.uint8:
+        code, xs = E4M3, _c(x_scales, np.float32)
+    else:
+        code, x = _storage(x)
+        xs = None
+    cols = x.shape[1]
+    assert cols % NC == 0
+    g = None if gather is None else _c(gather, np.int32)
+    rows = int(offsets[-1])
+    lens = np.diff(offsets.astype(np.int64))
+    nblk = int(((lens + NC - 1) // NC).sum())
+    q = np.empty((rows, cols), np.uint8)
+    s = np.empty((max(nblk, 1), cols), np.float32)
+    _load().oracle_quant_128x1(len(offsets) - 1, _p(offsets), cols, code, _p(x), _p(xs), _p(g), _p(q), _p(s))
+    return q, s[:nblk]
+
+
+def moe_backward_fp8(u, gate_w, topk_idx, routed_q, routed_s, shared_q, shared_s, dout, tokens=None, experts=None,
+                     dgate=True, dshared=True, routed_scale=1.0):
+    """Gradient of the FP8 layer (bf16 activations, e4m3 expert GEMMs with
+    128 x 128 weight blocks) for a fixed selection, with the Dgrad and Wgrad
+    GEMMs on FP8 operands (readings in moe_oracle.c).  u, gate_w: bf16 bits;
+    routed_q / shared_q: e4m3 codes (gate, up, down) with block scales
+    routed_s / shared_s; dout: float values of the bf16 upstream gradient.
+    Returns the dict of moe_backward."""
+    u = _c(u, np.uint16)
+    gate_w = _c(gate_w, np.uint16)
+    idx = _c(topk_idx, np.int32)
+    T, d = u.shape
+    Nr = gate_w.shape[0]
+    K = idx.shape[1]
+    I = routed_q[0].shape[1]
+    Ns = shared_q[0].shape[0] if shared_q is not None else 0
+    rq = [_c(a, np.uint8) for a in routed_q]
+    rsc = [_c(a, np.float32) for a in routed_s]
+    sq = [_c(a, np.uint8) for a in shared_q] if Ns else [None] * 3
+    ssc = [_c(a, np.float32) for a in shared_s] if Ns else [None] * 3
+    dout = _c(dout, np.float64)
+    tok = None if tokens is None else _c(tokens, np.int64)
+    exps = None if experts is None else _c(experts, np.int32)
+    ne = Nr if exps is None else exps.shape[0]
+    r = dict(du=np.zeros((T, d)), dg=np.zeros((T, K)),
+             dgate_w=np.empty((Nr, d)) if dgate else None,
+             dwg=np.empty((ne, I, d)), dwu=np.empty((ne, I, d)), dwd=np.empty((ne, d, I)),
+             dswg=np.empty((Ns, I, d)) if dshared and Ns else None,
+             dswu=np.empty((Ns, I, d)) if dshared and Ns else None,
+             dswd=np.empty((Ns, d, I)) if dshared and Ns else None)
+    rc = _load().oracle_moe_backward_fp8(T, d, Nr, Ns, K, I, _p(u), _p(gate_w), _p(idx), *[_p(a) for a in rq],
+                                         *[_p(a) for a in rsc], *[_p(a) for a in sq], *[_p(a) for a in ssc],
+                                         routed_scale, _p(dout), 0 if tok is None else tok.shape[0], _p(tok),
+                                         0 if exps is None else exps.shape[0], _p(exps), _p(r["du"]), _p(r["dg"]),
+                                         _p(r["dgate_w"]), _p(r["dwg"]), _p(r["dwu"]), _p(r["dwd"]), _p(r["dswg"]),
+                                         _p(r["dswu"]), _p(r["dswd"]))
+    if rc:
+        raise ValueError("oracle_moe_backward_fp8 rc=%d" % rc)
     return r
 
 

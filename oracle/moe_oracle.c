@@ -917,6 +917,345 @@ int oracle_moe_backward_f64(int64_t T, int d, int Nr, int Ns, int K, int I, int 
     return 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* FP8 backward (§3.3: Fprop, Dgrad and Wgrad GEMMs in FP8)                  */
+/* ------------------------------------------------------------------------ */
+
+/* Quantise v[n] (as fp32 values) in 1 x 128 tiles and replace it by the
+ * dequantised values. */
+static void q1x128_inplace(int n, double *v)
+{
+    for (int b = 0; b < n / OR_NC; ++b) {
+        float amax = 0.0f;
+        for (int k = b * OR_NC; k < (b + 1) * OR_NC; ++k) {
+            float a = fabsf((float)v[k]);
+            if (a > amax) amax = a;
+        }
+        const float sc = quant_scale(amax);
+        for (int k = b * OR_NC; k < (b + 1) * OR_NC; ++k)
+            v[k] = e4m3_table[quant_one((float)v[k], sc)] * (double)sc;
+    }
+}
+
+/* Rows v[nr][n] (row stride n) quantised in 128 x 1 tiles: column c of the
+ * rows [128 j, 128 j + 128) of the list shares one scale (the last tile may
+ * be shorter); replaced by the dequantised values. */
+static void q128x1_inplace(int64_t nr, int n, double *v, size_t stride)
+{
+    for (int64_t r0 = 0; r0 < nr; r0 += OR_NC) {
+        const int64_t r1 = r0 + OR_NC < nr ? r0 + OR_NC : nr;
+        for (int c = 0; c < n; ++c) {
+            float amax = 0.0f;
+            for (int64_t r = r0; r < r1; ++r) {
+                float a = fabsf((float)v[r * stride + c]);
+                if (a > amax) amax = a;
+            }
+            const float sc = quant_scale(amax);
+            for (int64_t r = r0; r < r1; ++r)
+                v[r * stride + c] = e4m3_table[quant_one((float)v[r * stride + c], sc)] * (double)sc;
+        }
+    }
+}
+
+/*
+ * 128 x 1 tiles along the rows of segments (the backward's Wgrad operands):
+ * segment e owns list rows off[e] .. off[e+1]; its rows are taken in runs of
+ * 128 from the segment's first row (the last run may be shorter), and column
+ * c of a run shares one scale.  List row r reads row (gather ? gather[r] : r)
+ * of x [*][cols], stored in in_dtype: OR_F32, OR_BF16, or OR_E4M3 with 1 x 128
+ * tile scales x_s[*][cols/128] (dequantised to fp32 first).  Outputs: codes
+ * q[rows][cols] and scales s[nblk][cols], where run j of segment e is block
+ * sum_{e' < e} ceil(len(e') / 128) + j.
+ */
+void oracle_quant_128x1(int n_seg, const int32_t *off, int cols, int in_dtype, const void *x, const float *x_s,
+                        const int32_t *gather, uint8_t *q, float *s)
+{
+    init_tables();
+    int64_t bbase = 0;
+    for (int e = 0; e < n_seg; ++e) {
+        const int64_t r0 = off[e], len = (int64_t)off[e + 1] - off[e];
+        const int64_t nb = (len + OR_NC - 1) / OR_NC;
+#pragma omp parallel for schedule(static)
+        for (int c = 0; c < cols; ++c) {
+            for (int64_t j = 0; j < nb; ++j) {
+                const int64_t a = r0 + j * OR_NC, b = a + OR_NC < r0 + len ? a + OR_NC : r0 + len;
+                float amax = 0.0f;
+                for (int64_t r = a; r < b; ++r) {
+                    const int64_t xr = gather ? gather[r] : r;
+                    float v = in_dtype == OR_E4M3 ? (float)(e4m3_table[((const uint8_t *)x)[xr * cols + c]] *
+                                                          (double)x_s[xr * (cols / OR_NC) + c / OR_NC])
+                                                  : (float)load_plain(in_dtype, x, xr * cols + c);
+                    if (fabsf(v) > amax) amax = fabsf(v);
+                }
+                const float sc = quant_scale(amax);
+                s[(bbase + j) * cols + c] = sc;
+                for (int64_t r = a; r < b; ++r) {
+                    const int64_t xr = gather ? gather[r] : r;
+                    float v = in_dtype == OR_E4M3 ? (float)(e4m3_table[((const uint8_t *)x)[xr * cols + c]] *
+                                                          (double)x_s[xr * (cols / OR_NC) + c / OR_NC])
+                                                  : (float)load_plain(in_dtype, x, xr * cols + c);
+                    q[r * cols + c] = quant_one(v, sc);
+                }
+            }
+        }
+        bbase += nb;
+    }
+}
+
+/*
+ * One (token, expert) pair of the FP8 layer (bf16 activations, e4m3 expert
+ * GEMMs) and the input-gradient chain through it, each GEMM on FP8 operands:
+ *   forward (as moe_forward computes it): a, b from the token's 1 x 128 tiles x
+ *     and the 128 x 128 weight blocks; h = SiLU(a) b, cached as 1 x 128 tiles
+ *     (hq, dequantised); y = W_down hq, stored in bf16;
+ *   dy = bf16(g dO) (the shared experts: dO);
+ *   Dgrad 1: dh = bf16(W_down^T Q1x128(dy));
+ *   SwiGLU gradient, elementwise in fp64 from a and b: da = bf16(dh b SiLU'(a)),
+ *     db = bf16(dh SiLU(a));
+ *   Dgrad 2: dx = bf16(W_gate^T da' + W_up^T db') with [da' | db'] = Q1x128([da | db]).
+ * (reading: every gradient operand of a Dgrad GEMM is tiled 1 x 128 along that
+ * GEMM's reduction, as the forward's activations are; the weights keep their
+ * 128 x 128 blocks, which the transposed use leaves square.)
+ * Outputs y, dy, hq, da, db, dx (any NULL to skip); a, b, wrow, t2 are scratch
+ * of I, I, max(d, I), 2I doubles.
+ */
+static void fp8_pair(int d, int I, const uint8_t *wg, const uint8_t *wu, const uint8_t *wd, const float *wg_s,
+                     const float *wu_s, const float *wd_s, const double *x, double gj, const double *dO, double *a,
+                     double *b, double *hq, double *y, double *dy, double *da, double *db, double *dx, double *wrow,
+                     double *t2)
+{
+    for (int k = 0; k < I; ++k) {
+        load_row(OR_E4M3, wg, wg_s, OR_NC, k, d, wrow);
+        a[k] = dot(x, wrow, d);
+        load_row(OR_E4M3, wu, wu_s, OR_NC, k, d, wrow);
+        b[k] = dot(x, wrow, d);
+        hq[k] = a[k] / (1.0 + exp(-a[k])) * b[k];
+    }
+    q1x128_inplace(I, hq);
+    for (int i = 0; i < d; ++i) {
+        load_row(OR_E4M3, wd, wd_s, OR_NC, i, I, wrow);
+        y[i] = oracle_round_bf16(dot(hq, wrow, I));
+    }
+    /* dy and its 1 x 128 tiles (t2 holds the dequantised copy, d <= 2I is not assumed) */
+    double *dyq = malloc(sizeof(double) * (size_t)d);
+    for (int c = 0; c < d; ++c) {
+        dy[c] = gj == 1.0 ? dO[c] : oracle_round_bf16(gj * dO[c]);
+        dyq[c] = dy[c];
+    }
+    q1x128_inplace(d, dyq);
+    double *dh = t2;   /* I values */
+    for (int k = 0; k < I; ++k) dh[k] = 0.0;
+    for (int c = 0; c < d; ++c) {
+        load_row(OR_E4M3, wd, wd_s, OR_NC, c, I, wrow);
+        for (int k = 0; k < I; ++k) dh[k] += dyq[c] * wrow[k];
+    }
+    free(dyq);
+    for (int k = 0; k < I; ++k) {
+        const double hk = oracle_round_bf16(dh[k]);
+        const double sg = 1.0 / (1.0 + exp(-a[k]));
+        da[k] = oracle_round_bf16(hk * b[k] * sg * (1.0 + a[k] * (1.0 - sg)));
+        db[k] = oracle_round_bf16(hk * a[k] * sg);
+    }
+    /* [da | db] in 1 x 128 tiles (I is a multiple of 128, so no tile straddles the halves) */
+    double *abq = t2;
+    for (int k = 0; k < I; ++k) { abq[k] = da[k]; abq[I + k] = db[k]; }
+    q1x128_inplace(2 * I, abq);
+    for (int c = 0; c < d; ++c) dx[c] = 0.0;
+    for (int k = 0; k < I; ++k) {
+        load_row(OR_E4M3, wg, wg_s, OR_NC, k, d, wrow);
+        for (int c = 0; c < d; ++c) dx[c] += abq[k] * wrow[c];
+    }
+    for (int k = 0; k < I; ++k) {
+        load_row(OR_E4M3, wu, wu_s, OR_NC, k, d, wrow);
+        for (int c = 0; c < d; ++c) dx[c] += abq[I + k] * wrow[c];
+    }
+    for (int c = 0; c < d; ++c) dx[c] = oracle_round_bf16(dx[c]);
+}
+
+/*
+ * Gradient of the FP8 layer for a fixed selection (reading R20 as for
+ * oracle_moe_backward_f64, with the FP8 GEMMs of fp8_pair).  u [T][d] and
+ * gate_w [Nr][d] are bf16; the expert weights are e4m3 codes with 128 x 128
+ * block scales ([n][I][d] gate and up, [n][d][I] down; scales [n][I/128][d/128]
+ * and [n][d/128][I/128]); dout [T][d] holds the values of the bf16 upstream
+ * gradient.  The router keeps bf16 activations and fp64 gates (gating is not
+ * quantised).  du and dtopk_w rows are written for the listed tokens.
+ * Wgrad (reading: the activations cached in 1 x 128 tiles, u's and H's, and
+ * the gradients dy, da, db are re-tiled 128 x 1 along the expert's rows, which
+ * are the GEMM's reduction, in runs of 128 from the expert's first row):
+ *   dW_down = sum_r Q(dy_r) Q(hq_r)^T, [dW_gate; dW_up] = sum_r Q([da_r; db_r]) Q(x_r)^T
+ * summed over the expert's rows in token order (fp64).  Routed gradients for
+ * the listed experts go to slot q of drwg/drwu/drwd; the shared experts' and
+ * dgate_w (every token) only when their pointers are non-NULL.
+ */
+int oracle_moe_backward_fp8(int64_t T, int d, int Nr, int Ns, int K, int I, const uint16_t *u,
+                            const uint16_t *gate_w, const int32_t *topk_idx, const uint8_t *rwg, const uint8_t *rwu,
+                            const uint8_t *rwd, const float *rwg_s, const float *rwu_s, const float *rwd_s,
+                            const uint8_t *swg, const uint8_t *swu, const uint8_t *swd, const float *swg_s,
+                            const float *swu_s, const float *swd_s, double rs, const double *dout, int64_t n_tok,
+                            const int64_t *tok, int n_exp, const int32_t *exps, double *du, double *dtopk_w,
+                            double *dgate_w, double *drwg, double *drwu, double *drwd, double *dswg, double *dswu,
+                            double *dswd)
+{
+    init_tables();
+    const size_t wm = (size_t)I * d, sm = (size_t)(I / OR_NC) * (d / OR_NC);
+    const omat U = {OR_BF16, u}, E = {OR_BF16, gate_w};
+    if (K > 32 || d % OR_NC || I % OR_NC) return -2;
+    /* the token's activations as the expert GEMMs see them: 1 x 128 tiles of u */
+#define FP8_X(t, x)                                  \
+    do {                                             \
+        orow(U, (t), d, (x));                        \
+        q1x128_inplace(d, (x));                      \
+    } while (0)
+    const int need_tok = du || dtopk_w, need_dz = dgate_w != NULL;
+    double *dzall = need_dz ? calloc((size_t)(T > 0 ? T : 1) * K, sizeof(double)) : NULL;
+    if (need_tok || need_dz) {
+#pragma omp parallel
+        {
+            const int mx = d > I ? d : I;
+            double *x = malloc(sizeof(double) * (size_t)d), *xr = malloc(sizeof(double) * (size_t)d);
+            double *a = malloc(sizeof(double) * (size_t)I), *b = malloc(sizeof(double) * (size_t)I);
+            double *hq = malloc(sizeof(double) * (size_t)I), *y = malloc(sizeof(double) * (size_t)d);
+            double *dy = malloc(sizeof(double) * (size_t)d), *da = malloc(sizeof(double) * (size_t)I);
+            double *db = malloc(sizeof(double) * (size_t)I), *dx = malloc(sizeof(double) * (size_t)d);
+            double *acc = malloc(sizeof(double) * (size_t)d), *wrow = malloc(sizeof(double) * (size_t)mx);
+            double *t2 = malloc(sizeof(double) * (size_t)(2 * I)), *row = malloc(sizeof(double) * (size_t)(d + I));
+            double s_sel[32], g[32], dg[32];
+            /* every token for the centroid gradient, else the listed ones */
+            const int64_t n_all = need_dz ? T : (tok ? n_tok : T);
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t n = 0; n < n_all; ++n) {
+                const int64_t t = (need_dz || !tok) ? n : tok[n];
+                int listed = 1;
+                if (need_dz && tok) {
+                    listed = 0;
+                    for (int64_t m = 0; m < n_tok; ++m)
+                        if (tok[m] == t) listed = 1;
+                }
+                const double *dO = dout + (size_t)t * d;
+                const int32_t *sel = topk_idx + t * K;
+                orow(U, t, d, xr);
+                gates64(d, K, xr, E, sel, rs, s_sel, g, row);
+                FP8_X(t, x);
+                for (int c = 0; c < d; ++c) acc[c] = 0.0;
+                for (int j = 0; j < K + Ns; ++j) {
+                    const int routed = j < K, e = routed ? sel[j] : j - K;
+                    if (!routed && !(listed && need_tok)) break;
+                    const uint8_t *cg = (routed ? rwg : swg) + (size_t)e * wm, *cu = (routed ? rwu : swu) + (size_t)e * wm;
+                    const uint8_t *cd = (routed ? rwd : swd) + (size_t)e * wm;
+                    const float *sg = (routed ? rwg_s : swg_s) + (size_t)e * sm, *su = (routed ? rwu_s : swu_s) + (size_t)e * sm;
+                    const float *sd = (routed ? rwd_s : swd_s) + (size_t)e * sm;
+                    fp8_pair(d, I, cg, cu, cd, sg, su, sd, x, routed ? g[j] : 1.0, dO, a, b, hq, y, dy, da, db, dx,
+                             wrow, t2);
+                    if (routed) dg[j] = dot(dO, y, d);
+                    for (int c = 0; c < d; ++c) acc[c] += dx[c];
+                }
+                double den = 0.0, sdg = 0.0;
+                for (int j = 0; j < K; ++j) { den += s_sel[j]; sdg += dg[j] * s_sel[j]; }
+                for (int j = 0; j < K; ++j) {
+                    const double dz = rs * (dg[j] / den - sdg / (den * den)) * s_sel[j] * (1.0 - s_sel[j]);
+                    if (need_dz) dzall[t * K + j] = dz;
+                    if (listed && need_tok) {
+                        orow(E, sel[j], d, row);
+                        for (int c = 0; c < d; ++c) acc[c] += dz * row[c];
+                    }
+                }
+                if (listed && du)
+                    for (int c = 0; c < d; ++c) du[(size_t)t * d + c] = acc[c];
+                if (listed && dtopk_w)
+                    for (int j = 0; j < K; ++j) dtopk_w[t * K + j] = dg[j];
+            }
+            free(x); free(xr); free(a); free(b); free(hq); free(y); free(dy); free(da); free(db); free(dx);
+            free(acc); free(wrow); free(t2); free(row);
+        }
+    }
+    if (need_dz) {
+        for (size_t q = 0; q < (size_t)Nr * d; ++q) dgate_w[q] = 0.0;
+        for (int64_t t = 0; t < T; ++t)          /* tokens in order: fixed summation order */
+            for (int j = 0; j < K; ++j) {
+                double *de = dgate_w + (size_t)topk_idx[t * K + j] * d;
+                for (int c = 0; c < d; ++c) de[c] += dzall[t * K + j] * load_plain(OR_BF16, u, t * d + c);
+            }
+        free(dzall);
+    }
+    /* Wgrad: per expert, the rows' dy, hq, da, db and x, re-tiled 128 x 1, then the outer products */
+    for (int pass = 0; pass < 2; ++pass) {
+        const int nE = pass == 0 ? (exps ? n_exp : (drwg ? Nr : 0)) : (dswg ? Ns : 0);
+        for (int q = 0; q < nE; ++q) {
+            const int e = pass == 0 ? (exps ? exps[q] : q) : q;
+            const uint8_t *cg = (pass ? swg : rwg) + (size_t)e * wm, *cu = (pass ? swu : rwu) + (size_t)e * wm;
+            const uint8_t *cd = (pass ? swd : rwd) + (size_t)e * wm;
+            const float *sg = (pass ? swg_s : rwg_s) + (size_t)e * sm, *su = (pass ? swu_s : rwu_s) + (size_t)e * sm;
+            const float *sd = (pass ? swd_s : rwd_s) + (size_t)e * sm;
+            double *gwg = (pass ? dswg : drwg) + q * wm, *gwu = (pass ? dswu : drwu) + q * wm;
+            double *gwd = (pass ? dswd : drwd) + q * wm;
+            int64_t nt = 0;
+            int64_t *tl = malloc(sizeof(int64_t) * (size_t)(T > 0 ? T : 1));
+            int *jl = malloc(sizeof(int) * (size_t)(T > 0 ? T : 1));
+            for (int64_t t = 0; t < T; ++t) {
+                if (pass) { tl[nt] = t; jl[nt++] = -1; continue; }
+                for (int j = 0; j < K; ++j)
+                    if (topk_idx[t * K + j] == e) { tl[nt] = t; jl[nt++] = j; }
+            }
+            /* per row: x[d], dy[d], hq[I], da[I], db[I] */
+            const size_t per = 2 * (size_t)d + 3 * (size_t)I;
+            double *buf = malloc(sizeof(double) * per * (size_t)(nt > 0 ? nt : 1));
+#pragma omp parallel
+            {
+                const int mx = d > I ? d : I;
+                double *a = malloc(sizeof(double) * (size_t)I), *b = malloc(sizeof(double) * (size_t)I);
+                double *y = malloc(sizeof(double) * (size_t)d), *dx = malloc(sizeof(double) * (size_t)d);
+                double *wrow = malloc(sizeof(double) * (size_t)mx), *t2 = malloc(sizeof(double) * (size_t)(2 * I));
+                double *xr = malloc(sizeof(double) * (size_t)d), *row = malloc(sizeof(double) * (size_t)(d + I));
+                double s_sel[32], g[32];
+#pragma omp for schedule(dynamic, 1)
+                for (int64_t n = 0; n < nt; ++n) {
+                    const int64_t t = tl[n];
+                    double *x = buf + per * n, *dy = x + d, *hq = dy + d, *da = hq + I, *db = da + I;
+                    double gj = 1.0;
+                    if (!pass) {
+                        orow(U, t, d, xr);
+                        gates64(d, K, xr, E, topk_idx + t * K, rs, s_sel, g, row);
+                        gj = g[jl[n]];
+                    }
+                    FP8_X(t, x);
+                    fp8_pair(d, I, cg, cu, cd, sg, su, sd, x, gj, dout + (size_t)t * d, a, b, hq, y, dy, da, db, dx,
+                             wrow, t2);
+                }
+                free(a); free(b); free(y); free(dx); free(wrow); free(t2); free(xr); free(row);
+            }
+            /* 128 x 1 tiles along the expert's rows, column by column */
+            q128x1_inplace(nt, d, buf, per);                 /* x  */
+            q128x1_inplace(nt, d, buf + d, per);             /* dy */
+            q128x1_inplace(nt, I, buf + 2 * d, per);         /* hq */
+            q128x1_inplace(nt, I, buf + 2 * d + I, per);     /* da */
+            q128x1_inplace(nt, I, buf + 2 * d + 2 * I, per); /* db */
+#pragma omp parallel for schedule(static)
+            for (int c = 0; c < d; ++c)
+                for (int k = 0; k < I; ++k) {
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < nt; ++n) acc += buf[per * n + d + c] * buf[per * n + 2 * d + k];
+                    gwd[(size_t)c * I + k] = acc;
+                }
+#pragma omp parallel for schedule(static)
+            for (int k = 0; k < I; ++k)
+                for (int c = 0; c < d; ++c) {
+                    double ag = 0.0, au = 0.0;
+                    for (int64_t n = 0; n < nt; ++n) {
+                        const double xc = buf[per * n + c];
+                        ag += buf[per * n + 2 * d + I + k] * xc;
+                        au += buf[per * n + 2 * d + 2 * I + k] * xc;
+                    }
+                    gwg[(size_t)k * d + c] = ag;
+                    gwu[(size_t)k * d + c] = au;
+                }
+            free(buf); free(tl); free(jl);
+        }
+    }
+#undef FP8_X
+    return 0;
+}
+
 int oracle_num_threads(void)
 {
 #ifdef _OPENMP

@@ -620,3 +620,96 @@ def test_backward_token_and_expert_subsets(orc):
     assert (sub["dg"][[2, 7]] == full["dg"][[2, 7]]).all()
     for k in ("dwg", "dwu", "dwd"):
         assert (sub[k][0] == full[k][4]).all() and (sub[k][1] == full[k][1]).all()
+
+
+# ---------------------------------------------------------------------------
+# FP8 backward (§3.3: Dgrad and Wgrad GEMMs in FP8)
+# ---------------------------------------------------------------------------
+
+def test_quant_128x1_is_the_transpose_of_1x128(orc):
+    """One segment whose length is a multiple of 128: 128 x 1 tiles along the
+    rows are the 1 x 128 tiles of the transposed matrix, bit for bit."""
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((256, 384)) * np.exp2(rng.integers(-6, 6, (1, 384)))).astype(np.float32)
+    x[:, 5] = 0.0
+    q, s = orc.quant_128x1(x, np.array([0, 256], np.int32))
+    qt, st = orc.quant_1x128(np.ascontiguousarray(x.T))
+    assert (q == qt.T).all() and (s.view(np.uint32) == st.T.view(np.uint32)).all()
+    assert (s[:, 5] == 1.0).all() and (q[:, 5] == 0).all()
+
+
+def test_quant_128x1_segments_gather_and_e4m3_input(orc):
+    rng = np.random.default_rng(4)
+    x = syn.to_bf16_bits(rng.standard_normal((500, 256)).astype(np.float32))
+    off = np.array([0, 130, 130, 300, 431], np.int32)        # ragged runs, one empty segment
+    gather = rng.integers(0, 500, 431).astype(np.int32)
+    q, s = orc.quant_128x1(x, off, gather=gather)
+    assert s.shape[0] == 2 + 0 + 2 + 2
+    xg = x[gather]
+    b = 0
+    for e in range(4):
+        seg = xg[off[e]:off[e + 1]]
+        if len(seg) == 0:
+            continue
+        qa, sa = orc.quant_128x1(seg, np.array([0, len(seg)], np.int32))   # the segment alone
+        assert (q[off[e]:off[e + 1]] == qa).all()
+        assert (s[b:b + len(sa)].view(np.uint32) == sa.view(np.uint32)).all()
+        b += len(sa)
+    # e4m3 input with 1 x 128 scales equals its dequantised fp32 values
+    c, cs = orc.quant_1x128(x)
+    tab = np.array([orc.decode_e4m3(k) for k in range(256)])
+    xd = (tab[c] * np.repeat(cs, 128, 1)).astype(np.float32)
+    q8, s8 = orc.quant_128x1(c, off, x_scales=cs, gather=gather)
+    qd, sd = orc.quant_128x1(xd, off, gather=gather)
+    assert (q8 == qd).all() and (s8 == sd).all()
+
+
+def _fp8_layer(seed, T=64, d=256, Nr=8, Ns=1, G=2, Mg=1, K=2, I=256):
+    import oracle
+    cfg = syn.LayerConfig("t", T=T, d=d, Nr=Nr, G=G, Mg=Mg, K=K, Ns=Ns, I=I, dtype="bf16", bias="uniform")
+    inp = syn.layer_inputs(cfg, seed=seed)
+    _, idx, _ = oracle.route(inp["u"], inp["gate_w"], inp["bias"], G=G, Mg=Mg, K=K)
+    rq = [oracle.quant_128x128(inp[k]) for k in ("wg", "wu", "wd")]
+    sq = [oracle.quant_128x128(inp[k]) for k in ("swg", "swu", "swd")] if Ns else None
+    dout = syn.grad_output(cfg, seed=seed)
+    doutf = (dout.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return inp, idx, rq, sq, doutf
+
+
+def test_backward_fp8_within_e4m3_precision_of_the_exact_gradient(orc):
+    """The FP8 chain (every Dgrad / Wgrad operand quantised) against the exact
+    fp64 chain rule of the same layer (dequantised weights, the 1 x 128 tiles
+    of u): every gradient within 8% of max|ref|.  e4m3 keeps 3 mantissa bits
+    (at most 2^-4 relative per element, about 2% r.m.s.) and each gradient
+    passes two to four quantisations; a transposed or dropped operand is off by
+    O(1)."""
+    inp, idx, rq, sq, dout = _fp8_layer(5)
+    r8 = orc.moe_backward_fp8(inp["u"], inp["gate_w"], idx, [a for a, _ in rq], [b for _, b in rq],
+                              [a for a, _ in sq], [b for _, b in sq], dout)
+    tab = np.array([orc.decode_e4m3(c) for c in range(256)])
+
+    def deq(q, s):
+        return tab[q] * np.repeat(np.repeat(s, 128, 1), 128, 2)
+
+    uq, us = orc.quant_1x128(inp["u"])
+    ud = tab[uq] * np.repeat(us, 128, 1)
+    gw = (inp["gate_w"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    r64 = orc.moe_backward(ud, gw, idx, [deq(a, b) for a, b in rq], [deq(a, b) for a, b in sq], dout)
+    for k in ("du", "dg", "dgate_w", "dwg", "dwu", "dwd", "dswg", "dswu", "dswd"):
+        err = np.abs(r8[k] - r64[k]).max() / np.abs(r64[k]).max()
+        assert err <= 0.08, (k, err)
+        assert err >= 1e-4, (k, err)          # the quantisation is really there
+
+
+def test_backward_fp8_subsets_and_empty_expert(orc):
+    inp, idx, rq, sq, dout = _fp8_layer(6, T=40, Nr=8, K=2)
+    args = (inp["u"], inp["gate_w"], idx, [a for a, _ in rq], [b for _, b in rq], [a for a, _ in sq],
+            [b for _, b in sq], dout)
+    full = orc.moe_backward_fp8(*args)
+    unused = sorted(set(range(8)) - set(idx.ravel().tolist()))
+    sub = orc.moe_backward_fp8(*args, tokens=[3, 17], experts=[int(idx[3, 0])] + unused[:1], dgate=False,
+                               dshared=False)
+    assert (sub["du"][[3, 17]] == full["du"][[3, 17]]).all() and (sub["dg"][[3, 17]] == full["dg"][[3, 17]]).all()
+    assert (sub["dwd"][0] == full["dwd"][idx[3, 0]]).all()
+    for i in unused:
+        assert (full["dwg"][i] == 0).all() and (full["dwd"][i] == 0).all() and (full["dgate_w"][i] == 0).all()
