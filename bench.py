@@ -82,20 +82,25 @@ def algorithmic_bwd(cfg, n_touched):
     operand read or written once (weights of touched experts once, u once,
     activations per expert row once), no padding rows."""
     T, d, I, K, Ns, Nr = cfg.T, cfg.d, cfg.I, cfg.K, cfg.Ns, cfg.Nr
-    a = esz(cfg.dtype)
+    fp8 = cfg.dtype == "fp8"
+    a = 2 if fp8 else esz(cfg.dtype)                  # activations, gradients (bf16 for e4m3 layers)
+    o = 1 + 4.0 / 128 if fp8 else a                   # GEMM operand: e4m3 code + its tile scale
+    wb = 1 + 4.0 / (128 * 128) if fp8 else a          # weight element (+ block scale)
     rr, rs = T * K, T * Ns
     rows = rr + rs
     ex = n_touched + Ns
     gemm = 2.0 * rows * I * d
+    # e4m3: the stages that produce a Dgrad input also write its 1x128 tiles
+    q = o if fp8 else 0
     return dict(
-        bwd_combine=(2.0 * rr * d, T * d * a + 2 * rr * d * a + rr * 12),
-        bwd_dh=(gemm, ex * I * d * a + (rr + T) * d * a + rows * I * a),
-        bwd_swiglu=(2 * gemm, ex * 2 * I * d * a + T * d * a + rows * I * a + rows * 2 * I * a),
-        bwd_dx=(2 * gemm, ex * 2 * I * d * a + rows * 2 * I * a + rows * d * a),
-        bwd_token=(2.0 * rows * d, rows * d * a + Nr * d * a + T * d * a + rr * 16 + T * Nr * 0),
+        bwd_combine=(2.0 * rr * d, T * d * a + 2 * rr * d * a + rr * 12 + (rr + T) * d * q),
+        bwd_dh=(gemm, ex * I * d * wb + (rr + T) * d * o + rows * I * a),
+        bwd_swiglu=(2 * gemm, ex * 2 * I * d * wb + T * d * o + rows * I * a + rows * 2 * I * (a + q)),
+        bwd_dx=(2 * gemm, ex * 2 * I * d * wb + rows * 2 * I * o + rows * d * a),
+        bwd_token=(2.0 * rows * d, rows * d * a + Nr * d * a + T * d * a + rr * 16),
         bwd_dgate=(2.0 * rr * d, T * d * a + Nr * d * 4 + rr * 8),
-        wgrad_down=(gemm, (rr + T) * d * a + rows * I * a + ex * I * d * a),
-        wgrad_gate_up=(2 * gemm, rows * 2 * I * a + T * d * a + ex * 2 * I * d * a))
+        wgrad_down=(gemm, (rr + T) * d * o + rows * I * o + ex * I * d * a),
+        wgrad_gate_up=(2 * gemm, rows * 2 * I * o + T * d * o + ex * 2 * I * d * a))
 
 
 BWD_KERNELS = {"bwd_combine": "bwd_combine_kernel", "bwd_dh": "bwd_dh", "bwd_swiglu": "bwd_swiglu",
@@ -180,15 +185,33 @@ def cpu_baseline_backward(cfg, inp, n_tokens):
     dout = syn.grad_output(cfg)[:n]
     dout = (dout.astype(np.uint32) << 16).view(np.float32) if dout.dtype == np.uint16 else dout
     _, idx, _ = oracle.route(u, inp["gate_w"], inp["bias"], G=cfg.G, Mg=cfg.Mg, K=cfg.K)
+    routed = (inp["wg"], inp["wu"], inp["wd"])
     shared = (inp["swg"], inp["swu"], inp["swd"]) if cfg.Ns else None
-    t0 = time.perf_counter()
-    oracle.moe_backward(u, inp["gate_w"], idx, (inp["wg"], inp["wu"], inp["wd"]), shared, dout,
-                        experts=np.zeros(0, np.int32), dgate=False, dshared=False)
+    none = np.zeros(0, np.int32)
+    if cfg.dtype == "fp8":
+        # weights quantised once before timing (only the experts the sample touches), as on the GPU
+        need = np.unique(idx)
+        rq, rsc = [], []
+        for w in routed:
+            qw = np.zeros(w.shape, np.uint8)
+            sw = np.ones((w.shape[0], w.shape[1] // 128, w.shape[2] // 128), np.float32)
+            qw[need], sw[need] = oracle.quant_128x128(w[need])
+            rq.append(qw)
+            rsc.append(sw)
+        sp = [oracle.quant_128x128(w) for w in shared] if shared else None
+        t0 = time.perf_counter()
+        oracle.moe_backward_fp8(u, inp["gate_w"], idx, rq, rsc, [p[0] for p in sp] if sp else None,
+                                [p[1] for p in sp] if sp else None, dout, experts=none, dgate=False, dshared=False)
+    else:
+        t0 = time.perf_counter()
+        oracle.moe_backward(u, inp["gate_w"], idx, routed, shared, dout, experts=none, dgate=False, dshared=False)
     dt = time.perf_counter() - t0
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": "input-gradient chain rule (du and dL/dg: %d routed + %d shared SwiGLU experts recomputed "
-                      "and differentiated per token, fp64) for the first %d tokens of the %d-token batch; weight "
-                      "and centroid gradients not in the sample; %.1f s" % (cfg.K, cfg.Ns, n, cfg.T, dt)}
+                      "and differentiated per token, fp64%s) for the first %d tokens of the %d-token batch; weight "
+                      "and centroid gradients not in the sample; %.1f s" % (
+                          cfg.K, cfg.Ns, ", Dgrad operands in e4m3 tiles" if cfg.dtype == "fp8" else "", n, cfg.T,
+                          dt)}
 
 
 def main():
@@ -218,9 +241,6 @@ def main():
     from mixture_experts_layer_35_amd.layer import MoeLayer, to_device
 
     cfg = syn.CONFIGS[args.config]
-    if args.backward and cfg.dtype == "fp8":
-        print("bench.py: the backward runs on fp32 / bf16 layers", file=sys.stderr)
-        sys.exit(2)
     if args.steps is None:
         args.steps = syn.SKEW_STEPS if cfg.skew else 20
     torch.cuda.set_device(0)
@@ -252,14 +272,16 @@ def main():
         # weight transposes are weight preparation (once per weight update), timed apart
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        rt, st = layer.transposed_weights(stream)
+        (rt, rts), (st, sts) = layer.transposed_weights(stream)
         e1.record()
         torch.cuda.synchronize()
-        bw = dict(rt=rt, st=st, transpose_ms=e0.elapsed_time(e1),
+        # weight gradients in the activation format (bf16 for e4m3 weights)
+        grad_like = lambda ws: tuple(torch.empty(w.shape, dtype=us[0].dtype, device="cuda") for w in ws)
+        bw = dict(rt=rt, rts=rts, st=st, sts=sts, transpose_ms=e0.elapsed_time(e1),
                   dout=to_device(syn.grad_output(cfg)), du=torch.empty_like(us[0]),
                   dgate=torch.empty((cfg.Nr, cfg.d), dtype=torch.float32, device="cuda"),
-                  dr=tuple(torch.empty_like(w) for w in layer.routed_w),
-                  ds=tuple(torch.empty_like(w) for w in layer.shared_w) if cfg.Ns else None,
+                  dr=grad_like(layer.routed_w),
+                  ds=grad_like(layer.shared_w) if cfg.Ns else None,
                   ws=torch.empty(max(moe.moe_backward_workspace_bytes(shape), 256), dtype=torch.uint8,
                                  device="cuda"))
 
@@ -267,9 +289,9 @@ def main():
         moe.moe_forward_timed(shape, us[k % len(us)], layer.gate_w, layer.bias, layer.routed_w, layer.routed_s,
                               layer.shared_w, layer.shared_s, out, None, None, counts[k], None, ws, stream, events)
         if bw is not None:
-            moe.moe_backward_timed(shape, us[k % len(us)], layer.gate_w, layer.routed_w, bw["rt"], layer.shared_w,
-                                   bw["st"], ws, bw["dout"], bw["du"], bw["dgate"], bw["dr"], bw["ds"], None,
-                                   bw["ws"], stream, bevents)
+            moe.moe_backward_timed(shape, us[k % len(us)], layer.gate_w, layer.routed_w, layer.routed_s, bw["rt"],
+                                   bw["rts"], layer.shared_w, layer.shared_s, bw["st"], bw["sts"], ws, bw["dout"],
+                                   bw["du"], bw["dgate"], bw["dr"], bw["ds"], None, bw["ws"], stream, bevents)
         if cfg.skew:
             moe.moe_bias_update(shape, counts[k], layer.bias, syn.SKEW_GAMMA, stream)
 
@@ -384,7 +406,7 @@ def main():
                                                                    "fp32": "fp32"}[cfg.dtype]))
     line = {
         "metric": "MoE layer tokens/s + achieved TFLOP/s (% MFMA peak), V3 shape bf16/fp8" if bw is None else
-                  "MoE layer forward+backward tokens/s + achieved TFLOP/s, V3 shape bf16",
+                  "MoE layer forward+backward tokens/s + achieved TFLOP/s, V3 shape bf16/fp8",
         "value": round(T / (ms / 1000.0), 1),
         "unit": "tokens/s",
         "n_gpus": 1,

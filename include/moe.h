@@ -221,15 +221,18 @@ int moe_forward_timed(const moe_shape *shape, const void *u, const void *gate_w,
  * moe_transpose_expert_weights -- the transposed weight copies moe_backward
  * reads (input gradients run through the same grouped expert kernel as the
  * forward, which wants the reduction dimension contiguous):
- *   w_down_t    [n][I][d]  = W_down^T per expert,
- *   w_gate_up_t [n][d][2I] = [W_gate^T | W_up^T] per expert.
- * w_gate, w_up [n][I][d], w_down [n][d][I] in shape->w_dtype (MOE_F32 or
- * MOE_BF16); the copies are bit-exact.  Rebuild them whenever the weights
- * change.  n = N_r for the routed and N_s for the shared experts.
- * Errors: MOE_ERR_UNSUPPORTED for E4M3 shapes.
+ *   wt[0] = W_down^T [n][I][d] per expert,
+ *   wt[1] = [W_gate^T | W_up^T] [n][d][2I] per expert,
+ * from w = {W_gate [n][I][d], W_up [n][I][d], W_down [n][d][I]} in
+ * shape->w_dtype.  For E4M3 the 128 x 128 block scales follow their blocks:
+ * w_s = the three forward scale grids ([n][I/128][d/128], .., [n][d/128][I/128])
+ * and wt_s = {[n][I/128][d/128], [n][d/128][2I/128]}; NULL otherwise.  The
+ * copies are bit-exact.  Rebuild them whenever the weights change.
+ * n = N_r for the routed and N_s for the shared experts.  (Pointer arrays are
+ * host memory; their elements are device pointers.)
  */
-int moe_transpose_expert_weights(const moe_shape *shape, int32_t n, const void *w_gate, const void *w_up,
-                                 const void *w_down, void *w_down_t, void *w_gate_up_t, void *stream);
+int moe_transpose_expert_weights(const moe_shape *shape, int32_t n, const void *const *w, const float *const *w_s,
+                                 void *const *wt, float *const *wt_s, void *stream);
 
 /*
  * moe_backward -- gradient of the layer (§2.1.2) for the selection that
@@ -246,45 +249,56 @@ int moe_transpose_expert_weights(const moe_shape *shape, int32_t n, const void *
  *     (z = u . e, s = sigmoid(z)),
  *   du_t = sum_j dx_{t,j} + sum_shared dx + sum_j dz_j e_{sel_j},
  *   de_i = sum over slots routed to i of dz u_t.
+ * E4M3 layers (§3.3: Fprop, Dgrad and Wgrad GEMMs in FP8): the Dgrad GEMMs take
+ * dy, dout and [da | db] in 1 x 128 tiles along their reduction with the
+ * transposed 128 x 128 weight blocks; the Wgrad GEMMs take both operands in
+ * 128 x 1 tiles along each expert's rows (runs of 128 from its first row):
+ * dy, dout, [da | db], and the forward's cached 1 x 128 tiles of H and u,
+ * re-tiled; fp32 accumulation per run with both column scales.  The router
+ * chain (dg, dz, du's centroid term, dgate_w) stays in fp32.
  * (With MOE_ADD_RESIDUAL the residual's own gradient, dout, is the caller's
  * to add: du holds the layer's part only.)
- * Inputs: u, gate_w and the weights exactly as passed to moe_forward;
- * routed_wt = {w_down_t, w_gate_up_t} from moe_transpose_expert_weights,
- * shared_wt likewise (NULL when N_s == 0); fwd_ws/fwd_ws_bytes: the forward
- * workspace of the moe_forward call whose output dout refers to, untouched
- * since (it holds the scores, selection, dispatch, H and Y, which are the saved
- * activations).  Storage: dout, du and the weight gradients in act_dtype.
- * Outputs: du [T][d]; optional (NULL to skip): dgate_w [N_r][d] fp32,
- * d_routed_w = {dW_gate, dW_up, dW_down} (layout of routed_w), d_shared_w
- * likewise, dtopk_w [T][K] fp32 = dL/dg.  Gradients are written, not
- * accumulated.  Sums run in fp32 in a fixed order (deterministic).
- * ws: moe_backward_workspace_bytes(shape).
- * Errors: MOE_ERR_UNSUPPORTED for E4M3 shapes; MOE_ERR_WORKSPACE when
- * fwd_ws_bytes is smaller than moe_workspace_bytes(shape, MOE_WS_FORWARD).
+ * Inputs: u, gate_w, the weights and (E4M3) their scales exactly as passed to
+ * moe_forward; routed_wt / routed_wt_s from moe_transpose_expert_weights,
+ * shared_* likewise (NULL when N_s == 0); *_s and *_wt_s are NULL for
+ * fp32 / bf16 layers.  fwd_ws/fwd_ws_bytes: the forward workspace of the
+ * moe_forward call whose output dout refers to, untouched since (it holds the
+ * scores, selection, dispatch, H and Y, which are the saved activations).
+ * Storage: dout, du and the weight gradients in act_dtype (bf16 for E4M3
+ * layers).  Outputs: du [T][d]; optional (NULL to skip): dgate_w [N_r][d]
+ * fp32, d_routed_w = {dW_gate, dW_up, dW_down} (layout of the forward weights,
+ * act_dtype), d_shared_w likewise, dtopk_w [T][K] fp32 = dL/dg.  Gradients
+ * are written, not accumulated.  Sums run in fp32 in a fixed order
+ * (deterministic).  ws: moe_backward_workspace_bytes(shape).
+ * Errors: MOE_ERR_WORKSPACE when fwd_ws_bytes is smaller than
+ * moe_workspace_bytes(shape, MOE_WS_FORWARD); MOE_ERR_INVALID_ARG for a NULL
+ * required pointer or scale.
  */
 int moe_backward(const moe_shape *shape, const void *u, const void *gate_w, const void *const *routed_w,
-                 const void *const *routed_wt, const void *const *shared_w, const void *const *shared_wt,
-                 const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du, float *dgate_w,
-                 void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes,
-                 void *stream);
+                 const float *const *routed_s, const void *const *routed_wt, const float *const *routed_wt_s,
+                 const void *const *shared_w, const float *const *shared_s, const void *const *shared_wt,
+                 const float *const *shared_wt_s, const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du,
+                 float *dgate_w, void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws,
+                 size_t ws_bytes, void *stream);
 
 /*
  * moe_backward_timed -- moe_backward that also records caller-created HIP
  * events on `stream` at its stage boundaries:
- *   stage_events[0] before the combine gradient   [1] after it (dY, dg)
- *   [2] after dH = dY W_down                      [3] after the SwiGLU gradient pass ([dA | dB])
+ *   stage_events[0] before the combine gradient   [1] after it (dY, dg; e4m3: their 1 x 128 tiles)
+ *   [2] after dH = dY W_down                      [3] after the SwiGLU gradient pass ([dA | dB], tiled)
  *   [4] after dX = [dA | dB] [W_gate ; W_up]      [5] after the token pass (du, dz)
- *   [6] after the centroid gradient               [7] after dW_down
+ *   [6] after the centroid gradient               [7] after dW_down (e4m3: with its operands' tiling)
  *   [8] after dW_gate / dW_up
  * NULL entries (or a NULL array, 9 entries otherwise) are skipped; skipped
  * optional outputs leave their stage empty.  Results are identical to
  * moe_backward.
  */
 int moe_backward_timed(const moe_shape *shape, const void *u, const void *gate_w, const void *const *routed_w,
-                       const void *const *routed_wt, const void *const *shared_w, const void *const *shared_wt,
-                       const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du, float *dgate_w,
-                       void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes,
-                       void *stream, void *const *stage_events);
+                       const float *const *routed_s, const void *const *routed_wt, const float *const *routed_wt_s,
+                       const void *const *shared_w, const float *const *shared_s, const void *const *shared_wt,
+                       const float *const *shared_wt_s, const void *fwd_ws, size_t fwd_ws_bytes, const void *dout,
+                       void *du, float *dgate_w, void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w,
+                       void *ws, size_t ws_bytes, void *stream, void *const *stage_events);
 
 /* Workspace bytes for moe_backward (0 when rejected). */
 size_t moe_backward_workspace_bytes(const moe_shape *shape);
@@ -349,6 +363,34 @@ int moe_quantize_1x128(int64_t rows, int32_t cols, int32_t x_dtype, const void *
  */
 int moe_quantize_weights_128x128(int64_t nmat, int32_t rows, int32_t cols, int32_t w_dtype, const void *w,
                                  uint8_t *q, float *s, void *stream);
+
+/*
+ * moe_quantize_128x1 -- Q over 128x1 tiles down the rows of segments, the
+ * operands of the FP8 weight-gradient GEMMs (§3.3 fine-grained quantization:
+ * its tiles are 1x128 for activations in the forward direction and 128x1
+ * where the backward reduces over tokens; the tile origin is not stated,
+ * read as runs of 128 list rows from each segment's first row).
+ *   n_seg segments; offsets [n_seg+1] (device, int32, offsets[0] >= 0,
+ *   nondecreasing, offsets[n_seg] <= max_rows): segment e owns list rows
+ *   offsets[e] .. offsets[e+1]-1, cut into runs of 128 rows from its first
+ *   row (the last run of a segment may be shorter);
+ *   list row r reads x row gather[r] (gather NULL: row r);
+ *   x [.][cols] MOE_BF16, or MOE_E4M3 codes with 1x128 fp32 scales
+ *   x_s [.][cols/128] (decoded to fp32 before the re-quantisation);
+ *   q [offsets[n_seg]][cols] e4m3 codes, rows offsets[0].. written;
+ *   s [n_blocks][cols] fp32: one scale per run and column, runs numbered
+ *   segment by segment; block_base [n_seg+1] (device, int32, out): the
+ *   first run of each segment, block_base[n_seg] = n_blocks
+ *   <= max_rows/128 + n_seg.
+ * A scale is amax/448 over its run's column (1 for an all-zero column);
+ * codes are round-to-nearest-even of clamp(v/scale, -448, 448).
+ * Offsets that break the stated order are undefined behaviour.
+ * Errors: INVALID_ARG for negative sizes or a NULL buffer; UNSUPPORTED for
+ * cols % 128 != 0 or another x_dtype.  n_seg == 0 does nothing.
+ */
+int moe_quantize_128x1(int32_t n_seg, const int32_t *offsets, int64_t max_rows, int32_t cols, int32_t x_dtype,
+                       const void *x, const float *x_s, const int32_t *gather, uint8_t *q, float *s,
+                       int32_t *block_base, void *stream);
 
 /* Message for the calling thread's last failed call ("" if none). */
 const char *moe_last_error(void);

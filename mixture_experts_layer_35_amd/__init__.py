@@ -28,7 +28,8 @@ EXPORTED = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_f
             "moe_workspace_bytes",
             "moe_ffn_workspace_bytes", "moe_bias_update", "moe_seq_balance", "moe_seq_balance_workspace_bytes",
             "moe_transpose_expert_weights", "moe_backward", "moe_backward_timed", "moe_backward_workspace_bytes",
-            "moe_quantize_1x128", "moe_quantize_weights_128x128", "moe_last_error", "moe_version")
+            "moe_quantize_1x128", "moe_quantize_weights_128x128", "moe_quantize_128x1", "moe_last_error",
+            "moe_version")
 
 
 class MoeError(RuntimeError):
@@ -80,11 +81,12 @@ def lib():
                 "moe_forward_timed": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P, P],
                 "moe_bias_update": [S, P, P, ctypes.c_float, P],
                 "moe_seq_balance": [S, P, P, i64, ctypes.c_float, P, P, P, P, sz, P],
-                "moe_transpose_expert_weights": [S, i32, P, P, P, P, P, P],
-                "moe_backward": [S, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, sz, P],
-                "moe_backward_timed": [S, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, sz, P, P],
+                "moe_transpose_expert_weights": [S, i32, P, P, P, P, P],
+                "moe_backward": [S, P, P, P, P, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, sz, P],
+                "moe_backward_timed": [S, P, P, P, P, P, P, P, P, P, P, P, sz, P, P, P, P, P, P, P, sz, P, P],
                 "moe_quantize_1x128": [i64, i32, i32, P, P, P, P],
                 "moe_quantize_weights_128x128": [i64, i32, i32, i32, P, P, P, P],
+                "moe_quantize_128x1": [i32, P, i64, i32, i32, P, P, P, P, P, P, P],
             }
             for name, args in sig.items():
                 f = getattr(L, name)
@@ -235,46 +237,66 @@ def moe_seq_balance(shape, scores, topk_idx, seq_len, alpha, loss, counts=None, 
                                         _ptr(counts), _ptr(share), _ptr(ws), _nbytes(ws), _stream(stream)))
 
 
-def moe_transpose_expert_weights(shape, n, w_gate, w_up, w_down, w_down_t, w_gate_up_t, stream=None):
-    return _check(lib().moe_transpose_expert_weights(ctypes.byref(shape), n, _ptr(w_gate), _ptr(w_up), _ptr(w_down),
-                                                     _ptr(w_down_t), _ptr(w_gate_up_t), _stream(stream)))
+def moe_transpose_expert_weights(shape, n, w, w_s, wt, wt_s, stream=None):
+    """w = (W_gate, W_up, W_down); wt = (W_down^T, [W_gate^T | W_up^T]); w_s / wt_s: the e4m3
+    block scales (3 and 2 arrays) or None."""
+    a, b, c, e = (_ptr_array(x) for x in (w, w_s, wt, wt_s))
+    return _check(lib().moe_transpose_expert_weights(ctypes.byref(shape), n, a[0] if a else None,
+                                                     b[0] if b else None, c[0] if c else None, e[0] if e else None,
+                                                     _stream(stream)))
 
 
 def moe_backward_workspace_bytes(shape: MoeShape) -> int:
     return lib().moe_backward_workspace_bytes(ctypes.byref(shape))
 
 
-def moe_backward(shape, u, gate_w, routed_w, routed_wt, shared_w, shared_wt, fwd_ws, dout, du, dgate_w=None,
-                 d_routed_w=None, d_shared_w=None, dtopk_w=None, ws=None, stream=None):
-    """routed_w / shared_w: (W_gate, W_up, W_down); *_wt: (W_down^T, [W_gate^T | W_up^T]); fwd_ws: the
-    workspace tensor of the forward call whose output dout refers to."""
-    rw, rt, sw, st, dr, ds = (_ptr_array(x) for x in (routed_w, routed_wt, shared_w, shared_wt, d_routed_w,
-                                                       d_shared_w))
-    return _check(lib().moe_backward(ctypes.byref(shape), _ptr(u), _ptr(gate_w), rw[0] if rw else None,
-                                     rt[0] if rt else None, sw[0] if sw else None, st[0] if st else None,
-                                     _ptr(fwd_ws), _nbytes(fwd_ws), _ptr(dout), _ptr(du), _ptr(dgate_w),
-                                     dr[0] if dr else None, ds[0] if ds else None, _ptr(dtopk_w), _ptr(ws),
-                                     _nbytes(ws), _stream(stream)))
+def _bwd_args(shape, u, gate_w, routed_w, routed_s, routed_wt, routed_wt_s, shared_w, shared_s, shared_wt,
+              shared_wt_s, fwd_ws, dout, du, dgate_w, d_routed_w, d_shared_w, dtopk_w, ws, stream):
+    arrs = [_ptr_array(x) for x in (routed_w, routed_s, routed_wt, routed_wt_s, shared_w, shared_s, shared_wt,
+                                    shared_wt_s, d_routed_w, d_shared_w)]
+    keep = [x for x in arrs if x]
+    p = [x[0] if x else None for x in arrs]
+    return keep, (ctypes.byref(shape), _ptr(u), _ptr(gate_w), p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7],
+                  _ptr(fwd_ws), _nbytes(fwd_ws), _ptr(dout), _ptr(du), _ptr(dgate_w), p[8], p[9], _ptr(dtopk_w),
+                  _ptr(ws), _nbytes(ws), _stream(stream))
 
 
-def moe_backward_timed(shape, u, gate_w, routed_w, routed_wt, shared_w, shared_wt, fwd_ws, dout, du, dgate_w=None,
-                       d_routed_w=None, d_shared_w=None, dtopk_w=None, ws=None, stream=None, stage_events=None):
+def moe_backward(shape, u, gate_w, routed_w, routed_s, routed_wt, routed_wt_s, shared_w, shared_s, shared_wt,
+                 shared_wt_s, fwd_ws, dout, du, dgate_w=None, d_routed_w=None, d_shared_w=None, dtopk_w=None, ws=None,
+                 stream=None):
+    """routed_w / shared_w: (W_gate, W_up, W_down); *_wt: (W_down^T, [W_gate^T | W_up^T]); *_s / *_wt_s: the
+    e4m3 block scales or None; fwd_ws: the workspace tensor of the forward call whose output dout refers to."""
+    keep, args = _bwd_args(shape, u, gate_w, routed_w, routed_s, routed_wt, routed_wt_s, shared_w, shared_s,
+                           shared_wt, shared_wt_s, fwd_ws, dout, du, dgate_w, d_routed_w, d_shared_w, dtopk_w, ws,
+                           stream)
+    rc = lib().moe_backward(*args)
+    del keep
+    return _check(rc)
+
+
+def moe_backward_timed(shape, u, gate_w, routed_w, routed_s, routed_wt, routed_wt_s, shared_w, shared_s, shared_wt,
+                       shared_wt_s, fwd_ws, dout, du, dgate_w=None, d_routed_w=None, d_shared_w=None, dtopk_w=None,
+                       ws=None, stream=None, stage_events=None):
     """stage_events: 9 raw hipEvent_t handles (ints) or None."""
-    rw, rt, sw, st, dr, ds = (_ptr_array(x) for x in (routed_w, routed_wt, shared_w, shared_wt, d_routed_w,
-                                                       d_shared_w))
+    keep, args = _bwd_args(shape, u, gate_w, routed_w, routed_s, routed_wt, routed_wt_s, shared_w, shared_s,
+                           shared_wt, shared_wt_s, fwd_ws, dout, du, dgate_w, d_routed_w, d_shared_w, dtopk_w, ws,
+                           stream)
     ev = None
     if stage_events is not None:
         arr = (ctypes.c_void_p * 9)(*stage_events)
         ev = ctypes.cast(arr, ctypes.c_void_p)
-    return _check(lib().moe_backward_timed(ctypes.byref(shape), _ptr(u), _ptr(gate_w), rw[0] if rw else None,
-                                           rt[0] if rt else None, sw[0] if sw else None, st[0] if st else None,
-                                           _ptr(fwd_ws), _nbytes(fwd_ws), _ptr(dout), _ptr(du), _ptr(dgate_w),
-                                           dr[0] if dr else None, ds[0] if ds else None, _ptr(dtopk_w), _ptr(ws),
-                                           _nbytes(ws), _stream(stream), ev))
+    rc = lib().moe_backward_timed(*args, ev)
+    del keep
+    return _check(rc)
 
 
 def moe_quantize_1x128(rows, cols, x_dtype, x, q, s, stream=None):
     return _check(lib().moe_quantize_1x128(rows, cols, x_dtype, _ptr(x), _ptr(q), _ptr(s), _stream(stream)))
+
+
+def moe_quantize_128x1(n_seg, offsets, max_rows, cols, x_dtype, x, x_s, gather, q, s, block_base, stream=None):
+    return _check(lib().moe_quantize_128x1(n_seg, _ptr(offsets), max_rows, cols, x_dtype, _ptr(x), _ptr(x_s),
+                                           _ptr(gather), _ptr(q), _ptr(s), _ptr(block_base), _stream(stream)))
 
 
 def moe_quantize_weights_128x128(nmat, rows, cols, w_dtype, w, q, s, stream=None):

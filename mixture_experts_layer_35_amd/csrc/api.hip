@@ -470,86 +470,134 @@ int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, con
     return MOE_OK;
 }
 
-// backward workspace: dy [TK][d], dg [TK], dz [TK], dh [R][I], dab [R][2I], dx [R][d] (R = TK + T*Ns)
+// backward workspace: dy [TK][d], dg [TK], dz [TK], dh [R][I], dab [R][2I], dx [R][d] (R = TK + T*Ns);
+// for e4m3 layers also the 1 x 128 tiles of dy, dO and [dA dB] (Dgrad inputs), the 128 x 1 tiles
+// of the weight-gradient operands and the experts' run bases
 struct BwdLayout {
-    size_t dy, dg, dz, dh, dab, dx, total;
+    size_t dy, dg, dz, dh, dab, dx;
+    size_t dyq, dys, doq, dos, abq, abs_;                       // Dgrad inputs
+    size_t bbase, p1q, p1s, q1q, q1s, p2q, p2s, q2q, q2s;      // routed Wgrad operands (down, gate/up)
+    size_t sp1q, sp1s, sq1q, sq1s, sp2q, sp2s, sq2q, sq2s;      // shared Wgrad operands
+    size_t total;
+    int64_t rblk, sblk;                                         // run bounds: routed (all experts), one T-row segment
 };
 
 static BwdLayout bwd_layout(const moe_shape *s) {
     BwdLayout L{};
-    const int64_t T = s->T, TK = T * s->topk, R = TK + T * s->n_shared;
+    const int64_t T = s->T, TK = T * s->topk, Ns = s->n_shared, R = TK + T * Ns;
+    const int64_t d = s->d, I = s->inter;
     const int a = esize(s->act_dtype);
     size_t o = 0;
     auto take = [&](size_t bytes) { size_t r = o; o += align256(bytes); return r; };
-    L.dy = take((size_t)TK * s->d * a);
+    L.dy = take((size_t)TK * d * a);
     L.dg = take((size_t)TK * 4);
     L.dz = take((size_t)TK * 4);
-    L.dh = take((size_t)R * s->inter * a);
-    L.dab = take((size_t)R * 2 * s->inter * a);
-    L.dx = take((size_t)R * s->d * a);
+    L.dh = take((size_t)R * I * a);
+    L.dab = take((size_t)R * 2 * I * a);
+    L.dx = take((size_t)R * d * a);
+    if (s->w_dtype == MOE_E4M3) {
+        L.rblk = TK / 128 + s->n_routed + 1;
+        L.sblk = (T + 127) / 128;
+        L.dyq = take((size_t)TK * d);
+        L.dys = take((size_t)TK * (d / 128) * 4);
+        L.doq = take((size_t)T * d);
+        L.dos = take((size_t)T * (d / 128) * 4);
+        L.abq = take((size_t)R * 2 * I);
+        L.abs_ = take((size_t)R * (2 * I / 128) * 4);
+        L.bbase = take((size_t)(s->n_routed + 1) * 4);
+        L.p1q = take((size_t)TK * d);
+        L.p1s = take((size_t)L.rblk * d * 4);
+        L.q1q = take((size_t)TK * I);
+        L.q1s = take((size_t)L.rblk * I * 4);
+        L.p2q = take((size_t)TK * 2 * I);
+        L.p2s = take((size_t)L.rblk * 2 * I * 4);
+        L.q2q = take((size_t)TK * d);
+        L.q2s = take((size_t)L.rblk * d * 4);
+        L.sp1q = take((size_t)T * d);
+        L.sp1s = take((size_t)L.sblk * d * 4);
+        L.sq1q = take((size_t)Ns * T * I);
+        L.sq1s = take((size_t)Ns * L.sblk * I * 4);
+        L.sp2q = take((size_t)Ns * T * 2 * I);
+        L.sp2s = take((size_t)Ns * L.sblk * 2 * I * 4);
+        L.sq2q = take((size_t)T * d);
+        L.sq2s = take((size_t)L.sblk * d * 4);
+    }
     L.total = o;
     return L;
 }
 
-static int check_bwd_shape(const moe_shape *s, const char *fn) {
-    int rc = check_shape(s, fn);
-    if (rc) return rc;
-    if (s->w_dtype == MOE_E4M3) return fail(MOE_ERR_UNSUPPORTED, "%s: the backward runs on fp32 / bf16 layers", fn);
-    return MOE_OK;
-}
-
 size_t moe_backward_workspace_bytes(const moe_shape *s) {
-    if (check_bwd_shape(s, "moe_backward_workspace_bytes") != MOE_OK) return 0;
+    if (check_shape(s, "moe_backward_workspace_bytes") != MOE_OK) return 0;
     return bwd_layout(s).total;
 }
 
-int moe_transpose_expert_weights(const moe_shape *s, int32_t n, const void *w_gate, const void *w_up,
-                                 const void *w_down, void *w_down_t, void *w_gate_up_t, void *stream) {
+int moe_transpose_expert_weights(const moe_shape *s, int32_t n, const void *const *w, const float *const *w_s,
+                                 void *const *wt, float *const *wt_s, void *stream) {
     const char *fn = "moe_transpose_expert_weights";
-    int rc = check_bwd_shape(s, fn);
+    int rc = check_shape(s, fn);
     if (rc) return rc;
     if (n < 0) return fail(MOE_ERR_INVALID_ARG, "%s: n < 0", fn);
     if (n == 0) return MOE_OK;
-    NEED(w_gate);
-    NEED(w_up);
-    NEED(w_down);
-    NEED(w_down_t);
-    NEED(w_gate_up_t);
+    NEED(w);
+    NEED(wt);
+    if (!w[0] || !w[1] || !w[2] || !wt[0] || !wt[1])
+        return fail(MOE_ERR_INVALID_ARG, "%s: weight entries must not be NULL", fn);
+    const bool fp8 = s->w_dtype == MOE_E4M3;
+    if (fp8) {
+        NEED(w_s);
+        NEED(wt_s);
+        if (!w_s[0] || !w_s[1] || !w_s[2] || !wt_s[0] || !wt_s[1])
+            return fail(MOE_ERR_INVALID_ARG, "%s: e4m3 scale entries must not be NULL", fn);
+    }
     const int dt = dt_of(s->w_dtype), d = s->d, I = s->inter;
     hipStream_t st = (hipStream_t)stream;
-    HIPCHK(launch_transpose(dt, w_down, n, d, I, w_down_t, d, 0, st));        // [n][d][I] -> [n][I][d]
-    HIPCHK(launch_transpose(dt, w_gate, n, I, d, w_gate_up_t, 2 * I, 0, st)); // [n][I][d] -> [n][d][0:I]
-    HIPCHK(launch_transpose(dt, w_up, n, I, d, w_gate_up_t, 2 * I, I, st));   // [n][I][d] -> [n][d][I:2I]
+    HIPCHK(launch_transpose(dt, w[2], n, d, I, wt[0], d, 0, st));        // [n][d][I] -> [n][I][d]
+    HIPCHK(launch_transpose(dt, w[0], n, I, d, wt[1], 2 * I, 0, st));    // [n][I][d] -> [n][d][0:I]
+    HIPCHK(launch_transpose(dt, w[1], n, I, d, wt[1], 2 * I, I, st));    // [n][I][d] -> [n][d][I:2I]
+    if (fp8) {
+        // 128 x 128 block scales follow their blocks
+        const int db = d / 128, ib = I / 128;
+        HIPCHK(launch_transpose_scales(w_s[2], n, db, ib, wt_s[0], db, 0, st));
+        HIPCHK(launch_transpose_scales(w_s[0], n, ib, db, wt_s[1], 2 * ib, 0, st));
+        HIPCHK(launch_transpose_scales(w_s[1], n, ib, db, wt_s[1], 2 * ib, ib, st));
+    }
     return MOE_OK;
 }
 
+static bool all3(const void *const *p) { return p && p[0] && p[1] && p[2]; }
+static bool all2(const void *const *p) { return p && p[0] && p[1]; }
+
 static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, const void *const *routed_w,
-                         const void *const *routed_wt, const void *const *shared_w, const void *const *shared_wt,
-                         const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du, float *dgate_w,
-                         void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes,
-                         void *stream, void *const *ev) {
+                         const float *const *routed_s, const void *const *routed_wt,
+                         const float *const *routed_wt_s, const void *const *shared_w, const float *const *shared_s,
+                         const void *const *shared_wt, const float *const *shared_wt_s, const void *fwd_ws,
+                         size_t fwd_ws_bytes, const void *dout, void *du, float *dgate_w, void *const *d_routed_w,
+                         void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes, void *stream,
+                         void *const *ev) {
     const char *fn = "moe_backward";
-    int rc = check_bwd_shape(s, fn);
+    int rc = check_shape(s, fn);
     if (rc) return rc;
     if (s->T == 0) return MOE_OK;
     NEED(u);
     NEED(gate_w);
-    NEED(routed_w);
-    NEED(routed_wt);
     NEED(fwd_ws);
     NEED(dout);
     NEED(du);
-    if (!routed_w[0] || !routed_w[1] || !routed_w[2] || !routed_wt[0] || !routed_wt[1])
+    const bool fp8 = s->w_dtype == MOE_E4M3;
+    const int Ns = s->n_shared;
+    if (!all3(routed_w) || !all2(routed_wt))
         return fail(MOE_ERR_INVALID_ARG, "%s: routed weight entries must not be NULL", fn);
-    if (s->n_shared > 0) {
-        NEED(shared_w);
-        NEED(shared_wt);
-        if (!shared_w[0] || !shared_w[1] || !shared_w[2] || !shared_wt[0] || !shared_wt[1])
+    if (fp8 && (!all3((const void *const *)routed_s) || !all2((const void *const *)routed_wt_s)))
+        return fail(MOE_ERR_INVALID_ARG, "%s: e4m3 routed scale entries must not be NULL", fn);
+    if (Ns > 0) {
+        if (!all3(shared_w) || !all2(shared_wt))
             return fail(MOE_ERR_INVALID_ARG, "%s: shared weight entries must not be NULL", fn);
+        if (fp8 && (!all3((const void *const *)shared_s) || !all2((const void *const *)shared_wt_s)))
+            return fail(MOE_ERR_INVALID_ARG, "%s: e4m3 shared scale entries must not be NULL", fn);
     }
-    if (d_routed_w && (!d_routed_w[0] || !d_routed_w[1] || !d_routed_w[2]))
+    if (d_routed_w && !all3((const void *const *)d_routed_w))
         return fail(MOE_ERR_INVALID_ARG, "%s: d_routed_w entries must not be NULL", fn);
-    if (s->n_shared > 0 && d_shared_w && (!d_shared_w[0] || !d_shared_w[1] || !d_shared_w[2]))
+    if (Ns > 0 && d_shared_w && !all3((const void *const *)d_shared_w))
         return fail(MOE_ERR_INVALID_ARG, "%s: d_shared_w entries must not be NULL", fn);
     const FwdLayout F = fwd_layout(s);
     if ((uintptr_t)fwd_ws & 255) return fail(MOE_ERR_INVALID_ARG, "%s: forward workspace must be 256-byte aligned", fn);
@@ -561,9 +609,9 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
     if (rc) return rc;
 
     hipStream_t st = (hipStream_t)stream;
-    const int dt = dt_of(s->act_dtype);
+    const int dt = dt_of(s->act_dtype), wdt = dt_of(s->w_dtype);
     const int64_t T = s->T, TK = T * s->topk;
-    const int d = s->d, I = s->inter, Ns = s->n_shared, a_sz = esize(s->act_dtype);
+    const int d = s->d, I = s->inter, a_sz = esize(s->act_dtype);
     const char *Fw = (const char *)fwd_ws;
     char *W = (char *)ws;
     const float *scores = (const float *)(Fw + F.scores);
@@ -576,6 +624,8 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
     float *dg = dtopk_w ? dtopk_w : (float *)(W + L.dg);
     float *dz = (float *)(W + L.dz);
     char *dh_s = dh + (size_t)TK * I * a_sz, *dab_s = dab + (size_t)TK * 2 * I * a_sz, *dx_s = dx + (size_t)TK * d * a_sz;
+    auto U8 = [&](size_t o) { return (uint8_t *)(W + o); };
+    auto F32 = [&](size_t o) { return (float *)(W + o); };
 
     auto mark = [&](int i) -> hipError_t {
         return (ev && ev[i]) ? hipEventRecord((hipEvent_t)ev[i], st) : hipSuccess;
@@ -583,20 +633,29 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
     HIPCHK(mark(0));
     // 1. combine: dY rows and gate gradients
     HIPCHK(launch_bwd_combine(dt, dout, Fw + F.yperm, inv, tw, T, d, s->topk, dy, dg, st));
+    if (fp8) {
+        // Dgrad inputs in 1 x 128 tiles along their reduction (d)
+        HIPCHK(launch_quant_rows(dt, dy, nullptr, TK, d, U8(L.dyq), F32(L.dys), st));
+        if (Ns) HIPCHK(launch_quant_rows(dt, dout, nullptr, T, d, U8(L.doq), F32(L.dos), st));
+    }
     HIPCHK(mark(1));
     // 2. dH = dY . W_down (transposed copies [n][I][d])
     FfnProblem p[2] = {}, q[2] = {};
     p[0].n_exp = s->n_routed;
     p[0].offsets = offsets;
-    p[0].x = dy;
+    p[0].x = fp8 ? (const void *)U8(L.dyq) : dy;
+    p[0].xs = fp8 ? F32(L.dys) : nullptr;
     p[0].w0 = routed_wt[0];
+    p[0].s0 = fp8 ? routed_wt_s[0] : nullptr;
     p[0].out = dh;
     if (Ns) {
         p[1].n_exp = Ns;
         p[1].rows_fixed = T;
         p[1].x_local = 1;
-        p[1].x = dout;
+        p[1].x = fp8 ? (const void *)U8(L.doq) : dout;
+        p[1].xs = fp8 ? F32(L.dos) : nullptr;
         p[1].w0 = shared_wt[0];
+        p[1].s0 = fp8 ? shared_wt_s[0] : nullptr;
         p[1].out = dh_s;
     }
     FfnArgs fa{};
@@ -604,15 +663,20 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
     fa.K = d;
     fa.F = I;
     for (int i = 0; i < fa.nprob; ++i) fa.p[i] = p[fa.nprob - 1 - i];
-    HIPCHK(launch_ffn(dt, FFN_BWD_DH, fa, st));
+    HIPCHK(launch_ffn(wdt, FFN_BWD_DH, fa, st));
     HIPCHK(mark(2));
-    // 3. gate/up recomputed from u; SwiGLU gradient against dH -> [dA | dB]
+    // 3. gate/up recomputed from u (e4m3: the forward's 1 x 128 tiles of u); SwiGLU gradient -> [dA | dB]
+    const void *xin = fp8 ? (const void *)(Fw + F.uq) : u;
+    const float *xsin = fp8 ? (const float *)(Fw + F.us) : nullptr;
     q[0].n_exp = s->n_routed;
     q[0].offsets = offsets;
     q[0].gather = perm;
-    q[0].x = u;
+    q[0].x = xin;
+    q[0].xs = xsin;
     q[0].w0 = routed_w[0];
     q[0].w1 = routed_w[1];
+    q[0].s0 = fp8 ? routed_s[0] : nullptr;
+    q[0].s1 = fp8 ? routed_s[1] : nullptr;
     q[0].dh = dh;
     q[0].out = dab;
     q[0].out_ld = 2 * I;
@@ -620,34 +684,42 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
         q[1].n_exp = Ns;
         q[1].rows_fixed = T;
         q[1].x_local = 1;
-        q[1].x = u;
+        q[1].x = xin;
+        q[1].xs = xsin;
         q[1].w0 = shared_w[0];
         q[1].w1 = shared_w[1];
+        q[1].s0 = fp8 ? shared_s[0] : nullptr;
+        q[1].s1 = fp8 ? shared_s[1] : nullptr;
         q[1].dh = dh_s;
         q[1].out = dab_s;
         q[1].out_ld = 2 * I;
     }
     for (int i = 0; i < fa.nprob; ++i) fa.p[i] = q[fa.nprob - 1 - i];
-    HIPCHK(launch_ffn(dt, FFN_GATEUP_BWD, fa, st));
+    HIPCHK(launch_ffn(wdt, FFN_GATEUP_BWD, fa, st));
+    if (fp8) HIPCHK(launch_quant_rows(dt, dab, nullptr, TK + T * Ns, 2 * I, U8(L.abq), F32(L.abs_), st));
     HIPCHK(mark(3));
     // 4. dX = [dA | dB] . [W_gate ; W_up] (transposed copies [n][d][2I])
     FfnProblem r[2] = {};
     r[0].n_exp = s->n_routed;
     r[0].offsets = offsets;
-    r[0].x = dab;
+    r[0].x = fp8 ? (const void *)U8(L.abq) : dab;
+    r[0].xs = fp8 ? F32(L.abs_) : nullptr;
     r[0].w0 = routed_wt[1];
+    r[0].s0 = fp8 ? routed_wt_s[1] : nullptr;
     r[0].out = dx;
     if (Ns) {
         r[1].n_exp = Ns;
         r[1].rows_fixed = T;
-        r[1].x = dab_s;
+        r[1].x = fp8 ? (const void *)(U8(L.abq) + (size_t)TK * 2 * I) : dab_s;
+        r[1].xs = fp8 ? F32(L.abs_) + (size_t)TK * (2 * I / 128) : nullptr;
         r[1].w0 = shared_wt[1];
+        r[1].s0 = fp8 ? shared_wt_s[1] : nullptr;
         r[1].out = dx_s;
     }
     fa.K = 2 * I;
     fa.F = d;
     for (int i = 0; i < fa.nprob; ++i) fa.p[i] = r[fa.nprob - 1 - i];
-    HIPCHK(launch_ffn(dt, FFN_BWD_DX, fa, st));
+    HIPCHK(launch_ffn(wdt, FFN_BWD_DX, fa, st));
     HIPCHK(mark(4));
     // 5. du: dispatch sum and router chain; dz per row
     HIPCHK(launch_bwd_token(dt, dx, dx_s, Ns, inv, idx, scores, dg, gate_w, T, d, s->n_routed, s->topk,
@@ -656,10 +728,29 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
     // 6. centroid gradient
     if (dgate_w) HIPCHK(launch_dgate(dt, u, perm, offsets, dz, s->n_routed, d, dgate_w, st));
     HIPCHK(mark(6));
-    // 7. weight gradients: down (dY rows x H rows), then gate/up ([dA | dB] rows x gathered u rows)
+    // 7. weight gradients: down (dY rows x H rows), then gate/up ([dA | dB] rows x gathered u rows);
+    // e4m3: both operands re-tiled 128 x 1 along the expert's rows first
     if (d_routed_w || (Ns && d_shared_w)) {
         // shared experts first: their long reductions start early, spread over every XCD
         const int64_t hint = (TK + s->n_routed - 1) / s->n_routed;
+        int32_t *bbase = fp8 ? (int32_t *)(W + L.bbase) : nullptr;
+        const uint8_t *hq = (const uint8_t *)(Fw + F.h), *hsq = (const uint8_t *)(Fw + F.hsh);
+        const float *hs = (const float *)(Fw + F.hs), *hss = (const float *)(Fw + F.hshs);
+        if (fp8) {
+            HIPCHK(launch_block_base(offsets, s->n_routed, bbase, st));
+            if (d_routed_w) {
+                HIPCHK(launch_quant_cols(DT_BF16, dy, nullptr, nullptr, offsets, bbase, 0, s->n_routed, L.rblk, d,
+                                         U8(L.p1q), F32(L.p1s), st));
+                HIPCHK(launch_quant_cols(DT_E4M3, hq, hs, nullptr, offsets, bbase, 0, s->n_routed, L.rblk, I,
+                                         U8(L.q1q), F32(L.q1s), st));
+            }
+            if (Ns && d_shared_w) {
+                HIPCHK(launch_quant_cols(DT_BF16, dout, nullptr, nullptr, nullptr, nullptr, T, 1, L.sblk, d,
+                                         U8(L.sp1q), F32(L.sp1s), st));
+                HIPCHK(launch_quant_cols(DT_E4M3, hsq, hss, nullptr, nullptr, nullptr, T, Ns, Ns * L.sblk, I,
+                                         U8(L.sq1q), F32(L.sq1s), st));
+            }
+        }
         WgradArgs wa{};
         int np = 0;
         if (Ns && d_shared_w) {
@@ -668,9 +759,11 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
             w.rows_fixed = T;
             w.rows_hint = T;
             w.p_local = 1;
-            w.P = dout;
+            w.P = fp8 ? (const void *)U8(L.sp1q) : dout;
+            w.Ps = fp8 ? F32(L.sp1s) : nullptr;
             w.P_ld = d;
-            w.Q = Fw + F.hsh;
+            w.Q = fp8 ? (const void *)U8(L.sq1q) : (const void *)hsq;
+            w.Qs = fp8 ? F32(L.sq1s) : nullptr;
             w.Q_ld = I;
             w.Pdim = d;
             w.Qdim = I;
@@ -681,10 +774,13 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
             WgradProblem &w = wa.p[np++];
             w.n_exp = s->n_routed;
             w.offsets = offsets;
+            w.bbase = bbase;
             w.rows_hint = hint;
-            w.P = dy;
+            w.P = fp8 ? (const void *)U8(L.p1q) : dy;
+            w.Ps = fp8 ? F32(L.p1s) : nullptr;
             w.P_ld = d;
-            w.Q = Fw + F.h;
+            w.Q = fp8 ? (const void *)U8(L.q1q) : (const void *)hq;
+            w.Qs = fp8 ? F32(L.q1s) : nullptr;
             w.Q_ld = I;
             w.Pdim = d;
             w.Qdim = I;
@@ -692,8 +788,22 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
             w.out0 = d_routed_w[2];
         }
         wa.nprob = np;
-        HIPCHK(launch_wgrad(dt, 0, wa, st));
+        HIPCHK(launch_wgrad(wdt, 0, wa, st));
         HIPCHK(mark(7));
+        if (fp8) {
+            if (d_routed_w) {
+                HIPCHK(launch_quant_cols(DT_BF16, dab, nullptr, nullptr, offsets, bbase, 0, s->n_routed, L.rblk,
+                                         2 * I, U8(L.p2q), F32(L.p2s), st));
+                HIPCHK(launch_quant_cols(DT_E4M3, Fw + F.uq, (const float *)(Fw + F.us), perm, offsets, bbase, 0,
+                                         s->n_routed, L.rblk, d, U8(L.q2q), F32(L.q2s), st));
+            }
+            if (Ns && d_shared_w) {
+                HIPCHK(launch_quant_cols(DT_BF16, dab_s, nullptr, nullptr, nullptr, nullptr, T, Ns, Ns * L.sblk,
+                                         2 * I, U8(L.sp2q), F32(L.sp2s), st));
+                HIPCHK(launch_quant_cols(DT_E4M3, Fw + F.uq, (const float *)(Fw + F.us), nullptr, nullptr, nullptr,
+                                         T, 1, L.sblk, d, U8(L.sq2q), F32(L.sq2s), st));
+            }
+        }
         np = 0;
         if (Ns && d_shared_w) {
             WgradProblem &w = wa.p[np++];
@@ -702,9 +812,11 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
             w.rows_fixed = T;
             w.rows_hint = T;
             w.q_local = 1;
-            w.P = dab_s;
+            w.P = fp8 ? (const void *)U8(L.sp2q) : dab_s;
+            w.Ps = fp8 ? F32(L.sp2s) : nullptr;
             w.P_ld = 2 * I;
-            w.Q = u;
+            w.Q = fp8 ? (const void *)U8(L.sq2q) : u;
+            w.Qs = fp8 ? F32(L.sq2s) : nullptr;
             w.Q_ld = d;
             w.Pdim = 2 * I;
             w.Qdim = d;
@@ -717,12 +829,15 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
             w = WgradProblem{};
             w.n_exp = s->n_routed;
             w.offsets = offsets;
+            w.bbase = bbase;
             w.rows_hint = hint;
-            w.P = dab;
+            w.P = fp8 ? (const void *)U8(L.p2q) : dab;
+            w.Ps = fp8 ? F32(L.p2s) : nullptr;
             w.P_ld = 2 * I;
-            w.Q = u;
+            w.Q = fp8 ? (const void *)U8(L.q2q) : u;
+            w.Qs = fp8 ? F32(L.q2s) : nullptr;
             w.Q_ld = d;
-            w.q_gather = perm;
+            w.q_gather = fp8 ? nullptr : perm;   // e4m3: the 128 x 1 copy is already gathered
             w.Pdim = 2 * I;
             w.Qdim = d;
             w.split = I;
@@ -730,7 +845,7 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
             w.out1 = d_routed_w[1];
         }
         wa.nprob = np;
-        HIPCHK(launch_wgrad(dt, 1, wa, st));
+        HIPCHK(launch_wgrad(wdt, 1, wa, st));
     } else {
         HIPCHK(mark(7));
     }
@@ -739,21 +854,25 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
 }
 
 int moe_backward(const moe_shape *s, const void *u, const void *gate_w, const void *const *routed_w,
-                 const void *const *routed_wt, const void *const *shared_w, const void *const *shared_wt,
-                 const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du, float *dgate_w,
-                 void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes,
-                 void *stream) {
-    return backward_impl(s, u, gate_w, routed_w, routed_wt, shared_w, shared_wt, fwd_ws, fwd_ws_bytes, dout, du,
-                         dgate_w, d_routed_w, d_shared_w, dtopk_w, ws, ws_bytes, stream, nullptr);
+                 const float *const *routed_s, const void *const *routed_wt, const float *const *routed_wt_s,
+                 const void *const *shared_w, const float *const *shared_s, const void *const *shared_wt,
+                 const float *const *shared_wt_s, const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du,
+                 float *dgate_w, void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws,
+                 size_t ws_bytes, void *stream) {
+    return backward_impl(s, u, gate_w, routed_w, routed_s, routed_wt, routed_wt_s, shared_w, shared_s, shared_wt,
+                         shared_wt_s, fwd_ws, fwd_ws_bytes, dout, du, dgate_w, d_routed_w, d_shared_w, dtopk_w, ws,
+                         ws_bytes, stream, nullptr);
 }
 
 int moe_backward_timed(const moe_shape *s, const void *u, const void *gate_w, const void *const *routed_w,
-                       const void *const *routed_wt, const void *const *shared_w, const void *const *shared_wt,
-                       const void *fwd_ws, size_t fwd_ws_bytes, const void *dout, void *du, float *dgate_w,
-                       void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w, void *ws, size_t ws_bytes,
-                       void *stream, void *const *stage_events) {
-    return backward_impl(s, u, gate_w, routed_w, routed_wt, shared_w, shared_wt, fwd_ws, fwd_ws_bytes, dout, du,
-                         dgate_w, d_routed_w, d_shared_w, dtopk_w, ws, ws_bytes, stream, stage_events);
+                       const float *const *routed_s, const void *const *routed_wt, const float *const *routed_wt_s,
+                       const void *const *shared_w, const float *const *shared_s, const void *const *shared_wt,
+                       const float *const *shared_wt_s, const void *fwd_ws, size_t fwd_ws_bytes, const void *dout,
+                       void *du, float *dgate_w, void *const *d_routed_w, void *const *d_shared_w, float *dtopk_w,
+                       void *ws, size_t ws_bytes, void *stream, void *const *stage_events) {
+    return backward_impl(s, u, gate_w, routed_w, routed_s, routed_wt, routed_wt_s, shared_w, shared_s, shared_wt,
+                         shared_wt_s, fwd_ws, fwd_ws_bytes, dout, du, dgate_w, d_routed_w, d_shared_w, dtopk_w, ws,
+                         ws_bytes, stream, stage_events);
 }
 
 size_t moe_seq_balance_workspace_bytes(const moe_shape *s, int64_t seq_len) {
@@ -820,6 +939,28 @@ int moe_quantize_weights_128x128(int64_t nmat, int32_t rows, int32_t cols, int32
     NEED(q);
     NEED(sc);
     HIPCHK(launch_quant_blocks(dt_of(w_dtype), w, nmat, rows, cols, q, sc, (hipStream_t)stream));
+    return MOE_OK;
+}
+
+int moe_quantize_128x1(int32_t n_seg, const int32_t *offsets, int64_t max_rows, int32_t cols, int32_t x_dtype,
+                       const void *x, const float *x_s, const int32_t *gather, uint8_t *q, float *sc,
+                       int32_t *block_base, void *stream) {
+    const char *fn = "moe_quantize_128x1";
+    if (n_seg < 0 || max_rows < 0 || cols <= 0) return fail(MOE_ERR_INVALID_ARG, "%s: bad size", fn);
+    if (cols % 128) return fail(MOE_ERR_UNSUPPORTED, "%s: cols = %d is not a multiple of 128", fn, cols);
+    if (x_dtype != MOE_BF16 && x_dtype != MOE_E4M3) return fail(MOE_ERR_UNSUPPORTED, "%s: x_dtype %d", fn, x_dtype);
+    if (n_seg == 0) return MOE_OK;
+    NEED(offsets);
+    NEED(x);
+    if (x_dtype == MOE_E4M3) NEED(x_s);
+    NEED(q);
+    NEED(sc);
+    NEED(block_base);
+    const int64_t max_blocks = max_rows / 128 + n_seg;
+    if (max_blocks >= (1ll << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: too many runs for one call", fn);
+    const hipStream_t s = (hipStream_t)stream;
+    HIPCHK(launch_block_base(offsets, n_seg, block_base, s));
+    HIPCHK(launch_quant_cols(dt_of(x_dtype), x, x_s, gather, offsets, block_base, 0, n_seg, max_blocks, cols, q, sc, s));
     return MOE_OK;
 }
 

@@ -62,7 +62,8 @@ constexpr int BW_NT = 256;
 template <int ESZ>
 __global__ __launch_bounds__(256) void transpose_kernel(const char *__restrict__ src, int rows, int cols,
                                                        char *__restrict__ dst, int dst_ld, int col0) {
-    typedef typename std::conditional<ESZ == 2, uint16_t, uint32_t>::type E;
+    typedef typename std::conditional<ESZ == 1, uint8_t,
+                                      typename std::conditional<ESZ == 2, uint16_t, uint32_t>::type>::type E;
     __shared__ E tile[64][65];
     const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
     const int64_t tiles_c = cols / 64, tiles_per = (int64_t)(rows / 64) * tiles_c;
@@ -692,6 +693,262 @@ __global__ __launch_bounds__(WGB_NT) void wgrad_bf16_kernel(const WgradArgs a, i
     }
 }
 
+// ---- FP8 backward helpers ------------------------------------------------------
+// Block-scale grids of transposed weights: dst[m][c][col0 + r] = src[m][r][c].
+__global__ __launch_bounds__(256) void scale_transpose_kernel(const float *__restrict__ src, int64_t nmat, int rows,
+                                                              int cols, float *__restrict__ dst, int dst_ld,
+                                                              int col0) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= nmat * rows * (int64_t)cols) return;
+    const int64_t m = i / ((int64_t)rows * cols);
+    const int rc = (int)(i - m * rows * (int64_t)cols), r = rc / cols, c = rc - r * cols;
+    dst[(m * cols + c) * dst_ld + col0 + r] = src[i];
+}
+
+// bbase[e] = sum over e' < e of ceil(len(e') / 128): the first 128-row run of expert e
+// among all experts' runs (bbase[n] = the total).
+__global__ void block_base_kernel(const int32_t *__restrict__ offsets, int n, int32_t *__restrict__ bbase) {
+    if (threadIdx.x != 0) return;
+    int32_t acc = 0;
+    for (int e = 0; e < n; ++e) {
+        bbase[e] = acc;
+        acc += (offsets[e + 1] - offsets[e] + 127) / 128;
+    }
+    bbase[n] = acc;
+}
+
+// 128 x 1 tiles along the rows of segments (the FP8 weight-gradient operands):
+// workgroup (b, chunk) takes 128-row run b and 256 columns.  Segment e owns
+// rows offsets[e] .. offsets[e+1] (or e*seg_rows .. +seg_rows); its runs start
+// at its first row and are numbered from bbase[e] (or e*ceil(seg_rows/128)).
+// List row r reads source row gather[r] (or r), bf16, or e4m3 with 1 x 128
+// scales (decoded to fp32 first).  Scale = amax / 448 (1 for an all-zero
+// column), codes = e4m3(clamp(v / scale)), nearest even.
+template <int IN>
+__global__ __launch_bounds__(256) void quant_cols_kernel(const void *__restrict__ src, const float *__restrict__ src_s,
+                                                         const int32_t *__restrict__ gather,
+                                                         const int32_t *__restrict__ offsets,
+                                                         const int32_t *__restrict__ bbase, int64_t seg_rows,
+                                                         int n_seg, int cols, uint8_t *__restrict__ q,
+                                                         float *__restrict__ sc) {
+    const int64_t b = blockIdx.x;
+    int64_t r0, r1;
+    if (offsets) {
+        if (b >= bbase[n_seg]) return;
+        int lo = 0, hi = n_seg - 1;   // the segment whose runs include b
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (bbase[mid] <= b) lo = mid;
+            else hi = mid - 1;
+        }
+        r0 = offsets[lo] + (b - bbase[lo]) * 128;
+        r1 = min(r0 + 128, (int64_t)offsets[lo + 1]);
+    } else {
+        const int64_t nbs = (seg_rows + 127) / 128;
+        if (b >= n_seg * nbs) return;
+        const int64_t e = b / nbs, j = b - e * nbs;
+        r0 = e * seg_rows + j * 128;
+        r1 = min(r0 + 128, (e + 1) * seg_rows);
+    }
+    const int c = blockIdx.y * 256 + threadIdx.x;
+    if (c >= cols) return;
+    auto load = [&](int64_t r) -> float {
+        const int64_t xr = gather ? (int64_t)gather[r] : r;
+        if (IN == DT_E4M3) {
+            const uint8_t code = ((const uint8_t *)src)[xr * cols + c];
+            return __builtin_amdgcn_cvt_f32_fp8((int)code, 0) * src_s[xr * (cols / 128) + c / 128];
+        }
+        return __uint_as_float((uint32_t)((const uint16_t *)src)[xr * cols + c] << 16);
+    };
+    float amax = 0.0f;
+    for (int64_t r = r0; r < r1; ++r) amax = fmaxf(amax, fabsf(load(r)));
+    const float scale = quant_scale(amax);
+    sc[b * cols + c] = scale;
+    for (int64_t r = r0; r < r1; ++r)
+        q[r * cols + c] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(load(r) / scale), 0.0f, 0, false) & 0xFF);
+}
+
+// ---- FP8 weight gradient -----------------------------------------------------------
+// C[p][q] = sum over an expert's 128-row runs of (sum_r Pq[r][p] Qq[r][q]) * sP[run][p] * sQ[run][q],
+// with both operands in 128 x 1 tiles along the rows (codes Pq, Qq, scales sP, sQ).  The
+// structure is the bf16 kernel's: one workgroup per (expert, 128-wide p tile, q group),
+// two producer waves filling an LDS ring with direct loads, four MFMA waves.  A step is
+// one 128-row run, i.e. one 16x16x128 e4m3 MFMA per 16 x 16 output block; its fp32
+// partial is scaled by the run's two column scales and added.  Fragments come from the
+// 8-bit LDS transpose read: in each 16-lane group, lane 8a+b receives byte b of the
+// 8-byte pieces addressed by lanes 2j+a (j = 0..7); four reads give a lane the 32
+// consecutive rows of its operand.  Staged rows are 128 bytes; their 16-byte chunks sit
+// in slots XOR-permuted by wf8_h so the 32 rows of one read spread over all banks.
+constexpr int WF8_S = 3;                                   // ring stages
+constexpr int WF8_R = 128;                                 // rows per step (one quantisation run)
+constexpr int WF8_PB = WF8_R * WG_T;                       // one operand's codes of a step (16 KB)
+constexpr int WF8_STAGE = 2 * WF8_PB + 2 * WG_T * 4;       // + the run's P and Q column scales
+constexpr int WF8_LDS = WF8_S * WF8_STAGE;
+constexpr int WF8_NT = 384;
+
+__device__ __forceinline__ int wf8_h(int r) { return ((r >> 1) & 3) | (((r >> 5) & 1) << 2); }
+
+typedef int wf8_v2i __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ wf8_v2i lds_tr8(const char *p) {
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) wf8_v2i *)p);
+}
+
+template <int PASS>
+__global__ __launch_bounds__(WF8_NT) void wgrad_fp8_kernel(const WgradArgs a, int64_t nlead, int64_t ntiles) {
+    extern __shared__ __align__(1024) char wsm[];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const bool producer = wid >= 4;
+    const int wp = (wid >> 1) & 1, wq = wid & 1;
+    WgTile T;
+    if (!wg_decode(a, nlead, ntiles, blockIdx.x, T)) return;
+    const WgradProblem &Pr = T.pi ? a.p[1] : a.p[0];
+    const uint8_t *const Pp = (const uint8_t *)Pr.P, *const Qp = (const uint8_t *)Pr.Q;
+    const float *const Ps = Pr.Ps, *const Qs = Pr.Qs;
+    const int64_t P_ld = Pr.P_ld, Q_ld = Pr.Q_ld;
+    const bool p_local = Pr.p_local != 0, q_local = Pr.q_local != 0;
+    const int Pdim = Pr.Pdim, Qdim = Pr.Qdim, split = Pr.split;
+    const int e = T.e, p0 = T.p0, qt0 = T.qt0, nq = T.nq;
+    const int64_t rb = Pr.offsets ? (int64_t)Pr.offsets[e] : (int64_t)e * Pr.rows_fixed;
+    const int M = (int)(Pr.offsets ? (int64_t)Pr.offsets[e + 1] - rb : Pr.rows_fixed);
+    const int nsteps = (M + WF8_R - 1) / WF8_R;
+    const int total = nq * nsteps;
+    // first 128-row run of this expert among the operand's runs
+    const int64_t bb = Pr.offsets ? (int64_t)Pr.bbase[e] : (int64_t)e * ((Pr.rows_fixed + 127) / 128);
+    const int64_t pbb = p_local ? 0 : bb, qbb = q_local ? 0 : bb;
+
+    if (producer) {
+        if (total == 0) return;
+        // instruction n (0..15) of an operand covers rows 8n .. 8n+7 of the step; producer k
+        // issues n = 2m + k.  This lane: row 8n + lane/8, slot lane%8 holding data chunk
+        // (lane%8) ^ h(row).  The run's scales: lanes 0-31 take P's 128, lanes 32-63 Q's.
+        const int k = wid - 4, drow = lane >> 3, pchunk = lane & 7;
+        const int64_t prb = p_local ? 0 : rb, qrb = q_local ? 0 : rb;
+        int yq = 0, ys = 0;
+        auto issue = [&](int y) {
+            char *slot = wsm + (y % WF8_S) * WF8_STAGE;
+            const int q0 = (qt0 + yq) * WG_T, r0 = ys * WF8_R;
+#pragma unroll
+            for (int m = 0; m < 8; ++m) {
+                const int n = 2 * m + k, kr = 8 * n + drow;
+                const int r = min(r0 + kr, M - 1);   // rows past the expert repeat its last (masked)
+                const int cofs = 16 * (pchunk ^ wf8_h(kr));
+                dma16(Pp + (prb + r) * P_ld + p0 + cofs, slot + n * 1024);
+                dma16(Qp + (qrb + r) * Q_ld + q0 + cofs, slot + WF8_PB + n * 1024);
+            }
+            if (k == 0) {
+                const float *src = lane < 32 ? Ps + (pbb + ys) * Pdim + p0 + 4 * lane
+                                             : Qs + (qbb + ys) * Qdim + q0 + 4 * (lane - 32);
+                dma16(src, slot + 2 * WF8_PB);
+            }
+            if (++ys == nsteps) { ys = 0; ++yq; }
+        };
+        const int nops = 16 + (k == 0 ? 1 : 0);
+        for (int y = 0; y < WF8_S - 1 && y < total; ++y) issue(y);
+        for (int x = 0; x < total; ++x) {
+            wait_vmcnt_dyn(nops * (min(x + WF8_S - 2, total - 1) - x));
+            cta_barrier();
+            if (x + WF8_S - 1 < total) issue(x + WF8_S - 1);
+        }
+        return;
+    }
+
+    const int split_rows = split < Pdim ? split : Pdim;
+    uint16_t *const out = (uint16_t *)(p0 < split ? Pr.out0 : Pr.out1);
+    const int prow0 = p0 < split ? p0 : p0 - split;
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+    auto store_tile = [&](int q0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int prow = prow0 + wp * 64 + j * 16 + (lane & 15);
+            uint16_t *orow = out + ((int64_t)e * split_rows + prow) * Qdim;
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                const float ya[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                const float yb[4] = {acc[i + 1][j][0], acc[i + 1][j][1], acc[i + 1][j][2], acc[i + 1][j][3]};
+                store_pair_bf16(orow, q0 + wq * 64 + i * 16, ya, yb, lane, Qdim);
+            }
+        }
+    };
+    if (total == 0) {
+        for (int q = 0; q < nq; ++q) store_tile((qt0 + q) * WG_T);
+        return;
+    }
+    // fragment reads: lane (group g, L = 2jj + aa) addresses row 32g + 8t + jj, bytes col0 + 8aa .. +7
+    const int g = lane >> 4, jj = (lane & 15) >> 1, aa = lane & 1;
+    int ofs[8][4];
+#pragma unroll
+    for (int f = 0; f < 8; ++f) {
+        const int col0 = f < 4 ? wq * 64 + f * 16 : wp * 64 + (f - 4) * 16;
+        const int base = f < 4 ? WF8_PB : 0;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int r = 32 * g + 8 * t + jj;
+            ofs[f][t] = base + r * WG_T + (((col0 >> 4) ^ wf8_h(r)) << 4) + 8 * aa;
+        }
+    }
+    const int vlast = M - (nsteps - 1) * WF8_R;
+    int qt = 0, st = 0, slot = 0;
+    for (int x = 0; x < total; ++x) {
+        cta_barrier();
+        const char *sb = wsm + slot * WF8_STAGE;
+        i32x8 fr[8];
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            wf8_v2i v[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) v[t] = lds_tr8(sb + ofs[f][t]);
+            fr[f] = i32x8{v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
+        }
+        if (st == nsteps - 1 && vlast < WF8_R) {
+            // rows past the expert: zero P's bytes (lane holds rows 32g .. 32g+31, low byte first)
+#pragma unroll
+            for (int f = 4; f < 8; ++f)
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    const int r = 32 * g + 4 * w;
+                    uint32_t m = 0;
+#pragma unroll
+                    for (int bt = 0; bt < 4; ++bt)
+                        if (r + bt < vlast) m |= 0xFFu << (8 * bt);
+                    fr[f][w] &= (int)m;
+                }
+        }
+        const float *scp = (const float *)(sb + 2 * WF8_PB), *scq = scp + WG_T;
+        f32x4 part[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                part[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fr[i], fr[4 + j], f32x4{0, 0, 0, 0}, 0,
+                                                                              0, 0, 127, 0, 127);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 sq = *(const f32x4 *)(scq + wq * 64 + i * 16 + 4 * (lane >> 4));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float sp = scp[wp * 64 + j * 16 + (lane & 15)];
+#pragma unroll
+                for (int v = 0; v < 4; ++v) acc[i][j][v] += part[i][j][v] * (sq[v] * sp);
+            }
+        }
+        slot = slot + 1 == WF8_S ? 0 : slot + 1;
+        if (++st == nsteps) {
+            store_tile((qt0 + qt) * WG_T);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0, 0, 0, 0};
+            st = 0;
+            ++qt;
+        }
+    }
+}
+
 }  // namespace
 
 hipError_t launch_transpose(int dt, const void *src, int64_t nmat, int rows, int cols, void *dst, int dst_ld, int col0,
@@ -700,8 +957,38 @@ hipError_t launch_transpose(int dt, const void *src, int64_t nmat, int rows, int
     if (blocks <= 0) return hipSuccess;
     if (dt == DT_F32)
         transpose_kernel<4><<<(unsigned)blocks, 256, 0, s>>>((const char *)src, rows, cols, (char *)dst, dst_ld, col0);
-    else
+    else if (dt == DT_BF16)
         transpose_kernel<2><<<(unsigned)blocks, 256, 0, s>>>((const char *)src, rows, cols, (char *)dst, dst_ld, col0);
+    else
+        transpose_kernel<1><<<(unsigned)blocks, 256, 0, s>>>((const char *)src, rows, cols, (char *)dst, dst_ld, col0);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose_scales(const float *src, int64_t nmat, int rows, int cols, float *dst, int dst_ld, int col0,
+                                   hipStream_t s) {
+    const int64_t n = nmat * rows * (int64_t)cols;
+    if (n <= 0) return hipSuccess;
+    scale_transpose_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(src, nmat, rows, cols, dst, dst_ld, col0);
+    return hipGetLastError();
+}
+
+hipError_t launch_block_base(const int32_t *offsets, int n, int32_t *bbase, hipStream_t s) {
+    block_base_kernel<<<1, 64, 0, s>>>(offsets, n, bbase);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_cols(int in_dt, const void *src, const float *src_s, const int32_t *gather,
+                             const int32_t *offsets, const int32_t *bbase, int64_t seg_rows, int n_seg, int64_t max_blocks,
+                             int cols, uint8_t *q, float *sc, hipStream_t s) {
+    if (max_blocks <= 0 || n_seg <= 0) return hipSuccess;
+    if (max_blocks >= (1ll << 31)) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)max_blocks, (unsigned)((cols + 255) / 256));
+    if (in_dt == DT_E4M3)
+        quant_cols_kernel<DT_E4M3><<<grid, 256, 0, s>>>(src, src_s, gather, offsets, bbase, seg_rows, n_seg, cols, q,
+                                                        sc);
+    else
+        quant_cols_kernel<DT_BF16><<<grid, 256, 0, s>>>(src, src_s, gather, offsets, bbase, seg_rows, n_seg, cols, q,
+                                                        sc);
     return hipGetLastError();
 }
 
@@ -751,6 +1038,19 @@ hipError_t launch_wgrad(int dt, int pass, const WgradArgs &a, hipStream_t s) {
     if (dt == DT_F32) {
         if (pass) wgrad_kernel<DT_F32, 1><<<(unsigned)grid, BW_NT, 0, s>>>(a, nlead, tiles);
         else wgrad_kernel<DT_F32, 0><<<(unsigned)grid, BW_NT, 0, s>>>(a, nlead, tiles);
+    } else if (dt == DT_E4M3) {
+        static std::once_flag once8;
+        static hipError_t attr8 = hipSuccess;
+        std::call_once(once8, [] {
+            attr8 = hipFuncSetAttribute((const void *)wgrad_fp8_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                        WF8_LDS);
+            if (attr8 == hipSuccess)
+                attr8 = hipFuncSetAttribute((const void *)wgrad_fp8_kernel<1>,
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, WF8_LDS);
+        });
+        if (attr8 != hipSuccess) return attr8;
+        if (pass) wgrad_fp8_kernel<1><<<(unsigned)grid, WF8_NT, WF8_LDS, s>>>(a, nlead, tiles);
+        else wgrad_fp8_kernel<0><<<(unsigned)grid, WF8_NT, WF8_LDS, s>>>(a, nlead, tiles);
     } else {
         static std::once_flag once;
         static hipError_t attr = hipSuccess;

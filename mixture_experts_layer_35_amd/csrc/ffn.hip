@@ -189,7 +189,6 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
     constexpr bool FP8 = DT == DT_E4M3;
     static_assert(!FP8 || !GATEUP || BF == 128, "fp8 H quantisation needs whole 128-feature groups per tile");
     static_assert(!FP8 || 128 % (GATEUP ? WRW / 2 : WRW) == 0, "fp8: a wave's rows sit in one weight block");
-    static_assert(!(FP8 && SWBWD), "the SwiGLU gradient pass is bf16 / fp32 only");
 
     extern __shared__ __align__(1024) char smem[];
     const int pbytes = prefix_bytes(a.p[0].n_exp, a.nprob > 1 ? a.p[1].n_exp : 0);
@@ -596,11 +595,14 @@ hipError_t run(const FfnArgs &a, hipStream_t s) {
 
 hipError_t launch_ffn(int dt, int mode, const FfnArgs &a, hipStream_t s) {
     if (mode == FFN_GATEUP_BWD || mode == FFN_BWD_DH || mode == FFN_BWD_DX) {
-        if (dt == DT_E4M3) return hipErrorInvalidValue;
-        const bool f32 = dt == DT_F32;
-        if (mode == FFN_GATEUP_BWD) return f32 ? run<DT_F32, FFN_GATEUP_BWD>(a, s) : run<DT_BF16, FFN_GATEUP_BWD>(a, s);
-        if (mode == FFN_BWD_DH) return f32 ? run<DT_F32, FFN_BWD_DH>(a, s) : run<DT_BF16, FFN_BWD_DH>(a, s);
-        return f32 ? run<DT_F32, FFN_BWD_DX>(a, s) : run<DT_BF16, FFN_BWD_DX>(a, s);
+        if (mode == FFN_GATEUP_BWD)
+            return dt == DT_F32 ? run<DT_F32, FFN_GATEUP_BWD>(a, s)
+                                : dt == DT_BF16 ? run<DT_BF16, FFN_GATEUP_BWD>(a, s) : run<DT_E4M3, FFN_GATEUP_BWD>(a, s);
+        if (mode == FFN_BWD_DH)
+            return dt == DT_F32 ? run<DT_F32, FFN_BWD_DH>(a, s)
+                                : dt == DT_BF16 ? run<DT_BF16, FFN_BWD_DH>(a, s) : run<DT_E4M3, FFN_BWD_DH>(a, s);
+        return dt == DT_F32 ? run<DT_F32, FFN_BWD_DX>(a, s)
+                            : dt == DT_BF16 ? run<DT_BF16, FFN_BWD_DX>(a, s) : run<DT_E4M3, FFN_BWD_DX>(a, s);
     }
     const bool gateup = mode == FFN_GATEUP;
     if (dt == DT_F32) return gateup ? run<DT_F32, FFN_GATEUP>(a, s) : run<DT_F32, FFN_DOWN>(a, s);

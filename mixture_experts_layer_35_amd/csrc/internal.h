@@ -93,6 +93,11 @@ struct WgradProblem {
     int Pdim, Qdim, split;
     void *out0, *out1;
     int64_t rows_hint;      // typical rows per expert (sizes the work per workgroup)
+    // e4m3 operands: 128 x 1 column scales per 128-row run ([run][Pdim], [run][Qdim]); the
+    // expert's first run is bbase[e] (offsets problems) or e * ceil(rows_fixed / 128); an
+    // operand read with p_local / q_local starts at run 0
+    const float *Ps, *Qs;
+    const int32_t *bbase;
 };
 struct WgradArgs {
     WgradProblem p[2];
@@ -100,6 +105,14 @@ struct WgradArgs {
 };
 hipError_t launch_transpose(int dt, const void *src, int64_t nmat, int rows, int cols, void *dst, int dst_ld, int col0,
                             hipStream_t s);
+hipError_t launch_transpose_scales(const float *src, int64_t nmat, int rows, int cols, float *dst, int dst_ld, int col0,
+                                   hipStream_t s);
+hipError_t launch_block_base(const int32_t *offsets, int n, int32_t *bbase, hipStream_t s);
+// 128 x 1 tiles along segment rows (segments: device offsets with run bases bbase, or n_seg
+// runs of seg_rows rows); in_dt DT_BF16, or DT_E4M3 with 1 x 128 scales src_s.
+hipError_t launch_quant_cols(int in_dt, const void *src, const float *src_s, const int32_t *gather,
+                             const int32_t *offsets, const int32_t *bbase, int64_t seg_rows, int n_seg, int64_t max_blocks,
+                             int cols, uint8_t *q, float *sc, hipStream_t s);
 hipError_t launch_bwd_combine(int dt, const void *dout, const void *y, const int32_t *inv, const float *topk_w, int64_t T,
                               int d, int K, void *dy, float *dg, hipStream_t s);
 hipError_t launch_bwd_token(int dt, const void *dxr, const void *dxs, int Ns, const int32_t *inv, const int32_t *idx,

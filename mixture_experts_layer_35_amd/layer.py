@@ -11,7 +11,7 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_WS_FORWARD, MoeError, MoeShape, MOE_ERR_UNSUPPORTED, moe_backward,
+from . import (MOE_BF16, MOE_E4M3, MOE_F32, MOE_WS_FORWARD, MoeShape, moe_backward,
                moe_backward_workspace_bytes, moe_forward, moe_quantize_weights_128x128,
                moe_transpose_expert_weights, moe_workspace_bytes)
 
@@ -107,24 +107,28 @@ class MoeLayer:
     # ---- backward -----------------------------------------------------------
 
     def transposed_weights(self, stream=None):
-        """(routed, shared) pairs (W_down^T [n, I, d], [W_gate^T | W_up^T] [n, d, 2I]) that the
-        backward reads; built on first use.  Call drop_transposed() after changing the weights."""
-        if self.shape.w_dtype == MOE_E4M3:
-            raise MoeError(MOE_ERR_UNSUPPORTED, "the backward runs on fp32 / bf16 layers")
+        """(routed, shared) transposed copies ((W_down^T [n, I, d], [W_gate^T | W_up^T] [n, d, 2I]),
+        e4m3 block scales or None) that the backward reads; built on first use.  Call
+        drop_transposed() after changing the weights."""
         if self._wt is None:
             d, I = self.shape.d, self.shape.inter
+            fp8 = self.shape.w_dtype == MOE_E4M3
 
-            def tr(ws):
+            def tr(ws, ss):
                 if ws is None:
-                    return None
+                    return None, None
                 wg, wu, wd = ws
                 n = wg.shape[0]
                 wdt = torch.empty((n, I, d), dtype=wd.dtype, device=wd.device)
                 wgut = torch.empty((n, d, 2 * I), dtype=wg.dtype, device=wg.device)
-                moe_transpose_expert_weights(self.shape, n, wg, wu, wd, wdt, wgut, stream)
-                return wdt, wgut
+                st = None
+                if fp8:
+                    st = (torch.empty((n, I // 128, d // 128), dtype=torch.float32, device=wd.device),
+                          torch.empty((n, d // 128, 2 * I // 128), dtype=torch.float32, device=wd.device))
+                moe_transpose_expert_weights(self.shape, n, ws, ss, (wdt, wgut), st, stream)
+                return (wdt, wgut), st
 
-            self._wt = (tr(self.routed_w), tr(self.shared_w))
+            self._wt = (tr(self.routed_w, self.routed_s), tr(self.shared_w, self.shared_s))
         return self._wt
 
     def drop_transposed(self):
@@ -139,7 +143,7 @@ class MoeLayer:
         T = u.shape[0]
         if self._ws is None or self._ws_T != T:
             raise ValueError("backward needs the workspace of a forward call on the same batch")
-        rt, st = self.transposed_weights(stream)
+        (rt, rts), (st, sts) = self.transposed_weights(stream)
         self.shape.T = T
         if self._bws is None or self._bws_T != T:
             n = moe_backward_workspace_bytes(self.shape)
@@ -147,6 +151,6 @@ class MoeLayer:
             self._bws_T = T
         if du is None:
             du = torch.empty((T, self.shape.d), dtype=u.dtype, device=u.device)
-        moe_backward(self.shape, u, self.gate_w, self.routed_w, rt, self.shared_w, st, self._ws, dout, du, dgate_w,
-                     d_routed_w, d_shared_w, dtopk_w, self._bws, stream)
+        moe_backward(self.shape, u, self.gate_w, self.routed_w, self.routed_s, rt, rts, self.shared_w, self.shared_s,
+                     st, sts, self._ws, dout, du, dgate_w, d_routed_w, d_shared_w, dtopk_w, self._bws, stream)
         return du

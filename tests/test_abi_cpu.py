@@ -111,6 +111,13 @@ def test_null_pointer_and_workspace_rejections(lib):
                                1 << 30, None) == moe.MOE_ERR_INVALID_ARG   # e4m3 needs scales
     assert lib.moe_quantize_1x128(4, 100, moe.MOE_BF16, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_quantize_weights_128x128(1, 128, 96, moe.MOE_BF16, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    q1 = lib.moe_quantize_128x1
+    assert q1(2, FAKE, 512, 100, moe.MOE_BF16, FAKE, None, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert q1(2, FAKE, 512, 128, moe.MOE_F32, FAKE, None, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert q1(2, FAKE, 512, 128, moe.MOE_E4M3, FAKE, None, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert q1(2, FAKE, 512, 128, moe.MOE_BF16, FAKE, None, None, FAKE, FAKE, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert q1(-1, FAKE, 512, 128, moe.MOE_BF16, FAKE, None, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert q1(0, None, 0, 128, moe.MOE_BF16, None, None, None, None, None, None, None) == moe.MOE_OK
 
 
 def test_empty_batch_is_a_noop(lib):
@@ -173,9 +180,9 @@ def test_backward_rejections(lib):
     w, wa = _parr(FAKE, FAKE, FAKE)
     wt, wta = _parr(FAKE, FAKE, None)
 
-    def call(shape=S, fwd_bytes=fwd, ws_bytes=need, routed_wt=wt, du=FAKE, fwd_ws=FAKE):
-        return lib.moe_backward(shape, FAKE, FAKE, w, routed_wt, w, wt, fwd_ws, fwd_bytes, FAKE, du, None, None,
-                                None, None, FAKE, ws_bytes, None)
+    def call(shape=S, fwd_bytes=fwd, ws_bytes=need, routed_wt=wt, du=FAKE, fwd_ws=FAKE, rs=None, rts=None):
+        return lib.moe_backward(shape, FAKE, FAKE, w, rs, routed_wt, rts, w, rs, wt, rts, fwd_ws, fwd_bytes, FAKE,
+                                du, None, None, None, None, FAKE, ws_bytes, None)
 
     assert call(ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert call(fwd_bytes=fwd - 1) == moe.MOE_ERR_WORKSPACE
@@ -184,15 +191,22 @@ def test_backward_rejections(lib):
     assert call(fwd_ws=FAKE + 16) == moe.MOE_ERR_INVALID_ARG
     bad_t, bad_ta = _parr(FAKE, None, None)
     assert call(routed_wt=bad_t) == moe.MOE_ERR_INVALID_ARG
+    # e4m3 layers need the forward and the transposed block scales
     s8 = moe.make_shape(256, 256, 16, 1, 4, 2, 2, 128, "fp8")
-    assert call(shape=ctypes.byref(s8)) == moe.MOE_ERR_UNSUPPORTED
-    assert lib.moe_backward_workspace_bytes(ctypes.byref(s8)) == 0
-    assert lib.moe_transpose_expert_weights(ctypes.byref(s8), 4, FAKE, FAKE, FAKE, FAKE, FAKE,
-                                            None) == moe.MOE_ERR_UNSUPPORTED
-    assert lib.moe_transpose_expert_weights(S, -1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
-    assert lib.moe_transpose_expert_weights(S, 4, FAKE, None, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    S8 = ctypes.byref(s8)
+    need8 = lib.moe_backward_workspace_bytes(S8)
+    fwd8 = lib.moe_workspace_bytes(S8, moe.MOE_WS_FORWARD)
+    assert need8 > 0
+    assert call(shape=S8, ws_bytes=need8, fwd_bytes=fwd8) == moe.MOE_ERR_INVALID_ARG
+    assert "scale" in moe.moe_last_error()
+    sc, sca = _parr(FAKE, FAKE, FAKE)
+    sct, scta = _parr(FAKE, FAKE, None)
+    assert call(shape=S8, ws_bytes=need8 - 1, fwd_bytes=fwd8, rs=sc, rts=sct) == moe.MOE_ERR_WORKSPACE
+    assert lib.moe_transpose_expert_weights(S8, 4, w, None, wt, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_transpose_expert_weights(S, -1, w, None, wt, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_transpose_expert_weights(S, 4, w, None, bad_t, None, None) == moe.MOE_ERR_INVALID_ARG
     # nothing to do: no device access
-    assert lib.moe_transpose_expert_weights(S, 0, None, None, None, None, None, None) == moe.MOE_OK
+    assert lib.moe_transpose_expert_weights(S, 0, None, None, None, None, None) == moe.MOE_OK
     s0 = tiny(T=0)
-    assert lib.moe_backward(ctypes.byref(s0), None, None, None, None, None, None, None, 0, None, None, None, None,
-                            None, None, None, 0, None) == moe.MOE_OK
+    assert lib.moe_backward(ctypes.byref(s0), None, None, None, None, None, None, None, None, None, None, None, 0,
+                            None, None, None, None, None, None, None, 0, None) == moe.MOE_OK

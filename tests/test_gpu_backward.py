@@ -8,7 +8,11 @@ the GPU's.  Where the two selections differ (near ties of the fp32 affinities,
 checked), those tokens are left out of the per-token comparison and the
 experts they touch out of the per-expert one.
 
-Bar: max|err|/max|ref| <= 1e-4 (fp32 layers), 2e-2 (bf16 layers)."""
+FP8 layers are checked against the oracle's FP8 backward (the same
+quantisation steps, §3.3) given the oracle's own 128 x 128 weight blocks; the
+segmented 128 x 1 quantiser and the weight transposes bit-exactly.
+
+Bar: max|err|/max|ref| <= 1e-4 (fp32 layers), 2e-2 (bf16), 5e-2 (fp8)."""
 import numpy as np
 import pytest
 
@@ -47,7 +51,7 @@ def host(t):
 
 
 def tol_of(cfg):
-    return {"fp32": 1e-4, "bf16": 2e-2}[cfg.dtype]
+    return {"fp32": 1e-4, "bf16": 2e-2, "fp8": 5e-2}[cfg.dtype]
 
 
 def cfg_of(dtype, T, d, Nr, G, Mg, K, Ns, I, bias="uniform"):
@@ -63,7 +67,9 @@ def gpu_forward_backward(cfg, inp, dout, flags=0, bias=None, want=("dgate", "dro
     u = dev(inp["u"])
     idx = torch.empty((T, cfg.K), dtype=torch.int32, device="cuda")
     layer.forward(u, topk_idx=idx)
-    like = lambda ws: tuple(torch.empty_like(w) for w in ws)
+    # weight gradients in the activation format (bf16 for e4m3 weights)
+    like = lambda ws: tuple(torch.empty(w.shape, dtype=torch.bfloat16 if w.element_size() == 1 else w.dtype,
+                                        device="cuda") for w in ws)
     g = dict(dgate=torch.empty((cfg.Nr, cfg.d), dtype=torch.float32, device="cuda") if "dgate" in want else None,
              drouted=like(layer.routed_w) if "drouted" in want else None,
              dshared=like(layer.shared_w) if "dshared" in want and cfg.Ns else None,
@@ -118,6 +124,18 @@ def compare(cfg, got, ref, same, clean, skip=()):
         assert v <= tol, (k, v)
 
 
+def oracle_backward(orc, cfg, inp, idx, dout, rs, **kw):
+    routed = (inp["wg"], inp["wu"], inp["wd"])
+    shared = (inp["swg"], inp["swu"], inp["swd"]) if cfg.Ns else None
+    if cfg.dtype != "fp8":
+        return orc.moe_backward(inp["u"], inp["gate_w"], idx, routed, shared, dec(dout), routed_scale=rs, **kw)
+    rq = [orc.quant_128x128(w) for w in routed]
+    sq = [orc.quant_128x128(w) for w in shared] if shared else None
+    return orc.moe_backward_fp8(inp["u"], inp["gate_w"], idx, [q for q, _ in rq], [x for _, x in rq],
+                                [q for q, _ in sq] if sq else None, [x for _, x in sq] if sq else None, dec(dout),
+                                routed_scale=rs, **kw)
+
+
 def run_case(moe, orc, cfg, seed, flags=0, bias=None, skip=(), rs=1.0):
     inp = syn.layer_inputs(cfg, seed=seed)
     b = inp["bias"] if bias is None else bias
@@ -125,9 +143,7 @@ def run_case(moe, orc, cfg, seed, flags=0, bias=None, skip=(), rs=1.0):
     got = gpu_forward_backward(cfg, inp, dout, flags=flags, bias=b, rs=rs)
     s_r, idx_r, _ = oracle_selection(orc, cfg, inp, b)
     same, clean = agreement(cfg, got["idx"], idx_r, s_r, b)
-    shared = (inp["swg"], inp["swu"], inp["swd"]) if cfg.Ns else None
-    ref = orc.moe_backward(inp["u"], inp["gate_w"], idx_r, (inp["wg"], inp["wu"], inp["wd"]), shared, dec(dout),
-                           routed_scale=rs)
+    ref = oracle_backward(orc, cfg, inp, idx_r, dout, rs)
     compare(cfg, got, ref, same, clean, skip)
     return got, ref, inp
 
@@ -139,6 +155,11 @@ def run_case(moe, orc, cfg, seed, flags=0, bias=None, skip=(), rs=1.0):
     ("bf16", 700, 512, 32, 4, 2, 4, 1, 256, 0, 1.0),
     ("bf16", 129, 384, 32, 8, 3, 6, 2, 128, 1, 1.0),        # ragged tail, odd group count
     ("bf16", 300, 256, 64, 8, 4, 8, 0, 256, 0, 2.5),        # no shared expert
+    ("fp8", 256, 256, 16, 4, 2, 2, 1, 256, 0, 1.0),
+    ("fp8", 1, 256, 16, 4, 2, 2, 1, 128, 0, 1.0),           # one token: one-row 128 x 1 runs
+    ("fp8", 700, 512, 32, 4, 2, 4, 1, 256, 0, 2.5),         # several runs per expert, ragged last runs
+    ("fp8", 129, 384, 32, 8, 3, 6, 2, 128, 1, 1.0),         # two shared experts, residual flag
+    ("fp8", 300, 256, 64, 8, 4, 8, 0, 384, 0, 1.0),         # no shared expert
 ])
 def test_backward_matches_oracle(moe, orc, dtype, T, d, Nr, G, Mg, K, Ns, I, flags, rs):
     cfg = cfg_of(dtype, T, d, Nr, G, Mg, K, Ns, I)
@@ -183,20 +204,92 @@ def test_backward_deterministic_and_optional_outputs(moe, orc):
         assert (x == y).all()
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp8"])
 def test_transpose_expert_weights_exact(moe, dtype):
     import mixture_experts_layer_35_amd as m
     n, I, d = 3, 256, 384
     rng = np.random.default_rng(5)
     w = [rng.standard_normal(s).astype(np.float32) for s in ((n, I, d), (n, I, d), (n, d, I))]
+    ws = wts = None
     if dtype == "bf16":
         w = [syn.to_bf16_bits(x) for x in w]
+    if dtype == "fp8":
+        # codes and block scales are moved, never decoded: any byte but the NaNs
+        w = [rng.integers(0, 255, x.shape).astype(np.uint8) for x in w]
+        w = [np.where(x == 0x7F, 0, x).astype(np.uint8) for x in w]
+        ws = [rng.uniform(0.5, 2.0, (n, a // 128, b // 128)).astype(np.float32)
+              for a, b in ((I, d), (I, d), (d, I))]
     shape = m.make_shape(1, d, 4, 1, 1, 1, 1, I, dtype)
-    wdt = torch.empty((n, I, d), dtype=torch.float32 if dtype == "fp32" else torch.bfloat16, device="cuda")
-    wgut = torch.empty((n, d, 2 * I), dtype=wdt.dtype, device="cuda")
+    tdt = {"fp32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[dtype]
+    wdt = torch.empty((n, I, d), dtype=tdt, device="cuda")
+    wgut = torch.empty((n, d, 2 * I), dtype=tdt, device="cuda")
+    if ws is not None:
+        wts = (torch.empty((n, I // 128, d // 128), dtype=torch.float32, device="cuda"),
+               torch.empty((n, d // 128, 2 * I // 128), dtype=torch.float32, device="cuda"))
     print("transpose", dtype, flush=True)
-    m.moe_transpose_expert_weights(shape, n, dev(w[0]), dev(w[1]), dev(w[2]), wdt, wgut)
+    m.moe_transpose_expert_weights(shape, n, [dev(x) for x in w], None if ws is None else [dev(x) for x in ws],
+                                   (wdt, wgut), wts)
     assert (host(wdt) == np.transpose(w[2], (0, 2, 1))).all()
     gu = host(wgut)
     assert (gu[:, :, :I] == np.transpose(w[0], (0, 2, 1))).all()
     assert (gu[:, :, I:] == np.transpose(w[1], (0, 2, 1))).all()
+    if ws is not None:
+        assert (host(wts[0]) == np.transpose(ws[2], (0, 2, 1))).all()
+        sgu = host(wts[1])
+        assert (sgu[:, :, :I // 128] == np.transpose(ws[0], (0, 2, 1))).all()
+        assert (sgu[:, :, I // 128:] == np.transpose(ws[1], (0, 2, 1))).all()
+
+
+def test_backward_fp8_empty_expert(moe, orc):
+    # expert 5 is never chosen: its 128 x 1 operand lists are empty and its
+    # gradients exactly zero
+    cfg = cfg_of("fp8", 640, 256, 32, 4, 2, 4, 1, 256)
+    bias = np.zeros(32, np.float32)
+    bias[5] = -10.0
+    print("backward fp8 empty expert", flush=True)
+    got, _, _ = run_case(moe, orc, cfg, seed=33, bias=bias)
+    assert (got["idx"] != 5).all()
+    assert (got["dgate"][5] == 0).all()
+    for a in got["drouted"]:
+        assert (dec(a[5]) == 0).all()
+
+
+@pytest.mark.parametrize("x_dtype,gather", [("bf16", False), ("bf16", True), ("e4m3", True), ("e4m3", False)])
+def test_quantize_128x1_matches_oracle(moe, orc, x_dtype, gather):
+    """moe_quantize_128x1 (the FP8 weight-gradient operands): codes, scales and
+    run bases bit-exact against the oracle's 128 x 1 quantiser, over segments
+    that are empty, one row, exactly one run and ragged, with an all-zero
+    column (scale 1) and rows of very different magnitude."""
+    import mixture_experts_layer_35_amd as m
+    rng = np.random.default_rng(11 + gather)
+    lens = [0, 300, 128, 1, 0, 257, 129, 0]
+    off = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    rows, cols, n_src = int(off[-1]), 384, 900
+    if x_dtype == "bf16":
+        x = rng.standard_normal((n_src, cols)) * np.exp2(rng.integers(-12, 12, (n_src, 1)))
+        x[:, 7] = 0.0
+        x = syn.to_bf16_bits(x.astype(np.float32))
+        xs, code = None, m.MOE_BF16
+    else:
+        x = rng.integers(0, 255, (n_src, cols)).astype(np.uint8)
+        x = np.where(x == 0x7F, 0x3A, x).astype(np.uint8)
+        x[:, 7] = 0
+        xs = np.exp2(rng.uniform(-20, 4, (n_src, cols // 128))).astype(np.float32)
+        code = m.MOE_E4M3
+    g = rng.integers(0, n_src, rows).astype(np.int32) if gather else None
+    if not gather:
+        x, xs = x[:rows], None if xs is None else xs[:rows]
+    q_r, s_r = orc.quant_128x1(x, off, x_scales=xs, gather=g)
+    nblk = s_r.shape[0]
+    q = torch.full((rows, cols), 0xAA, dtype=torch.uint8, device="cuda")
+    sc = torch.full((nblk + 4, cols), -1.0, dtype=torch.float32, device="cuda")
+    bb = torch.full((len(lens) + 1,), -1, dtype=torch.int32, device="cuda")
+    print("quantize_128x1", x_dtype, gather, flush=True)
+    m.moe_quantize_128x1(len(lens), dev(off), rows, cols, code, dev(x), None if xs is None else dev(xs),
+                         None if g is None else dev(g), q, sc, bb)
+    assert (host(bb) == np.concatenate([[0], np.cumsum((np.array(lens) + 127) // 128)])).all()
+    assert (host(q) == q_r).all()
+    sg = host(sc)
+    assert (sg[:nblk].view(np.uint32) == s_r.view(np.uint32)).all()
+    assert (sg[nblk:] == -1.0).all()           # nothing past the last run
+    assert (s_r[:, 7] == 1.0).all()

@@ -152,11 +152,12 @@ def test_v3_decode_bf16(moe, orc, v3):
     check(cfg, cfg.T, got, ref, tokens, inp["bias"], 2e-2)
 
 
-def test_v3_fp8(moe, orc, v3):
-    from mixture_experts_layer_35_amd.layer import MoeLayer, quantize_weights_128x128, to_host
-    cfg0, inp, layer16 = v3
+@pytest.fixture(scope="module")
+def v3_fp8(moe, v3):
+    """The e4m3 layer: weights quantised on the device from the same bf16 master weights."""
+    from mixture_experts_layer_35_amd.layer import MoeLayer, quantize_weights_128x128
+    _, inp, layer16 = v3
     cfg = syn.CONFIGS["v3_fp8"]
-    # e4m3 weights quantised on the device from the same bf16 master weights
     rq, rs, sq, ss = [], [], [], []
     for w in layer16.routed_w:
         q, s = quantize_weights_128x128(w)
@@ -167,31 +168,43 @@ def test_v3_fp8(moe, orc, v3):
         sq.append(q)
         ss.append(s)
     torch.cuda.synchronize()
-    # device quantisation of two experts is bit-identical to the oracle's
-    for k, name in enumerate(("wg", "wu", "wd")):
-        for e in (0, 255):
-            qo, so = orc.quant_128x128(inp[name][e:e + 1])
-            assert (to_host(rq[k][e]) == qo[0]).all()
-            assert (to_host(rs[k][e]).view(np.uint32) == so[0].view(np.uint32)).all()
-    layer = MoeLayer(shape_of(cfg), layer16.gate_w, layer16.bias, rq, sq, rs, ss)
-    u = syn.hidden(cfg)
-    print("forward V3 fp8 T=%d" % cfg.T, flush=True)
-    got = run(layer, cfg, u)
-    tokens = np.sort(np.random.default_rng(2).choice(cfg.T, 16, replace=False))
-    _, idx_o, _ = orc.route(u, inp["gate_w"], inp["bias"], G=cfg.G, Mg=cfg.Mg, K=cfg.K, tokens=tokens)
-    need = np.unique(idx_o)
+    return cfg, MoeLayer(shape_of(cfg), layer16.gate_w, layer16.bias, rq, sq, rs, ss)
+
+
+def quantise_for_oracle(orc, inp, experts):
+    """The oracle's own 128 x 128 blocks of the listed routed experts (the others
+    zero, scale 1: never read) and of the shared expert."""
     routed_q, routed_s = [], []
     for name in ("wg", "wu", "wd"):
         w = inp[name]
         q = np.zeros(w.shape, np.uint8)
         s = np.ones((w.shape[0], w.shape[1] // 128, w.shape[2] // 128), np.float32)
-        q[need], s[need] = orc.quant_128x128(w[need])
+        q[experts], s[experts] = orc.quant_128x128(w[experts])
         routed_q.append(q)
         routed_s.append(s)
     shared = [orc.quant_128x128(inp[n]) for n in ("swg", "swu", "swd")]
-    ref = orc.moe_forward(u, inp["gate_w"], inp["bias"], tuple(routed_q), tuple(p[0] for p in shared), G=cfg.G,
+    return routed_q, routed_s, [p[0] for p in shared], [p[1] for p in shared]
+
+
+def test_v3_fp8(moe, orc, v3, v3_fp8):
+    from mixture_experts_layer_35_amd.layer import to_host
+    _, inp, _ = v3
+    cfg, layer = v3_fp8
+    # device quantisation of two experts is bit-identical to the oracle's
+    for k, name in enumerate(("wg", "wu", "wd")):
+        for e in (0, 255):
+            qo, so = orc.quant_128x128(inp[name][e:e + 1])
+            assert (to_host(layer.routed_w[k][e]) == qo[0]).all()
+            assert (to_host(layer.routed_s[k][e]).view(np.uint32) == so[0].view(np.uint32)).all()
+    u = syn.hidden(cfg)
+    print("forward V3 fp8 T=%d" % cfg.T, flush=True)
+    got = run(layer, cfg, u)
+    tokens = np.sort(np.random.default_rng(2).choice(cfg.T, 16, replace=False))
+    _, idx_o, _ = orc.route(u, inp["gate_w"], inp["bias"], G=cfg.G, Mg=cfg.Mg, K=cfg.K, tokens=tokens)
+    routed_q, routed_s, shared_q, shared_s = quantise_for_oracle(orc, inp, np.unique(idx_o))
+    ref = orc.moe_forward(u, inp["gate_w"], inp["bias"], tuple(routed_q), tuple(shared_q), G=cfg.G,
                           Mg=cfg.Mg, K=cfg.K, w_code=orc.E4M3, out_code=orc.BF16, tokens=tokens,
-                          routed_scales=tuple(routed_s), shared_scales=tuple(p[1] for p in shared))
+                          routed_scales=tuple(routed_s), shared_scales=tuple(shared_s))
     check(cfg, cfg.T, got, ref, tokens, inp["bias"], 5e-2)
 
 
@@ -302,3 +315,57 @@ def test_v3_backward_sampled(moe, orc, v3, v3_routing):
     torch.cuda.empty_cache()
     for k, v in errs.items():
         assert v <= 2e-2, (k, v)
+
+
+def test_v3_backward_fp8_sampled(moe, orc, v3, v3_fp8):
+    """The e4m3 layer's backward (FP8 Dgrad and Wgrad GEMMs) at the V3 FP8
+    shape (T = 16384) in the launch configuration the benchmark times: input
+    and gate gradients of sampled tokens and the weight gradients of three
+    sampled experts against the oracle's FP8 backward at its own routing, given
+    its own 128 x 128 weight blocks."""
+    from mixture_experts_layer_35_amd.layer import to_device, to_host
+    _, inp, _ = v3
+    cfg, layer = v3_fp8
+    T, K, Nr = cfg.T, cfg.K, cfg.Nr
+    uh = syn.hidden(cfg)
+    u = to_device(uh)
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    print("V3 fp8 backward: forward T=%d" % T, flush=True)
+    layer.forward(u, topk_idx=idx)
+    dout = syn.grad_output(cfg)
+    dg = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    dW = tuple(torch.empty(w.shape, dtype=torch.bfloat16, device="cuda") for w in layer.routed_w)
+    print("V3 fp8 backward: weight transposes and backward", flush=True)
+    du = layer.backward(u, to_device(dout), d_routed_w=dW, dtopk_w=dg)
+    torch.cuda.synchronize()
+    gidx = to_host(idx)
+    print("V3 fp8 backward: oracle routing of all %d tokens" % T, flush=True)
+    s_r, ir, _ = orc.route(uh, inp["gate_w"], inp["bias"], G=cfg.G, Mg=cfg.Mg, K=K)
+    same = (gidx == ir).all(1)
+    for t in np.nonzero(~same)[0]:
+        assert routing_disagreement_is_near_tie(s_r[t], inp["bias"], ir[t], gidx[t], cfg.G, 4e-6), t
+    assert same.mean() >= 0.97
+    touched = set(gidx[~same].ravel().tolist()) | set(ir[~same].ravel().tolist())
+    counts = np.bincount(ir.ravel(), minlength=Nr)
+    clean = [e for e in range(Nr) if e not in touched and counts[e] > 0]
+    rng = np.random.default_rng(8)
+    exps = sorted({max(clean, key=lambda e: counts[e]), min(clean, key=lambda e: counts[e]),
+                   int(rng.choice(clean))})
+    tokens = np.sort(rng.choice(np.nonzero(same)[0], 16, replace=False))
+    need = np.unique(np.concatenate([ir[tokens].ravel(), exps]))
+    rq, rs, sq, ss = quantise_for_oracle(orc, inp, need)
+    print("V3 fp8 backward: oracle on tokens %s, experts %s (rows %s)" % (tokens.tolist(), exps,
+                                                                          counts[exps].tolist()), flush=True)
+    ref = orc.moe_backward_fp8(uh, inp["gate_w"], ir, rq, rs, sq, ss, dec(dout), tokens=tokens,
+                               experts=np.array(exps, np.int32), dgate=False, dshared=False)
+    errs = dict(du=rel_err(to_host(du)[tokens], ref["du"][tokens]),
+                dtopk_w=rel_err(to_host(dg)[tokens], ref["dg"][tokens]))
+    for name, a, key in zip(("dW_gate", "dW_up", "dW_down"), dW, ("dwg", "dwu", "dwd")):
+        for q, e in enumerate(exps):
+            errs["%s[%d]" % (name, e)] = rel_err(to_host(a[e]), ref[key][q])
+    print("V3 fp8 backward errors:", {k: "%.2e" % v for k, v in errs.items()}, flush=True)
+    del dW
+    layer.drop_transposed()
+    torch.cuda.empty_cache()
+    for k, v in errs.items():
+        assert v <= 5e-2, (k, v)
