@@ -73,8 +73,8 @@ def stage_bytes(cfg):
     return dict(router=router, dispatch=dispatch, combine=combine)
 
 
-BWD_STAGES = ("bwd_combine", "bwd_dh", "bwd_swiglu", "bwd_dx", "bwd_token", "bwd_dgate", "wgrad_down",
-              "wgrad_gate_up")
+BWD_STAGES = ("bwd_combine", "bwd_dh", "bwd_swiglu", "bwd_dx", "bwd_token", "bwd_dgate", "wgrad_tile",
+              "wgrad_down", "wgrad_gate_up")
 
 
 def algorithmic_bwd(cfg, n_touched):
@@ -99,12 +99,16 @@ def algorithmic_bwd(cfg, n_touched):
         bwd_dx=(2 * gemm, ex * 2 * I * d * wb + rows * 2 * I * o + rows * d * a),
         bwd_token=(2.0 * rows * d, rows * d * a + Nr * d * a + T * d * a + rr * 16),
         bwd_dgate=(2.0 * rr * d, T * d * a + Nr * d * 4 + rr * 8),
+        # e4m3: both weight-gradient passes' operands re-tiled 128 x 1 (read once, written once)
+        wgrad_tile=(0.0, (rr + T) * d * a + rows * I * o + rows * 2 * I * a + (rr + T) * d * o
+                    + ((rr + T) * d + rows * I + rows * 2 * I + (rr + T) * d) * o if fp8 else 0.0),
         wgrad_down=(gemm, (rr + T) * d * o + rows * I * o + ex * I * d * a),
         wgrad_gate_up=(2 * gemm, rows * 2 * I * o + T * d * o + ex * 2 * I * d * a))
 
 
 BWD_KERNELS = {"bwd_combine": "bwd_combine_kernel", "bwd_dh": "bwd_dh", "bwd_swiglu": "bwd_swiglu",
                "bwd_dx": "bwd_dx", "bwd_token": "bwd_token_kernel", "bwd_dgate": "dgate_kernel",
+               "wgrad_tile": None,      # eight quantiser launches: no single kernel's traffic
                "wgrad_down": "wgrad_down", "wgrad_gate_up": "wgrad_gate_up"}
 
 
@@ -121,6 +125,8 @@ def traffic_from_profile(cfg, kernel, backward=False):
     """HBM bytes per launch of `kernel` (a name or a tuple of names, summed)
     from the committed rocprofv3 PMC summary, or None when there is none for
     this workload or the kernel sources changed since it was taken."""
+    if kernel is None:
+        return None
     if isinstance(kernel, tuple):
         parts = [traffic_from_profile(cfg, k, backward) for k in kernel]
         parts = [p for p in parts if p is not None]
@@ -310,7 +316,7 @@ def main():
         return rows
 
     evs = event_rows(6)
-    bevs = event_rows(9) if bw is not None else None
+    bevs = event_rows(10) if bw is not None else None
     torch.cuda.synchronize()
     handles = [[e.cuda_event for e in row] for row in evs]
     bhandles = [[e.cuda_event for e in row] for row in bevs] if bevs else [None] * args.steps

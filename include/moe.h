@@ -287,9 +287,10 @@ int moe_backward(const moe_shape *shape, const void *u, const void *gate_w, cons
  *   stage_events[0] before the combine gradient   [1] after it (dY, dg; e4m3: their 1 x 128 tiles)
  *   [2] after dH = dY W_down                      [3] after the SwiGLU gradient pass ([dA | dB], tiled)
  *   [4] after dX = [dA | dB] [W_gate ; W_up]      [5] after the token pass (du, dz)
- *   [6] after the centroid gradient               [7] after dW_down (e4m3: with its operands' tiling)
- *   [8] after dW_gate / dW_up
- * NULL entries (or a NULL array, 9 entries otherwise) are skipped; skipped
+ *   [6] after the centroid gradient               [7] after the weight-gradient operands' tiling
+ *   [8] after dW_down                             (e4m3: run bases and 128 x 1 tiles; else empty)
+ *   [9] after dW_gate / dW_up
+ * NULL entries (or a NULL array, 10 entries otherwise) are skipped; skipped
  * optional outputs leave their stage empty.  Results are identical to
  * moe_backward.
  */

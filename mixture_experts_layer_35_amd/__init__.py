@@ -277,13 +277,13 @@ def moe_backward(shape, u, gate_w, routed_w, routed_s, routed_wt, routed_wt_s, s
 def moe_backward_timed(shape, u, gate_w, routed_w, routed_s, routed_wt, routed_wt_s, shared_w, shared_s, shared_wt,
                        shared_wt_s, fwd_ws, dout, du, dgate_w=None, d_routed_w=None, d_shared_w=None, dtopk_w=None,
                        ws=None, stream=None, stage_events=None):
-    """stage_events: 9 raw hipEvent_t handles (ints) or None."""
+    """stage_events: 10 raw hipEvent_t handles (ints) or None."""
     keep, args = _bwd_args(shape, u, gate_w, routed_w, routed_s, routed_wt, routed_wt_s, shared_w, shared_s,
                            shared_wt, shared_wt_s, fwd_ws, dout, du, dgate_w, d_routed_w, d_shared_w, dtopk_w, ws,
                            stream)
     ev = None
     if stage_events is not None:
-        arr = (ctypes.c_void_p * 9)(*stage_events)
+        arr = (ctypes.c_void_p * 10)(*stage_events)
         ev = ctypes.cast(arr, ctypes.c_void_p)
     rc = lib().moe_backward_timed(*args, ev)
     del keep

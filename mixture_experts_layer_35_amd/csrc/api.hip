@@ -729,28 +729,40 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
     if (dgate_w) HIPCHK(launch_dgate(dt, u, perm, offsets, dz, s->n_routed, d, dgate_w, st));
     HIPCHK(mark(6));
     // 7. weight gradients: down (dY rows x H rows), then gate/up ([dA | dB] rows x gathered u rows);
-    // e4m3: both operands re-tiled 128 x 1 along the expert's rows first
-    if (d_routed_w || (Ns && d_shared_w)) {
+    // e4m3: both operands of both passes re-tiled 128 x 1 along the expert's rows first
+    const bool wgr = d_routed_w || (Ns && d_shared_w);
+    int32_t *bbase = fp8 ? (int32_t *)(W + L.bbase) : nullptr;
+    const uint8_t *hq = (const uint8_t *)(Fw + F.h), *hsq = (const uint8_t *)(Fw + F.hsh);
+    const float *hs = (const float *)(Fw + F.hs), *hss = (const float *)(Fw + F.hshs);
+    if (fp8 && wgr) {
+        const uint8_t *uq = (const uint8_t *)(Fw + F.uq);
+        const float *us = (const float *)(Fw + F.us);
+        if (d_routed_w) {
+            HIPCHK(launch_block_base(offsets, s->n_routed, bbase, st));
+            HIPCHK(launch_quant_cols(DT_BF16, dy, nullptr, nullptr, offsets, bbase, 0, s->n_routed, L.rblk, d,
+                                     U8(L.p1q), F32(L.p1s), st));
+            HIPCHK(launch_quant_cols(DT_E4M3, hq, hs, nullptr, offsets, bbase, 0, s->n_routed, L.rblk, I,
+                                     U8(L.q1q), F32(L.q1s), st));
+            HIPCHK(launch_quant_cols(DT_BF16, dab, nullptr, nullptr, offsets, bbase, 0, s->n_routed, L.rblk, 2 * I,
+                                     U8(L.p2q), F32(L.p2s), st));
+            HIPCHK(launch_quant_cols(DT_E4M3, uq, us, perm, offsets, bbase, 0, s->n_routed, L.rblk, d, U8(L.q2q),
+                                     F32(L.q2s), st));
+        }
+        if (Ns && d_shared_w) {
+            HIPCHK(launch_quant_cols(DT_BF16, dout, nullptr, nullptr, nullptr, nullptr, T, 1, L.sblk, d,
+                                     U8(L.sp1q), F32(L.sp1s), st));
+            HIPCHK(launch_quant_cols(DT_E4M3, hsq, hss, nullptr, nullptr, nullptr, T, Ns, Ns * L.sblk, I,
+                                     U8(L.sq1q), F32(L.sq1s), st));
+            HIPCHK(launch_quant_cols(DT_BF16, dab_s, nullptr, nullptr, nullptr, nullptr, T, Ns, Ns * L.sblk, 2 * I,
+                                     U8(L.sp2q), F32(L.sp2s), st));
+            HIPCHK(launch_quant_cols(DT_E4M3, uq, us, nullptr, nullptr, nullptr, T, 1, L.sblk, d, U8(L.sq2q),
+                                     F32(L.sq2s), st));
+        }
+    }
+    HIPCHK(mark(7));
+    if (wgr) {
         // shared experts first: their long reductions start early, spread over every XCD
         const int64_t hint = (TK + s->n_routed - 1) / s->n_routed;
-        int32_t *bbase = fp8 ? (int32_t *)(W + L.bbase) : nullptr;
-        const uint8_t *hq = (const uint8_t *)(Fw + F.h), *hsq = (const uint8_t *)(Fw + F.hsh);
-        const float *hs = (const float *)(Fw + F.hs), *hss = (const float *)(Fw + F.hshs);
-        if (fp8) {
-            HIPCHK(launch_block_base(offsets, s->n_routed, bbase, st));
-            if (d_routed_w) {
-                HIPCHK(launch_quant_cols(DT_BF16, dy, nullptr, nullptr, offsets, bbase, 0, s->n_routed, L.rblk, d,
-                                         U8(L.p1q), F32(L.p1s), st));
-                HIPCHK(launch_quant_cols(DT_E4M3, hq, hs, nullptr, offsets, bbase, 0, s->n_routed, L.rblk, I,
-                                         U8(L.q1q), F32(L.q1s), st));
-            }
-            if (Ns && d_shared_w) {
-                HIPCHK(launch_quant_cols(DT_BF16, dout, nullptr, nullptr, nullptr, nullptr, T, 1, L.sblk, d,
-                                         U8(L.sp1q), F32(L.sp1s), st));
-                HIPCHK(launch_quant_cols(DT_E4M3, hsq, hss, nullptr, nullptr, nullptr, T, Ns, Ns * L.sblk, I,
-                                         U8(L.sq1q), F32(L.sq1s), st));
-            }
-        }
         WgradArgs wa{};
         int np = 0;
         if (Ns && d_shared_w) {
@@ -789,21 +801,7 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
         }
         wa.nprob = np;
         HIPCHK(launch_wgrad(wdt, 0, wa, st));
-        HIPCHK(mark(7));
-        if (fp8) {
-            if (d_routed_w) {
-                HIPCHK(launch_quant_cols(DT_BF16, dab, nullptr, nullptr, offsets, bbase, 0, s->n_routed, L.rblk,
-                                         2 * I, U8(L.p2q), F32(L.p2s), st));
-                HIPCHK(launch_quant_cols(DT_E4M3, Fw + F.uq, (const float *)(Fw + F.us), perm, offsets, bbase, 0,
-                                         s->n_routed, L.rblk, d, U8(L.q2q), F32(L.q2s), st));
-            }
-            if (Ns && d_shared_w) {
-                HIPCHK(launch_quant_cols(DT_BF16, dab_s, nullptr, nullptr, nullptr, nullptr, T, Ns, Ns * L.sblk,
-                                         2 * I, U8(L.sp2q), F32(L.sp2s), st));
-                HIPCHK(launch_quant_cols(DT_E4M3, Fw + F.uq, (const float *)(Fw + F.us), nullptr, nullptr, nullptr,
-                                         T, 1, L.sblk, d, U8(L.sq2q), F32(L.sq2s), st));
-            }
-        }
+        HIPCHK(mark(8));
         np = 0;
         if (Ns && d_shared_w) {
             WgradProblem &w = wa.p[np++];
@@ -847,9 +845,9 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
         wa.nprob = np;
         HIPCHK(launch_wgrad(wdt, 1, wa, st));
     } else {
-        HIPCHK(mark(7));
+        HIPCHK(mark(8));
     }
-    HIPCHK(mark(8));
+    HIPCHK(mark(9));
     return MOE_OK;
 }
 

@@ -293,3 +293,41 @@ def test_quantize_128x1_matches_oracle(moe, orc, x_dtype, gather):
     assert (sg[:nblk].view(np.uint32) == s_r.view(np.uint32)).all()
     assert (sg[nblk:] == -1.0).all()           # nothing past the last run
     assert (s_r[:, 7] == 1.0).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_backward_timed_is_backward(moe, dtype):
+    """moe_backward_timed (ten stage events) writes exactly what moe_backward writes."""
+    import mixture_experts_layer_35_amd as m
+    from mixture_experts_layer_35_amd.layer import MoeLayer
+    cfg = cfg_of(dtype, 300, 256, 16, 4, 2, 2, 1, 256)
+    inp = syn.layer_inputs(cfg, seed=51)
+    layer = MoeLayer.from_host(shape_of(cfg), inp["gate_w"], inp["bias"], inp["wg"], inp["wu"], inp["wd"],
+                               inp["swg"], inp["swu"], inp["swd"])
+    u = dev(inp["u"])
+    layer.forward(u)
+    dout = dev(syn.grad_output(cfg, seed=51))
+    grads = lambda: (torch.empty((cfg.Nr, cfg.d), dtype=torch.float32, device="cuda"),
+                     tuple(torch.empty(w.shape, dtype=torch.bfloat16, device="cuda") for w in layer.routed_w),
+                     tuple(torch.empty(w.shape, dtype=torch.bfloat16, device="cuda") for w in layer.shared_w))
+    g0, r0, s0 = grads()
+    print("backward timed", dtype, flush=True)
+    du0 = layer.backward(u, dout, dgate_w=g0, d_routed_w=r0, d_shared_w=s0)
+    (rt, rts), (st, sts) = layer.transposed_weights()
+    g1, r1, s1 = grads()
+    du1 = torch.empty_like(du0)
+    ws = torch.empty(max(m.moe_backward_workspace_bytes(layer.shape), 256), dtype=torch.uint8, device="cuda")
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(10)]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    m.moe_backward_timed(layer.shape, u, layer.gate_w, layer.routed_w, layer.routed_s, rt, rts, layer.shared_w,
+                         layer.shared_s, st, sts, layer.workspace(cfg.T), dout, du1, g1, r1, s1, None, ws,
+                         torch.cuda.current_stream(), [e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    assert (host(du0) == host(du1)).all()
+    assert (host(g0).view(np.uint32) == host(g1).view(np.uint32)).all()
+    for a, b in zip(r0 + s0, r1 + s1):
+        assert (host(a) == host(b)).all()
+    ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(9)]
+    assert all(x >= 0 for x in ms), ms
