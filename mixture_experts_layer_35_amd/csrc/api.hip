@@ -116,7 +116,7 @@ int dt_of(int d) { return d == MOE_F32 ? DT_F32 : d == MOE_BF16 ? DT_BF16 : DT_E
 // ---- workspace layouts --------------------------------------------------------
 
 struct FwdLayout {
-    size_t scores, idx, w, counts, offsets, bc, perm, inv, uq, us, h, hs, hsh, hshs, yperm, ysh, total;
+    size_t scores, idx, w, counts, offsets, bc, perm, inv, uq, us, h, hs, hsh, hshs, yperm, ysh, fq, total;
 };
 
 FwdLayout fwd_layout(const moe_shape *s) {
@@ -143,6 +143,7 @@ FwdLayout fwd_layout(const moe_shape *s) {
     L.hshs = take(fp8 ? (size_t)TS * (s->inter / 128) * 4 : 0);
     L.yperm = take((size_t)TK * s->d * osz);
     L.ysh = take((size_t)TS * s->d * osz);
+    L.fq = take(FFN_QUEUE_INTS * 4);
     L.total = o;
     return L;
 }
@@ -150,12 +151,14 @@ FwdLayout fwd_layout(const moe_shape *s) {
 size_t ffn_ws(const moe_shape *s, int64_t max_rows) {
     const bool fp8 = s->w_dtype == MOE_E4M3;
     const int hsz = fp8 ? 1 : esize(s->act_dtype);
-    return align256((size_t)max_rows * s->inter * hsz) + (fp8 ? align256((size_t)max_rows * (s->inter / 128) * 4) : 0);
+    return align256((size_t)max_rows * s->inter * hsz) + (fp8 ? align256((size_t)max_rows * (s->inter / 128) * 4) : 0) +
+           align256(FFN_QUEUE_INTS * 4);
 }
 
-int run_ffn_pair(const moe_shape *s, const FfnProblem *gu, const FfnProblem *dn, int nprob, hipStream_t st) {
+int run_ffn_pair(const moe_shape *s, const FfnProblem *gu, const FfnProblem *dn, int nprob, int *ctr, hipStream_t st) {
     FfnArgs a{};
     a.nprob = nprob;
+    a.ctr = ctr;
     a.K = s->d;
     a.F = s->inter;
     for (int i = 0; i < nprob; ++i) a.p[i] = gu[i];
@@ -301,7 +304,8 @@ int moe_grouped_ffn(const moe_shape *s, int32_t n_exp, const int32_t *offsets, i
     dn.w0 = w_down;
     dn.s0 = fp8 ? w_scales[2] : nullptr;
     dn.out = y;
-    return run_ffn_pair(s, &gu, &dn, 1, (hipStream_t)stream);
+    int *ctr = (int *)(h + ffn_ws(s, max_rows) - align256(FFN_QUEUE_INTS * 4));
+    return run_ffn_pair(s, &gu, &dn, 1, ctr, (hipStream_t)stream);
 }
 
 int moe_combine(const moe_shape *s, const void *y_perm, const int32_t *inv_perm, const float *topk_w,
@@ -451,8 +455,9 @@ int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, con
         a.nprob = nprob;
         a.K = s->d;
         a.F = s->inter;
-        // the shared experts' tiles go first: every workgroup starts at the same time, so the
-        // row blocks of one shared weight block run together and share it through L2
+        a.ctr = (int *)(W + L.fq);
+        // the shared experts' tiles go first: their row blocks of one weight block are list
+        // neighbours, taken together by the workgroups of one XCD
         for (int i = 0; i < nprob; ++i) a.p[i] = gu[nprob - 1 - i];
         HIPCHK(launch_ffn(dt_of(s->w_dtype), FFN_GATEUP, a, st));
         HIPCHK(mark(3));
@@ -474,7 +479,7 @@ int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, con
 // for e4m3 layers also the 1 x 128 tiles of dy, dO and [dA dB] (Dgrad inputs), the 128 x 1 tiles
 // of the weight-gradient operands and the experts' run bases
 struct BwdLayout {
-    size_t dy, dg, dz, dh, dab, dx;
+    size_t dy, dg, dz, dh, dab, dx, fq;
     size_t dyq, dys, doq, dos, abq, abs_;                       // Dgrad inputs
     size_t bbase, p1q, p1s, q1q, q1s, p2q, p2s, q2q, q2s;      // routed Wgrad operands (down, gate/up)
     size_t sp1q, sp1s, sq1q, sq1s, sp2q, sp2s, sq2q, sq2s;      // shared Wgrad operands
@@ -495,6 +500,7 @@ static BwdLayout bwd_layout(const moe_shape *s) {
     L.dh = take((size_t)R * I * a);
     L.dab = take((size_t)R * 2 * I * a);
     L.dx = take((size_t)R * d * a);
+    L.fq = take(FFN_QUEUE_INTS * 4);
     if (s->w_dtype == MOE_E4M3) {
         L.rblk = TK / 128 + s->n_routed + 1;
         L.sblk = (T + 127) / 128;
@@ -660,6 +666,7 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
     }
     FfnArgs fa{};
     fa.nprob = Ns ? 2 : 1;
+    fa.ctr = (int *)(W + L.fq);
     fa.K = d;
     fa.F = I;
     for (int i = 0; i < fa.nprob; ++i) fa.p[i] = p[fa.nprob - 1 - i];

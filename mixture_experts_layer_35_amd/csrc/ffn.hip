@@ -9,11 +9,15 @@
 //
 // Scheduling.  Rows are ragged per expert and only known on the device, so the
 // grid is persistent (one 512-thread workgroup per CU) and every workgroup
-// walks a tile list derived from the row offsets.  A tile is (expert, block of
-// 256 weight rows, block of up to 256 tokens); row blocks of one (expert,
-// weight block) are adjacent in the list and consecutive tiles run on one XCD,
-// so a weight tile shared by several row blocks is fetched once into that
-// XCD's L2.  Up to two problems (e.g. shared and routed experts) share a launch.
+// takes tiles from a list derived from the row offsets.  A tile is (expert,
+// block of 256 weight rows, block of up to 256 tokens); row blocks of one
+// (expert, weight block) are adjacent in the list, then the weight blocks of
+// the expert.  The list is cut into eight ranges of about equal cost, one per
+// XCD, and the workgroups of an XCD take its tiles in order through a counter,
+// so the tiles in flight on an XCD are always list neighbours: a weight block
+// shared by several row blocks, and the token rows shared by the weight
+// blocks, are fetched once into that XCD's L2 even though tiles take unequal
+// times.  Up to two problems (e.g. shared and routed experts) share a launch.
 //
 // Data movement.  The reduction dimension is walked in 128-byte steps.  Each
 // step's weight rows and token rows are copied from global memory straight
@@ -96,8 +100,91 @@ constexpr int TB = BM / WM / 16;        // 16-token blocks per wave (8)
 constexpr int SCL_BYTES = 2048;         // fp8: per-stage scale area (BM activation + 2 weight scales)
 constexpr int LDS_TOTAL = 160 * 1024;
 
-// LDS bytes besides the ring: tile prefixes of both problems (n_exp + 1 each).
-__host__ __device__ inline int prefix_bytes(int n0, int n1) { return ((n0 + 1 + n1 + 1) * 4 + 255) & ~255; }
+// LDS bytes besides the ring: tile prefixes of both problems (n_exp + 1 each),
+// then the tile queues' bounds and the next-tile slots (SCHED_INTS ints).
+constexpr int SCHED_INTS = 16;
+constexpr int NQ = 8;                   // tile queues, one per XCD
+constexpr int TILE_COST_W = 128;        // a tile's weight streaming, in token rows (queue balance)
+__host__ __device__ inline int prefix_bytes(int n0, int n1) {
+    return ((n0 + 1 + n1 + 1 + SCHED_INTS) * 4 + 255) & ~255;
+}
+
+// Tile queues.  The tile list is cut into NQ contiguous ranges of about equal
+// estimated cost (a tile of v token rows costs v + TILE_COST_W), one per XCD:
+// workgroups on XCD x take the tiles of range x in list order through a counter
+// (ctr[x]), so the tiles running at any moment on one XCD are neighbours in the
+// list and share their weight block and token rows through that XCD's L2 however
+// long each tile takes; a workgroup whose range is used up takes tiles from the
+// next ranges.  bounds[0..NQ]: first tile of each range, bounds[NQ] = total.
+// Expert e of a problem (m rows, mt = ceil(m / bm) row blocks, ftiles feature
+// blocks) costs ftiles * (m + mt * TILE_COST_W).  scan: NT int64 of scratch.
+template <int NT>
+__device__ void queue_bounds(const FfnArgs &a, int bm, int ftiles, const int *pre, const int *pre1, int total0,
+                             int total, long long *scan, int *bounds) {
+    const int tid = threadIdx.x;
+    const int n0 = a.p[0].n_exp, n = n0 + (a.nprob > 1 ? a.p[1].n_exp : 0);
+    const int per = (n + NT - 1) / NT;
+    const int lo = min(tid * per, n), hi = min(lo + per, n);
+    auto expert = [&](int g, long long &cost, int &tile0, int &ntiles) {
+        const FfnProblem &P = g < n0 ? a.p[0] : a.p[1];
+        const int e = g < n0 ? g : g - n0;
+        const int m = P.offsets ? P.offsets[e + 1] - P.offsets[e] : (int)P.rows_fixed;
+        const int mt = (m + bm - 1) / bm;
+        cost = (long long)ftiles * ((long long)m + (long long)mt * TILE_COST_W);
+        tile0 = g < n0 ? pre[e] : total0 + pre1[e];
+        ntiles = mt * ftiles;
+    };
+    long long local = 0;
+    for (int g = lo; g < hi; ++g) {
+        long long c;
+        int t0, nt;
+        expert(g, c, t0, nt);
+        local += c;
+    }
+    scan[tid] = local;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {
+        const long long v = tid >= off ? scan[tid - off] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    const long long ctot = scan[NT - 1];
+    long long c0 = scan[tid] - local;
+    if (tid == 0) {
+        bounds[0] = 0;
+        bounds[NQ] = total;
+    }
+    // the thread whose experts hold cost position B_x = x * ctot / NQ places boundary x
+    for (int g = lo; g < hi; ++g) {
+        long long c;
+        int t0, nt;
+        expert(g, c, t0, nt);
+        for (int x = 1; x < NQ; ++x) {
+            const long long B = ctot * x / NQ;
+            if (c > 0 && B >= c0 && B < c0 + c) bounds[x] = t0 + (int)((B - c0) * nt / c);
+        }
+        c0 += c;
+    }
+    if (ctot == 0 && tid > 0 && tid < NQ) bounds[tid] = 0;
+    __syncthreads();
+}
+
+// One grab from the tile queues by a single lane: *qpos (in LDS) is how many
+// queues, in the order xcd, xcd + 1, ..., this workgroup has used up.  Returns
+// the tile, or -1 once every queue is used up.  Waits for each counter value.
+__device__ __forceinline__ int grab_tile(int *ctr, const int *bounds, int xcd, int *qpos) {
+    int q = *qpos;
+    int t = -1;
+    for (; q < NQ; ++q) {
+        const int qq = (xcd + q) & (NQ - 1);
+        t = bounds[qq] + atomicAdd(ctr + qq, 1);
+        if (t < bounds[qq + 1]) break;
+        t = -1;
+    }
+    *qpos = q;
+    return t;
+}
 
 // One 128-byte reduction step of the tile: products of the wave's RB weight
 // blocks with its first NTB token blocks.  A producer wave (PROD) also issues
@@ -206,10 +293,13 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
     const int kb_per_row = K / 128;               // fp8 scale blocks along K (one per step)
 
     int *pre1 = pre + a.p[0].n_exp + 1;
+    int *bounds = (int *)(smem + pbytes) - SCHED_INTS;                // [NQ + 1] queue bounds
+    int *slot = bounds + NQ + 1;                                       // [3] tile slots, [3] grab position
     tile_prefix<NT>(a.p[0], BM, ftiles, pre, scan);
     if (a.nprob > 1) tile_prefix<NT>(a.p[1], BM, ftiles, pre1, scan);
     const int total0 = pre[a.p[0].n_exp];
     const int total = total0 + (a.nprob > 1 ? pre1[a.p[1].n_exp] : 0);
+    queue_bounds<NT>(a, BM, ftiles, pre, pre1, total0, total, (long long *)ring, bounds);
 
     // Loads are issued by the NP producer waves only (one per SIMD), so each
     // SIMD always has a consumer wave free to run MFMAs while its producer
@@ -352,17 +442,28 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
         }
     };
 
-    // XCD-aware order: workgroup b runs on XCD b % 8; give each XCD a contiguous run of tiles.
-    const int G = gridDim.x;
-    const int first = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+    // Tiles come from the queues (workgroup b runs on XCD b % 8).  One lane grabs,
+    // one tile ahead: right after a tile's last barrier it takes the tile after
+    // next, while the other waves start the next tile's loads and write results.
+    // Tile ids pass through three LDS slots: the tile of iteration k is in slot k % 3.
+    const int xcd = blockIdx.x & (NQ - 1);
+    const bool grabber = wid == NW - 1 && lane == 0;
+    if (grabber) {
+        slot[3] = 0;
+        slot[0] = grab_tile(a.ctr, bounds, xcd, slot + 3);
+        slot[1] = grab_tile(a.ctr, bounds, xcd, slot + 3);
+    }
+    __syncthreads();
+    const int first = slot[0];
     Tile cur, nxt;
-    if (first < total) {
+    if (first >= 0) {
         setup(first, cur);
         cta_barrier();   // the start-up scratch in the ring is no longer read
         prologue(cur);
     }
 
-    for (int t = first; t < total; t += G) {
+    int it = 0;   // iteration k, kept as k % 3
+    for (int t = first; t >= 0;) {
         f32x4 acc[RB][TB];
 #pragma unroll
         for (int i = 0; i < RB; ++i)
@@ -427,8 +528,20 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
         // Every wave is done with the ring: start the next tile's loads, then
         // write this tile's results while they are in flight.
         cta_barrier();
-        if (t + G < total) {
-            setup(t + G, nxt);
+        const int it1 = it == 2 ? 0 : it + 1, it2 = it1 == 2 ? 0 : it1 + 1;
+        const int tn = slot[it1];
+        if (grabber && tn >= 0) {
+            // slot it2 was last read at the end of the previous iteration, before this
+            // tile's barriers; it is read at the end of the next tile, after its barriers
+            slot[it2] = grab_tile(a.ctr, bounds, xcd, slot + 3);
+            wait_lgkm0();
+        } else if (grabber) {
+            slot[it2] = -1;
+            wait_lgkm0();
+        }
+        it = it1;
+        if (tn >= 0) {
+            setup(tn, nxt);
             prologue(nxt);
         }
 
@@ -568,11 +681,18 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
             }
         }
         cur = nxt;
+        t = tn;
     }
+}
+
+// The tile-queue counters start at zero in every launch.
+__global__ void zero_queues_kernel(int *ctr) {
+    if (threadIdx.x < NQ) ctr[threadIdx.x] = 0;
 }
 
 template <int DT, int MODE>
 hipError_t run(const FfnArgs &a, hipStream_t s) {
+    if (!a.ctr) return hipErrorInvalidValue;
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(once, [&] {
@@ -587,6 +707,7 @@ hipError_t run(const FfnArgs &a, hipStream_t s) {
     if (ring < 2 * ((WR + BM) * CB + (DT == DT_E4M3 ? SCL_BYTES : 0))) return hipErrorInvalidValue;
     int grid = device_cus();
     grid = (grid + 7) / 8 * 8;
+    zero_queues_kernel<<<1, 64, 0, s>>>(a.ctr);
     ffn_kernel<DT, MODE><<<grid, NT, LDS_TOTAL, s>>>(a, ring);
     return hipGetLastError();
 }

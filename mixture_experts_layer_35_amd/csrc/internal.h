@@ -62,9 +62,11 @@ struct FfnProblem {
 struct FfnArgs {
     FfnProblem p[2];
     int nprob;
-    int K;   // reduction length
-    int F;   // output features (I for gate/up, d for down)
+    int K;      // reduction length
+    int F;      // output features (I for gate/up, d for down)
+    int *ctr;   // FFN_QUEUE_INTS device ints of tile-queue counters (zeroed by launch_ffn)
 };
+constexpr int FFN_QUEUE_INTS = 8;
 constexpr int kMaxExperts = 1024;
 // mode: FFN_DOWN (out = x . w^T), FFN_GATEUP (out = SiLU(x . w0^T) * (x . w1^T)),
 // FFN_GATEUP_BWD (a = x . w0^T, b = x . w1^T recomputed; with dh read from P.dh,
