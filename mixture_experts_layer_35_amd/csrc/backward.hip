@@ -924,8 +924,7 @@ __global__ __launch_bounds__(WF8_NT) void wgrad_fp8_kernel(const WgradArgs a, in
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                part[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(fr[i], fr[4 + j], f32x4{0, 0, 0, 0}, 0,
-                                                                              0, 0, 127, 0, 127);
+                part[i][j] = FTraits<DT_E4M3>::mma(fr[i], fr[4 + j], f32x4{0, 0, 0, 0});
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const f32x4 sq = *(const f32x4 *)(scq + wq * 64 + i * 16 + 4 * (lane >> 4));

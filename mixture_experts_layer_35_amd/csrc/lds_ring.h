@@ -33,7 +33,9 @@ struct FTraits<DT_E4M3> {
     // one 16x16x128 MFMA covers exactly one 128-long quantisation block
     static constexpr int esz = 1;
     __device__ static f32x4 mma(i32x8 a, i32x8 b, f32x4 c) {
-        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);   // unit E8M0 scales
+        // zero scale operands give the unscaled instruction (bit-identical to unit E8M0
+        // scales, and faster to issue)
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
     }
 };
 
