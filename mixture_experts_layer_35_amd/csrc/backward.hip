@@ -718,12 +718,16 @@ __global__ void block_base_kernel(const int32_t *__restrict__ offsets, int n, in
 }
 
 // 128 x 1 tiles along the rows of segments (the FP8 weight-gradient operands):
-// workgroup (b, chunk) takes 128-row run b and 256 columns.  Segment e owns
-// rows offsets[e] .. offsets[e+1] (or e*seg_rows .. +seg_rows); its runs start
-// at its first row and are numbered from bbase[e] (or e*ceil(seg_rows/128)).
-// List row r reads source row gather[r] (or r), bf16, or e4m3 with 1 x 128
-// scales (decoded to fp32 first).  Scale = amax / 448 (1 for an all-zero
-// column), codes = e4m3(clamp(v / scale)), nearest even.
+// workgroup (b, chunk) takes 128-row run b and 2048 columns, eight adjacent
+// columns per thread (16-byte bf16 or 8-byte e4m3 loads, four rows in flight).
+// Segment e owns rows offsets[e] .. offsets[e+1] (or e*seg_rows .. +seg_rows);
+// its runs start at its first row and are numbered from bbase[e] (or
+// e*ceil(seg_rows/128)).  List row r reads source row gather[r] (or r), bf16, or
+// e4m3 with 1 x 128 scales (decoded to fp32 first).  Scale = amax / 448 (1 for an
+// all-zero column), codes = e4m3(clamp(v / scale)), nearest even.  The run is read
+// twice (amax, then codes); the second pass finds it in L2.
+constexpr int QC_COLS = 8;                  // columns per thread
+constexpr int QC_CHUNK = 256 * QC_COLS;     // columns per workgroup
 template <int IN>
 __global__ __launch_bounds__(256) void quant_cols_kernel(const void *__restrict__ src, const float *__restrict__ src_s,
                                                          const int32_t *__restrict__ gather,
@@ -750,22 +754,58 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const void *__restrict_
         r0 = e * seg_rows + j * 128;
         r1 = min(r0 + 128, (e + 1) * seg_rows);
     }
-    const int c = blockIdx.y * 256 + threadIdx.x;
+    const int c = blockIdx.y * QC_CHUNK + threadIdx.x * QC_COLS;
     if (c >= cols) return;
-    auto load = [&](int64_t r) -> float {
+    auto load = [&](int64_t r, float (&v)[QC_COLS]) {
         const int64_t xr = gather ? (int64_t)gather[r] : r;
         if (IN == DT_E4M3) {
-            const uint8_t code = ((const uint8_t *)src)[xr * cols + c];
-            return __builtin_amdgcn_cvt_f32_fp8((int)code, 0) * src_s[xr * (cols / 128) + c / 128];
+            const u32x2 w = *(const u32x2 *)((const uint8_t *)src + xr * cols + c);
+            const float s = src_s[xr * (cols / 128) + c / 128];
+#pragma unroll
+            for (int k = 0; k < QC_COLS; ++k)
+                v[k] = __builtin_amdgcn_cvt_f32_fp8((int)((w[k >> 2] >> (8 * (k & 3))) & 0xFF), 0) * s;
+        } else {
+            const u32x4 w = *(const u32x4 *)((const uint16_t *)src + xr * cols + c);
+#pragma unroll
+            for (int k = 0; k < QC_COLS; k += 2) {
+                v[k] = __uint_as_float(w[k >> 1] << 16);
+                v[k + 1] = __uint_as_float(w[k >> 1] & 0xFFFF0000u);
+            }
         }
-        return __uint_as_float((uint32_t)((const uint16_t *)src)[xr * cols + c] << 16);
     };
-    float amax = 0.0f;
-    for (int64_t r = r0; r < r1; ++r) amax = fmaxf(amax, fabsf(load(r)));
-    const float scale = quant_scale(amax);
-    sc[b * cols + c] = scale;
-    for (int64_t r = r0; r < r1; ++r)
-        q[r * cols + c] = (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(clamp448(load(r) / scale), 0.0f, 0, false) & 0xFF);
+    float amax[QC_COLS];
+#pragma unroll
+    for (int k = 0; k < QC_COLS; ++k) amax[k] = 0.0f;
+    for (int64_t r = r0; r < r1; r += 4) {
+        float v[4][QC_COLS];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) load(min(r + u, r1 - 1), v[u]);   // rows past the run repeat its last
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int k = 0; k < QC_COLS; ++k) amax[k] = fmaxf(amax[k], fabsf(v[u][k]));
+    }
+    float scale[QC_COLS];
+#pragma unroll
+    for (int k = 0; k < QC_COLS; ++k) scale[k] = quant_scale(amax[k]);
+    *(f32x4 *)(sc + b * cols + c) = f32x4{scale[0], scale[1], scale[2], scale[3]};
+    *(f32x4 *)(sc + b * cols + c + 4) = f32x4{scale[4], scale[5], scale[6], scale[7]};
+    for (int64_t r = r0; r < r1; r += 4) {
+        float v[4][QC_COLS];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) load(min(r + u, r1 - 1), v[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (r + u >= r1) break;
+            u32x2 o;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                o[h] = pack_e4m3x4(clamp448(v[u][4 * h] / scale[4 * h]), clamp448(v[u][4 * h + 1] / scale[4 * h + 1]),
+                                   clamp448(v[u][4 * h + 2] / scale[4 * h + 2]),
+                                   clamp448(v[u][4 * h + 3] / scale[4 * h + 3]));
+            *(u32x2 *)(q + (r + u) * cols + c) = o;
+        }
+    }
 }
 
 // ---- FP8 weight gradient -----------------------------------------------------------
@@ -981,7 +1021,7 @@ hipError_t launch_quant_cols(int in_dt, const void *src, const float *src_s, con
                              int cols, uint8_t *q, float *sc, hipStream_t s) {
     if (max_blocks <= 0 || n_seg <= 0) return hipSuccess;
     if (max_blocks >= (1ll << 31)) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)max_blocks, (unsigned)((cols + 255) / 256));
+    const dim3 grid((unsigned)max_blocks, (unsigned)((cols + QC_CHUNK - 1) / QC_CHUNK));
     if (in_dt == DT_E4M3)
         quant_cols_kernel<DT_E4M3><<<grid, 256, 0, s>>>(src, src_s, gather, offsets, bbase, seg_rows, n_seg, cols, q,
                                                         sc);
