@@ -209,7 +209,8 @@ __global__ __launch_bounds__(BW_NT) void dgate_kernel(const void *__restrict__ u
 
 // ---- weight-gradient tile order ---------------------------------------------
 // A tile is (problem, expert, 128-wide p tile, group of 128-wide q tiles); the
-// group size wg_qgroup keeps roughly 32 reduction steps per workgroup.  Tiles
+// group size wg_qgroup keeps roughly 32 reduction steps (of the kernel's
+// step_rows rows) per workgroup.  Tiles
 // of a fixed-rows problem (the shared experts: every token, long reductions)
 // come first, one per workgroup in launch order so they spread over all XCDs
 // and start early; the routed experts' tiles follow in contiguous ranges per
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(BW_NT) void dgate_kernel(const void *__restrict__ u
 // into one or two L2s rather than all eight.
 __host__ __device__ inline int wg_qgroup(const WgradProblem &P) {
     const int nqt = P.Qdim / 128;
-    const int64_t steps = (P.rows_hint + 31) / 32;
+    const int64_t steps = (P.rows_hint + P.step_rows - 1) / P.step_rows;
     const int g = steps >= 32 ? 1 : (int)(32 / (steps > 0 ? steps : 1));
     return g < nqt ? g : nqt;
 }
@@ -1066,7 +1067,9 @@ hipError_t launch_dgate(int dt, const void *u, const int32_t *perm, const int32_
     return hipGetLastError();
 }
 
-hipError_t launch_wgrad(int dt, int pass, const WgradArgs &a, hipStream_t s) {
+hipError_t launch_wgrad(int dt, int pass, const WgradArgs &args, hipStream_t s) {
+    WgradArgs a = args;
+    for (int i = 0; i < a.nprob; ++i) a.p[i].step_rows = dt == DT_E4M3 ? WF8_R : 32;
     int64_t tiles = 0;
     for (int i = 0; i < a.nprob; ++i) tiles += wg_tiles(a.p[i]);
     if (tiles <= 0) return hipSuccess;
