@@ -400,7 +400,7 @@ def main():
     cpu = None
     if args.cpu_tokens > 0:
         cpu = cpu_baseline(cfg, inp, args.cpu_tokens) if bw is None else \
-            cpu_baseline_backward(cfg, inp, max(1, args.cpu_tokens // 8))
+            cpu_baseline_backward(cfg, inp, max(1, args.cpu_tokens // 2))
 
     wl = ("%s: DeepSeekMoE layer %s, T=%d tokens, d=%d, %d routed + %d shared SwiGLU experts (I=%d), "
           "%d groups / top-%d groups / top-%d experts, %s" % (cfg.name, "forward" if bw is None else
