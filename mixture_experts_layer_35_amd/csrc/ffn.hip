@@ -206,6 +206,50 @@ __device__ __forceinline__ void compute_step(const char *st, const float *sc, f3
             __builtin_amdgcn_sched_barrier(0);
         }
     };
+    if constexpr (DT == DT_E4M3) {
+        constexpr int CB = Fr::CB;
+        // Fragment addresses: a lane reads chunks c = 2 (lane >> 4) and c + 1 of its row, in
+        // slots c ^ swz(row) and (c ^ swz(row)) ^ 1.  swz depends on row bits 0-3 only, so the
+        // 16-row blocks of a wave share one pair of lane offsets and differ by constants.
+        const int r15 = lane & 15, c2 = 2 * (lane >> 4);
+        const int arow = (GATEUP ? wf * (BF / WF) : wf * WRW) + r15, brow = WR + wm * 16 + r15;
+        const int alo = arow * CB + ((c2 ^ swz<CB>(arow)) << 4), blo = brow * CB + ((c2 ^ swz<CB>(brow)) << 4);
+        const char *a0 = st + alo, *a1 = st + (alo ^ 16), *b0 = st + blo, *b1 = st + (blo ^ 16);
+        auto frag = [](const char *lo, const char *hi, int delta) {
+            const i32x4 x = *(const i32x4 *)(lo + delta), y = *(const i32x4 *)(hi + delta);
+            return i32x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+        };
+        i32x8 af[RB];
+#pragma unroll
+        for (int i = 0; i < RB; ++i) {
+            // gate/up: first half of the wave's blocks are gate rows, second half the matching up rows
+            const int drow = GATEUP ? ((i < RB / 2) ? i * 16 : BF + (i - RB / 2) * 16) : i * 16;
+            af[i] = frag(a0, a1, drow * CB);
+        }
+        const float sw0 = sc[BM], sw1 = sc[BM + 1];
+        // down: the wave's rows sit in the first or the second 128-row block
+        const float swd = ((wf * WRW) >= 128) ? sw1 : sw0;
+        const float *scb = sc + wm * 16 + r15;
+#pragma unroll
+        for (int j = 0; j < NTB; ++j) {
+            const i32x8 bfr = frag(b0, b1, j * WM * 16 * CB);
+            const float sa = scb[j * WM * 16];
+            // the block's products first, then their scaling: the scaling of one
+            // product then waits only for that product, not for a chain of them
+            f32x4 part[RB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) part[i] = Tr::mma(af[i], bfr, f32x4{0, 0, 0, 0});
+            const float c0 = sa * sw0, c1 = sa * sw1, cd = sa * swd;
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const float cc = GATEUP ? ((i >= RB / 2) ? c1 : c0) : cd;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[i][j][q] += part[i][q] * cc;
+            }
+            group_dma(j);
+        }
+        return;
+    }
 #pragma unroll
     for (int s = 0; s < Fr::kSub; ++s) {
         typename Fr::t af[RB];
@@ -488,7 +532,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
             for (int kt = 0; kt < KT; ++kt) {
                 // step kt has landed once at most the later steps' loads are outstanding
                 if (producer) {
-                    if (kt + S - 2 < KT) wait_vmcnt_dyn(nlive * (S - 2));
+                    if (kt + S - 2 < KT) wait_vmcnt_dyn(__builtin_amdgcn_readfirstlane(nlive * (S - 2)));
                     else wait_vmcnt<0>();
                 }
                 cta_barrier();
