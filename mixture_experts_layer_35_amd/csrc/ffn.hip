@@ -250,6 +250,37 @@ __device__ __forceinline__ void compute_step(const char *st, const float *sc, f3
         }
         return;
     }
+    if constexpr (DT == DT_BF16) {
+        constexpr int CB = Fr::CB;
+        // As for e4m3: a lane reads chunk g = lane >> 4 (sub-step 0) and g + 4 (sub-step 1),
+        // in slots g ^ swz(row) and (g ^ swz(row)) ^ 4, one lane offset per operand and sub-step.
+        const int r15 = lane & 15, g = lane >> 4;
+        const int arow = (GATEUP ? wf * (BF / WF) : wf * WRW) + r15, brow = WR + wm * 16 + r15;
+        const int alo = arow * CB + ((g ^ swz<CB>(arow)) << 4), blo = brow * CB + ((g ^ swz<CB>(brow)) << 4);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const char *as = st + (s ? (alo ^ 64) : alo), *bs = st + (s ? (blo ^ 64) : blo);
+            bf16x8 af[RB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const int drow = GATEUP ? ((i < RB / 2) ? i * 16 : BF + (i - RB / 2) * 16) : i * 16;
+                af[i] = *(const bf16x8 *)(as + drow * CB);
+            }
+            bf16x8 bfr[NTB];
+#pragma unroll
+            for (int j = 0; j < NTB; ++j) bfr[j] = *(const bf16x8 *)(bs + j * WM * 16 * CB);
+            // every read above stays ahead of the first product; LDS returns in order, so each
+            // group of products waits only for its own operands
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < NTB; ++j) {
+#pragma unroll
+                for (int i = 0; i < RB; ++i) acc[i][j] = Tr::mma(af[i], bfr[j], acc[i][j]);
+                group_dma(s * NTB + j);
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int s = 0; s < Fr::kSub; ++s) {
         typename Fr::t af[RB];
