@@ -820,7 +820,7 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const void *__restrict_
 // 8-byte pieces addressed by lanes 2j+a (j = 0..7); four reads give a lane the 32
 // consecutive rows of its operand.  Staged rows are 128 bytes; their 16-byte chunks sit
 // in slots XOR-permuted by wf8_h so the 32 rows of one read spread over all banks.
-constexpr int WF8_S = 3;                                   // ring stages
+constexpr int WF8_S = 2;                                   // ring stages (two workgroups per CU)
 constexpr int WF8_R = 128;                                 // rows per step (one quantisation run)
 constexpr int WF8_PB = WF8_R * WG_T;                       // one operand's codes of a step (16 KB)
 constexpr int WF8_STAGE = 2 * WF8_PB + 2 * WG_T * 4;       // + the run's P and Q column scales
@@ -836,7 +836,7 @@ __device__ __forceinline__ wf8_v2i lds_tr8(const char *p) {
 }
 
 template <int PASS>
-__global__ __launch_bounds__(WF8_NT) void wgrad_fp8_kernel(const WgradArgs a, int64_t nlead, int64_t ntiles) {
+__global__ __launch_bounds__(WF8_NT, 3) void wgrad_fp8_kernel(const WgradArgs a, int64_t nlead, int64_t ntiles) {
     extern __shared__ __align__(1024) char wsm[];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const bool producer = wid >= 4;
@@ -921,34 +921,35 @@ __global__ __launch_bounds__(WF8_NT) void wgrad_fp8_kernel(const WgradArgs a, in
     }
     // fragment reads: lane (group g, L = 2jj + aa) addresses row 32g + 8t + jj, bytes col0 + 8aa .. +7
     const int g = lane >> 4, jj = (lane & 15) >> 1, aa = lane & 1;
-    int ofs[8][4];
+    // wf8_h(r) reads row bits 1, 2 and 5, which the read index t (rows 8t apart) leaves
+    // alone: one offset per fragment, the four reads 8 rows (1 KB) apart
+    int ofs[8];
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
         const int col0 = f < 4 ? wq * 64 + f * 16 : wp * 64 + (f - 4) * 16;
         const int base = f < 4 ? WF8_PB : 0;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int r = 32 * g + 8 * t + jj;
-            ofs[f][t] = base + r * WG_T + (((col0 >> 4) ^ wf8_h(r)) << 4) + 8 * aa;
-        }
+        const int r = 32 * g + jj;
+        ofs[f] = base + r * WG_T + (((col0 >> 4) ^ wf8_h(r)) << 4) + 8 * aa;
     }
     const int vlast = M - (nsteps - 1) * WF8_R;
     int qt = 0, st = 0, slot = 0;
     for (int x = 0; x < total; ++x) {
         cta_barrier();
         const char *sb = wsm + slot * WF8_STAGE;
-        i32x8 fr[8];
-#pragma unroll
-        for (int f = 0; f < 8; ++f) {
+        auto frag = [&](int f) {
             wf8_v2i v[4];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] = lds_tr8(sb + ofs[f][t]);
-            fr[f] = i32x8{v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
-        }
+            for (int t = 0; t < 4; ++t) v[t] = lds_tr8(sb + ofs[f] + 8 * t * WG_T);
+            return i32x8{v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
+        };
+        // P fragments for the whole step, Q fragments one at a time below
+        i32x8 fp[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) fp[j] = frag(4 + j);
         if (st == nsteps - 1 && vlast < WF8_R) {
             // rows past the expert: zero P's bytes (lane holds rows 32g .. 32g+31, low byte first)
 #pragma unroll
-            for (int f = 4; f < 8; ++f)
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
                 for (int w = 0; w < 8; ++w) {
                     const int r = 32 * g + 4 * w;
@@ -956,25 +957,26 @@ __global__ __launch_bounds__(WF8_NT) void wgrad_fp8_kernel(const WgradArgs a, in
 #pragma unroll
                     for (int bt = 0; bt < 4; ++bt)
                         if (r + bt < vlast) m |= 0xFFu << (8 * bt);
-                    fr[f][w] &= (int)m;
+                    fp[j][w] &= (int)m;
                 }
         }
         const float *scp = (const float *)(sb + 2 * WF8_PB), *scq = scp + WG_T;
-        f32x4 part[4][4];
+        float sp[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                part[i][j] = FTraits<DT_E4M3>::mma(fr[i], fr[4 + j], f32x4{0, 0, 0, 0});
+        for (int j = 0; j < 4; ++j) sp[j] = scp[wp * 64 + j * 16 + (lane & 15)];
+        // one row of four products at a time, then its scaling: four partial sums live
+        // instead of sixteen, which keeps the kernel at three waves per SIMD
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+            const i32x8 fq = frag(i);
+            f32x4 part[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part[j] = FTraits<DT_E4M3>::mma(fq, fp[j], f32x4{0, 0, 0, 0});
             const f32x4 sq = *(const f32x4 *)(scq + wq * 64 + i * 16 + 4 * (lane >> 4));
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float sp = scp[wp * 64 + j * 16 + (lane & 15)];
+            for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int v = 0; v < 4; ++v) acc[i][j][v] += part[i][j][v] * (sq[v] * sp);
-            }
+                for (int v = 0; v < 4; ++v) acc[i][j][v] += part[j][v] * (sq[v] * sp[j]);
         }
         slot = slot + 1 == WF8_S ? 0 : slot + 1;
         if (++st == nsteps) {
