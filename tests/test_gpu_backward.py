@@ -167,6 +167,15 @@ def test_backward_matches_oracle(moe, orc, dtype, T, d, Nr, G, Mg, K, Ns, I, fla
     run_case(moe, orc, cfg, seed=T + d + K, flags=flags, rs=rs)
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp8"])
+def test_backward_at_the_shape_limits(moe, orc, dtype):
+    """Every shape limit of moe_shape at once: 1024 routed experts in 64 groups,
+    top-8 groups, top-32 experts, 8 shared experts."""
+    cfg = cfg_of(dtype, 150, 128, 1024, 64, 8, 32, 8, 128)
+    print("backward at the limits", dtype, flush=True)
+    run_case(moe, orc, cfg, seed=78)
+
+
 def test_backward_empty_expert_and_single_expert_dense(moe, orc):
     # expert 5 can never be chosen: its gradients are exactly zero
     cfg = cfg_of("bf16", 640, 256, 32, 4, 2, 4, 1, 256)

@@ -332,6 +332,19 @@ def test_forward_tiny_fp32(moe, orc, T):
     check_layer(cfg, got, ref, inp["bias"])
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp8"])
+def test_forward_at_the_shape_limits(moe, orc, dtype):
+    """Every shape limit of moe_shape at once: 1024 routed experts in 64 groups,
+    top-8 groups, top-32 experts, 8 shared experts (the e4m3 layer at the
+    smallest d and I, one 128 block each)."""
+    cfg = small_cfg(dtype, 150, d=128, Nr=1024, G=64, Mg=8, K=32, Ns=8, I=128)
+    inp = syn.layer_inputs(cfg, seed=77)
+    print("forward at the limits", dtype, flush=True)
+    got = run_forward(moe, cfg, inp)
+    ref = oracle_forward(orc, cfg, inp)
+    check_layer(cfg, got, ref, inp["bias"])
+
+
 @pytest.mark.parametrize("dtype,T,Ns,flags", [("bf16", 700, 1, 0), ("bf16", 129, 2, 1), ("bf16", 300, 0, 0),
                                               ("fp8", 500, 1, 0), ("fp8", 77, 0, 1), ("fp32", 400, 2, 1)])
 def test_forward_small_shapes(moe, orc, dtype, T, Ns, flags):
