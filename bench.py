@@ -143,6 +143,17 @@ def traffic_from_profile(cfg, kernel, backward=False):
     return float(t.group(1))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(cfg, inp, n_tokens):
     import numpy as np
     import oracle
@@ -173,6 +184,7 @@ def cpu_baseline(cfg, inp, n_tokens):
                        w_code=wcode, out_code=ocode, tokens=tokens, routed_scales=rs, shared_scales=ss)
     dt = time.perf_counter() - t0
     return {"value": round(len(tokens) / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "first %d tokens of the same %d-token batch: routing, %d routed + %d shared SwiGLU experts "
                       "each, combine (fp64 sums)%s; %.1f s" % (len(tokens), cfg.T, cfg.K, cfg.Ns,
                                                                ", activation and H quantisation (weights "
@@ -213,6 +225,7 @@ def cpu_baseline_backward(cfg, inp, n_tokens):
         oracle.moe_backward(u, inp["gate_w"], idx, routed, shared, dout, experts=none, dgate=False, dshared=False)
     dt = time.perf_counter() - t0
     return {"value": round(n / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": "input-gradient chain rule (du and dL/dg: %d routed + %d shared SwiGLU experts recomputed "
                       "and differentiated per token, fp64%s) for the first %d tokens of the %d-token batch; weight "
                       "and centroid gradients not in the sample; %.1f s" % (
@@ -385,11 +398,20 @@ def main():
         hbm_stages[name] = {"algorithmic_bytes": int(nb), "ms": round(stage_ms[name], 4), "GB/s": round(gbs, 1),
                             "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "traffic": traffic_from_profile(cfg, STAGE_KERNELS[name])}
+    # "% attainable": the layer's algorithmic flops against min(MFMA peak, AI x HBM peak),
+    # with AI over the algorithmic bytes of every stage of the step
+    fwd_alg = algorithmic(cfg, n_touched)
+    layer_bytes = sum(stage_bytes(cfg).values()) + sum(b for _, b in fwd_alg.values())
     layer_flops = T * cfg.flops_per_token
     if bw is not None:
+        layer_bytes += sum(b for _, b in alg.values())
         layer_flops += sum(f for name, (f, _) in alg.items() if name in ("bwd_dh", "bwd_swiglu", "bwd_dx",
                                                                          "wgrad_down", "wgrad_gate_up"))
     tflops = layer_flops / (ms / 1000.0) / 1e12
+    attainable = min(peak_f, layer_flops / layer_bytes * PEAK_HBM_GBS / 1000.0)
+    # per-step GPU time from the stage events (first to last event of each step)
+    step_gpu = [evs[k][0].elapsed_time(evs[k][5]) + (bevs[k][0].elapsed_time(bevs[k][9]) if bevs else 0.0)
+                for k in range(args.steps)]
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         b = torch.empty_like(a)
@@ -428,6 +450,10 @@ def main():
                    "n_groups": cfg.G, "topk_groups": cfg.Mg, "inter": cfg.I, "parallelism": "single GPU"},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / peak_f, 4),
+        "attainable_tflops": round(attainable, 1),
+        "attainable_frac": round(tflops / attainable, 4),
+        "step_gpu_ms": {"median": round(float(np.median(step_gpu)), 4), "min": round(float(np.min(step_gpu)), 4),
+                        "max": round(float(np.max(step_gpu)), 4)},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "backward_stages": bwd_stages,
         "backward_ms": round(sum(bstage_ms.values()), 4) if bstage_ms else None,

@@ -332,6 +332,22 @@ def test_forward_tiny_fp32(moe, orc, T):
     check_layer(cfg, got, ref, inp["bias"])
 
 
+def test_forward_fp8_with_outlier_channels(moe, orc):
+    """Activation outliers, the case fine-grained scaling is for (§3.3): two
+    hidden channels of u scaled by 100.  Each 1 x 128 tile holding an outlier
+    gets its own scale, so the other tiles keep their precision; the layer still
+    meets the fp8 bar against the oracle applying the same quantisation."""
+    cfg = small_cfg("fp8", 300, d=512, Nr=32, G=4, Mg=2, K=4, Ns=1, I=256)
+    inp = syn.layer_inputs(cfg, seed=91)
+    u = dec(inp["u"])
+    u[:, [7, 300]] *= 100.0
+    inp["u"] = syn.to_bf16_bits(u.astype(np.float32))
+    print("forward fp8 outliers", flush=True)
+    got = run_forward(moe, cfg, inp)
+    ref = oracle_forward(orc, cfg, inp)
+    check_layer(cfg, got, ref, inp["bias"])
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16", "fp8"])
 def test_forward_at_the_shape_limits(moe, orc, dtype):
     """Every shape limit of moe_shape at once: 1024 routed experts in 64 groups,
