@@ -415,15 +415,15 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
         T.r0 = mi * mq + min(mi, mr);
         T.valid = mq + (mi < mr ? 1 : 0);
         T.n0 = nt * BF;
-        // Token blocks this tile needs per wave: NTB = ceil(valid / (16*WM)) rounded up to an
-        // even count, so the specialised loops below cover 64, 128, 192 or 256 tokens.  Stage
+        // Token blocks this tile needs per wave: NTB = ceil(valid / (16*WM)), so the specialised
+        // loops below cover 32, 64, ..., 256 tokens (padding under 32 rows per tile).  Stage
         // layout: WR weight rows, then the token rows, then (fp8) the scales.  Staging only the
         // valid rows (rounded to whole instructions) keeps stages small; the token blocks then
         // read up to `over` bytes past the last slot, which the ring keeps free.  When that
         // still leaves only two slots, the stage holds all 32*NTB token rows instead (rows past
         // the valid ones repeat the last valid token and are never stored) so that every
         // producer issues the same loads each step, spread over its products.
-        T.ntb = min(TB, ((T.valid + 16 * WM - 1) / (16 * WM) + 1) & ~1);
+        T.ntb = min(TB, (T.valid + 16 * WM - 1) / (16 * WM));
         {
             const int tmin = (T.valid + RPI - 1) / RPI * RPI, tfull = T.ntb * 16 * WM;
             const int over = (tfull - tmin) * CB;
@@ -595,10 +595,16 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
             if (cur.spread) kloop(ntb, std::true_type{});
             else kloop(ntb, std::false_type{});
         };
-        if (cur.ntb == 2) kloop_s(std::integral_constant<int, 2>{});
-        else if (cur.ntb == 4) kloop_s(std::integral_constant<int, 4>{});
-        else if (cur.ntb == 6) kloop_s(std::integral_constant<int, 6>{});
-        else kloop_s(std::integral_constant<int, TB>{});
+        switch (cur.ntb) {
+            case 1: kloop_s(std::integral_constant<int, 1>{}); break;
+            case 2: kloop_s(std::integral_constant<int, 2>{}); break;
+            case 3: kloop_s(std::integral_constant<int, 3>{}); break;
+            case 4: kloop_s(std::integral_constant<int, 4>{}); break;
+            case 5: kloop_s(std::integral_constant<int, 5>{}); break;
+            case 6: kloop_s(std::integral_constant<int, 6>{}); break;
+            case 7: kloop_s(std::integral_constant<int, 7>{}); break;
+            default: kloop_s(std::integral_constant<int, TB>{}); break;
+        }
 
         // Every wave is done with the ring: start the next tile's loads, then
         // write this tile's results while they are in flight.
