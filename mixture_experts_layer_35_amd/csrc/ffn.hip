@@ -291,42 +291,18 @@ __device__ __forceinline__ void compute_step(const char *st, const float *sc, f3
                                     : wf * WRW + i * 16;
             af[i] = Fr::load(st, wrow + (lane & 15), s, lane);
         }
-        if (DT == DT_E4M3) {
-            const float sw0 = sc[BM], sw1 = sc[BM + 1];
-            // down: the wave's rows sit in the first or the second 128-row block
-            const float swd = ((wf * WRW) >= 128) ? sw1 : sw0;
+        // fp32 (bf16 and e4m3 take the paths above)
+        typename Fr::t bfr[NTB];
 #pragma unroll
-            for (int j = 0; j < NTB; ++j) {
-                const int tok = (j * WM + wm) * 16 + (lane & 15);
-                const typename Fr::t bfr = Fr::load(st, WR + tok, s, lane);
-                const float sa = sc[tok];
-                // the block's products first, then their scaling: the scaling of one
-                // product then waits only for that product, not for a chain of them
-                f32x4 part[RB];
+        for (int j = 0; j < NTB; ++j) bfr[j] = Fr::load(st, WR + (j * WM + wm) * 16 + (lane & 15), s, lane);
+        // every read above stays ahead of the first product; LDS returns in order, so each
+        // group of products waits only for its own operands
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < RB; ++i) part[i] = Tr::mma(af[i], bfr, f32x4{0, 0, 0, 0});
-                const float c0 = sa * sw0, c1 = sa * sw1, cd = sa * swd;
+        for (int j = 0; j < NTB; ++j) {
 #pragma unroll
-                for (int i = 0; i < RB; ++i) {
-                    const float cc = GATEUP ? ((i >= RB / 2) ? c1 : c0) : cd;
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[i][j][q] += part[i][q] * cc;
-                }
-                group_dma(s * NTB + j);
-            }
-        } else {
-            typename Fr::t bfr[NTB];
-#pragma unroll
-            for (int j = 0; j < NTB; ++j) bfr[j] = Fr::load(st, WR + (j * WM + wm) * 16 + (lane & 15), s, lane);
-            // every read above stays ahead of the first product; LDS returns in order, so each
-            // group of products waits only for its own operands
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < NTB; ++j) {
-#pragma unroll
-                for (int i = 0; i < RB; ++i) acc[i][j] = Tr::mma(af[i], bfr[j], acc[i][j]);
-                group_dma(s * NTB + j);
-            }
+            for (int i = 0; i < RB; ++i) acc[i][j] = Tr::mma(af[i], bfr[j], acc[i][j]);
+            group_dma(s * NTB + j);
         }
     }
 }
