@@ -224,7 +224,7 @@ __host__ __device__ inline int wg_qgroup(const WgradProblem &P) {
 }
 __host__ __device__ inline int64_t wg_tiles(const WgradProblem &P) {
     const int nqt = P.Qdim / 128, g = wg_qgroup(P);
-    return (int64_t)P.n_exp * (P.Pdim / 128) * ((nqt + g - 1) / g);
+    return (int64_t)P.n_exp * (P.Pdim / P.p_tile) * ((nqt + g - 1) / g);
 }
 
 struct WgTile {
@@ -251,11 +251,11 @@ __device__ inline bool wg_decode(const WgradArgs &a, int64_t nlead, int64_t ntil
         T.pi = 1;
     }
     const WgradProblem &P = T.pi ? a.p[1] : a.p[0];
-    const int ptiles = P.Pdim / 128, nqt = P.Qdim / 128, g = wg_qgroup(P);
+    const int ptiles = P.Pdim / P.p_tile, nqt = P.Qdim / 128, g = wg_qgroup(P);
     const int ngroups = (nqt + g - 1) / g;
     T.e = (int)(t / ((int64_t)ptiles * ngroups));
     const int r = (int)(t - (int64_t)T.e * ptiles * ngroups);
-    T.p0 = (r / ngroups) * 128;
+    T.p0 = (r / ngroups) * P.p_tile;
     T.qt0 = (r % ngroups) * g;
     T.nq = min(g, nqt - T.qt0);
     return true;
@@ -483,12 +483,15 @@ __global__ __launch_bounds__(BW_NT) void wgrad_kernel(const WgradArgs a, int64_t
 // over all banks.  For a gathered Q operand the row indices of a step travel
 // in the ring S - 1 steps ahead of their step, so the producer reads them from
 // LDS instead of waiting on global memory.
+// PW = 2: the p tile is 256 wide (two 128-value halves staged side by side, eight MFMA
+// waves), which cuts the operand rows each output value costs by a quarter; it is used
+// when every p dimension and split of the launch is a multiple of 256.
 constexpr int WGB_S = 4;                                  // ring stages
-constexpr int WGB_PB = WG_R * WG_T * 2;                   // one operand's rows of a step (8 KB)
+constexpr int WGB_PB = WG_R * WG_T * 2;                   // one operand half's rows of a step (8 KB)
 constexpr int WGB_IDX = 256;                              // gather indices of a later step
-constexpr int WGB_STAGE = 2 * WGB_PB + WGB_IDX;
-constexpr int WGB_LDS = WGB_S * WGB_STAGE;
-constexpr int WGB_NT = 384;
+template <int PW> constexpr int wgb_stage() { return (PW + 1) * WGB_PB + WGB_IDX; }
+template <int PW> constexpr int wgb_lds() { return WGB_S * wgb_stage<PW>(); }
+template <int PW> constexpr int wgb_nt() { return 64 * (4 * PW + 2); }
 
 // slot permutation of a staged row's 16 chunks (an even XOR keeps chunk pairs together)
 __device__ __forceinline__ int wgb_h(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
@@ -514,12 +517,13 @@ __device__ __forceinline__ void lds_u32_x4(uint32_t (&v)[4], uint32_t a0, uint32
 }
 
 // PASS only separates the down and gate/up instantiations in profiles.
-template <int PASS>
-__global__ __launch_bounds__(WGB_NT) void wgrad_bf16_kernel(const WgradArgs a, int64_t nlead, int64_t ntiles) {
+template <int PASS, int PW>
+__global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArgs a, int64_t nlead, int64_t ntiles) {
     extern __shared__ __align__(1024) char wsm[];
+    constexpr int STAGE = wgb_stage<PW>(), QB = PW * WGB_PB;   // Q rows follow the PW halves of P
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const bool producer = wid >= 4;
-    const int wp = (wid >> 1) & 1, wq = wid & 1;
+    const bool producer = wid >= 4 * PW;
+    const int wp = (wid >> 1) & (2 * PW - 1), wq = wid & 1;
 
     WgTile T;
     if (!wg_decode(a, nlead, ntiles, blockIdx.x, T)) return;
@@ -542,7 +546,7 @@ __global__ __launch_bounds__(WGB_NT) void wgrad_bf16_kernel(const WgradArgs a, i
         // instruction n (0..7) of an operand covers rows 4n .. 4n+3 of the step; producer k issues
         // n = 2m + k.  This lane: row 4n + lane/16, chunk slot lane%16 holding data chunk
         // (lane%16) ^ h(row).  Row pointers are formed once and advanced by a uniform offset per step.
-        const int k = wid - 4, drow = lane >> 4, pchunk = lane & 15;
+        const int k = wid - 4 * PW, drow = lane >> 4, pchunk = lane & 15;
         const bool gather = qg != nullptr;
         const int32_t *const qgb = gather ? qg + rb : nullptr;
         const int64_t prb = p_local ? 0 : rb, qrb = q_local ? 0 : rb;
@@ -557,11 +561,11 @@ __global__ __launch_bounds__(WGB_NT) void wgrad_bf16_kernel(const WgradArgs a, i
             plast[m] = Pp + (prb + M - 1) * P_ld + p0 + cofs[m];   // rows past the expert repeat its last
             qlast[m] = Qp + (qrb + M - 1) * Q_ld + cofs[m];
         }
-        auto nops = [&](int y) { return 8 + ((k == 0 && gather && y + WGB_S - 1 < total) ? 1 : 0); };
+        auto nops = [&](int y) { return 4 * (PW + 1) + ((k == 0 && gather && y + WGB_S - 1 < total) ? 1 : 0); };
         int yq = 0, ys = 0;   // q tile and step of the next step to issue
         // step y into ring slot y % S; qrow: gathered Q rows of this lane's 4 rows (if gather)
         auto issue = [&](int y, const int (&qrow)[4]) {
-            char *slot = wsm + (y % WGB_S) * WGB_STAGE;
+            char *slot = wsm + (y % WGB_S) * STAGE;
             const int q0 = (qt0 + yq) * WG_T, r0 = ys * WG_R;
             const bool ragged = r0 + WG_R > M;
             const int64_t po = (int64_t)r0 * P_ld, qo = (int64_t)r0 * Q_ld + q0;
@@ -569,16 +573,18 @@ __global__ __launch_bounds__(WGB_NT) void wgrad_bf16_kernel(const WgradArgs a, i
             for (int m = 0; m < 4; ++m) {
                 const int n = 2 * m + k;
                 const bool past = ragged && r0 + 4 * n + drow >= M;
-                dma16(past ? plast[m] : pbase[m] + po, slot + n * 1024);
+#pragma unroll
+                for (int h = 0; h < PW; ++h)
+                    dma16((past ? plast[m] : pbase[m] + po) + h * WG_T, slot + h * WGB_PB + n * 1024);
                 const uint16_t *qs;
                 if (gather) qs = Qp + (int64_t)qrow[m] * Q_ld + q0 + cofs[m];
                 else qs = past ? qlast[m] + q0 : qbase[m] + qo;
-                dma16(qs, slot + WGB_PB + n * 1024);
+                dma16(qs, slot + QB + n * 1024);
             }
             if (k == 0 && gather && y + WGB_S - 1 < total) {
                 // row indices of step y + S - 1 ride along (64 words, the first 32 used)
                 const int ys2 = (ys + WGB_S - 1) % nsteps;
-                dma4(qgb + min(ys2 * WG_R + (lane & 31), M - 1), slot + 2 * WGB_PB);
+                dma4(qgb + min(ys2 * WG_R + (lane & 31), M - 1), slot + QB + WGB_PB);
             }
             if (++ys == nsteps) { ys = 0; ++yq; }
         };
@@ -598,7 +604,7 @@ __global__ __launch_bounds__(WGB_NT) void wgrad_bf16_kernel(const WgradArgs a, i
             const int y = x + WGB_S - 1;
             if (y < total) {
                 if (gather) {
-                    const uint32_t ib = (uint32_t)(uintptr_t)(wsm + (x % WGB_S) * WGB_STAGE + 2 * WGB_PB);
+                    const uint32_t ib = (uint32_t)(uintptr_t)(wsm + (x % WGB_S) * STAGE + QB + WGB_PB);
                     uint32_t v[4];
                     lds_u32_x4(v, ib + 4 * (4 * k + drow), ib + 4 * (4 * (2 + k) + drow), ib + 4 * (4 * (4 + k) + drow),
                                ib + 4 * (4 * (6 + k) + drow));
@@ -645,10 +651,11 @@ __global__ __launch_bounds__(WGB_NT) void wgrad_bf16_kernel(const WgradArgs a, i
     int ofs[16];
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
-        const int col0 = f < 4 ? wq * 64 + f * 16 : wp * 64 + (f - 4) * 16;
+        // P values of this wave: half wp / 2 of the staged p tile, columns (wp % 2) * 64 ..
+        const int col0 = f < 4 ? wq * 64 + f * 16 : (wp & 1) * 64 + (f - 4) * 16;
         const int c = (col0 + 4 * aa) >> 3, off = 8 * (aa & 1);
         const int k0 = 8 * g + jj, k1 = k0 + 4;
-        const int base = f < 4 ? WGB_PB : 0;
+        const int base = f < 4 ? QB : (wp >> 1) * WGB_PB;
         ofs[2 * f] = base + k0 * 256 + ((c ^ wgb_h(k0)) << 4) + off;
         ofs[2 * f + 1] = base + k1 * 256 + ((c ^ wgb_h(k1)) << 4) + off;
     }
@@ -656,7 +663,7 @@ __global__ __launch_bounds__(WGB_NT) void wgrad_bf16_kernel(const WgradArgs a, i
     int qt = 0, st = 0, slot = 0;
     for (int x = 0; x < total; ++x) {
         cta_barrier();                           // step x has landed
-        const char *sb = wsm + slot * WGB_STAGE;
+        const char *sb = wsm + slot * STAGE;
         wgb_v4s r[16];
 #pragma unroll
         for (int f = 0; f < 16; ++f) r[f] = lds_tr16(sb + ofs[f]);
@@ -1071,13 +1078,16 @@ hipError_t launch_dgate(int dt, const void *u, const int32_t *perm, const int32_
 
 hipError_t launch_wgrad(int dt, int pass, const WgradArgs &args, hipStream_t s) {
     WgradArgs a = args;
-    for (int i = 0; i < a.nprob; ++i) a.p[i].step_rows = dt == DT_E4M3 ? WF8_R : 32;
+    for (int i = 0; i < a.nprob; ++i) {
+        a.p[i].step_rows = dt == DT_E4M3 ? WF8_R : 32;
+        a.p[i].p_tile = 128;
+    }
     int64_t tiles = 0;
     for (int i = 0; i < a.nprob; ++i) tiles += wg_tiles(a.p[i]);
     if (tiles <= 0) return hipSuccess;
     // a leading fixed-rows problem is spread over all XCDs (see wg_decode)
-    const int64_t nlead = (a.nprob > 1 && !a.p[0].offsets) ? wg_tiles(a.p[0]) : 0;
-    const int64_t grid = (nlead + 7) / 8 * 8 + (tiles - nlead + 7) / 8 * 8;
+    int64_t nlead = (a.nprob > 1 && !a.p[0].offsets) ? wg_tiles(a.p[0]) : 0;
+    int64_t grid = (nlead + 7) / 8 * 8 + (tiles - nlead + 7) / 8 * 8;
     if (grid >= (1ll << 31)) return hipErrorInvalidValue;
     if (dt == DT_F32) {
         if (pass) wgrad_kernel<DT_F32, 1><<<(unsigned)grid, BW_NT, 0, s>>>(a, nlead, tiles);
@@ -1096,18 +1106,33 @@ hipError_t launch_wgrad(int dt, int pass, const WgradArgs &args, hipStream_t s) 
         if (pass) wgrad_fp8_kernel<1><<<(unsigned)grid, WF8_NT, WF8_LDS, s>>>(a, nlead, tiles);
         else wgrad_fp8_kernel<0><<<(unsigned)grid, WF8_NT, WF8_LDS, s>>>(a, nlead, tiles);
     } else {
+        // the 256-wide p tile needs every p dimension and split of the launch on 256-value boundaries
+        bool wide = true;
+        for (int i = 0; i < a.nprob; ++i) wide = wide && a.p[i].Pdim % 256 == 0 && a.p[i].split % 256 == 0;
+        if (wide) {
+            for (int i = 0; i < a.nprob; ++i) a.p[i].p_tile = 256;
+            tiles = 0;
+            for (int i = 0; i < a.nprob; ++i) tiles += wg_tiles(a.p[i]);
+            nlead = (a.nprob > 1 && !a.p[0].offsets) ? wg_tiles(a.p[0]) : 0;
+            grid = (nlead + 7) / 8 * 8 + (tiles - nlead + 7) / 8 * 8;
+        }
         static std::once_flag once;
         static hipError_t attr = hipSuccess;
         std::call_once(once, [] {
-            attr = hipFuncSetAttribute((const void *)wgrad_bf16_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       WGB_LDS);
-            if (attr == hipSuccess)
-                attr = hipFuncSetAttribute((const void *)wgrad_bf16_kernel<1>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, WGB_LDS);
+            const void *k[4] = {(const void *)wgrad_bf16_kernel<0, 1>, (const void *)wgrad_bf16_kernel<1, 1>,
+                                (const void *)wgrad_bf16_kernel<0, 2>, (const void *)wgrad_bf16_kernel<1, 2>};
+            const int lds[4] = {wgb_lds<1>(), wgb_lds<1>(), wgb_lds<2>(), wgb_lds<2>()};
+            for (int i = 0; i < 4 && attr == hipSuccess; ++i)
+                attr = hipFuncSetAttribute(k[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds[i]);
         });
         if (attr != hipSuccess) return attr;
-        if (pass) wgrad_bf16_kernel<1><<<(unsigned)grid, WGB_NT, WGB_LDS, s>>>(a, nlead, tiles);
-        else wgrad_bf16_kernel<0><<<(unsigned)grid, WGB_NT, WGB_LDS, s>>>(a, nlead, tiles);
+        if (wide) {
+            if (pass) wgrad_bf16_kernel<1, 2><<<(unsigned)grid, wgb_nt<2>(), wgb_lds<2>(), s>>>(a, nlead, tiles);
+            else wgrad_bf16_kernel<0, 2><<<(unsigned)grid, wgb_nt<2>(), wgb_lds<2>(), s>>>(a, nlead, tiles);
+        } else {
+            if (pass) wgrad_bf16_kernel<1, 1><<<(unsigned)grid, wgb_nt<1>(), wgb_lds<1>(), s>>>(a, nlead, tiles);
+            else wgrad_bf16_kernel<0, 1><<<(unsigned)grid, wgb_nt<1>(), wgb_lds<1>(), s>>>(a, nlead, tiles);
+        }
     }
     return hipGetLastError();
 }

@@ -96,6 +96,7 @@ struct WgradProblem {
     void *out0, *out1;
     int64_t rows_hint;      // typical rows per expert (sizes the work per workgroup)
     int step_rows;          // rows per reduction step of the kernel (set by launch_wgrad)
+    int p_tile;             // width of a workgroup's p tile, 128 or 256 (set by launch_wgrad)
     // e4m3 operands: 128 x 1 column scales per 128-row run ([run][Pdim], [run][Qdim]); the
     // expert's first run is bbase[e] (offsets problems) or e * ceil(rows_fixed / 128); an
     // operand read with p_local / q_local starts at run 0
