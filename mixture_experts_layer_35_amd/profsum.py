@@ -28,7 +28,9 @@ def short_name(full: str) -> str:
     m = re.search(r"ffn_kernel<(\d+), (\d+)>", full)
     if m:
         return {0: "ffn_down", 1: "ffn_gate_up", 2: "bwd_swiglu", 3: "bwd_dh", 4: "bwd_dx"}[int(m.group(2))]
-    m = re.search(r"wgrad_(?:bf16_|fp8_)?kernel<(?:\d+, )?(\d+)>", full)
+    # the pass (0: dW_down, 1: dW_gate / dW_up) is the first template argument of the bf16
+    # and e4m3 kernels and the second of the fp32 one
+    m = re.search(r"wgrad_(?:bf16|fp8)_kernel<(\d+)", full) or re.search(r"wgrad_kernel<\d+, (\d+)>", full)
     if m:
         return "wgrad_gate_up" if m.group(1) == "1" else "wgrad_down"
     if "copyBuffer" in full:
