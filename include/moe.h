@@ -39,8 +39,10 @@
  *     contiguous).  bf16 is stored as its 16-bit pattern; e4m3 is OCP E4M3FN
  *     (largest finite 448) in one byte.
  *   - Inputs must be finite; NaN and infinity are not checked.
- *   - Calls on different streams that share a buffer race; the library holds
- *     no global mutable state, so calls on different data may overlap.
+ *   - Calls on different streams that share a buffer race, workspaces
+ *     included (a workspace holds intermediate results and the expert
+ *     kernel's tile-queue counters); the library holds no global mutable
+ *     state, so calls on different data may overlap.
  */
 #ifndef MOE_H_
 #define MOE_H_
