@@ -830,9 +830,11 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const void *__restrict_
 constexpr int WF8_S = 2;                                   // ring stages (two workgroups per CU)
 constexpr int WF8_R = 128;                                 // rows per step (one quantisation run)
 constexpr int WF8_PB = WF8_R * WG_T;                       // one operand's codes of a step (16 KB)
-constexpr int WF8_STAGE = 2 * WF8_PB + 2 * WG_T * 4;       // + the run's P and Q column scales
-constexpr int WF8_LDS = WF8_S * WF8_STAGE;
-constexpr int WF8_NT = 384;
+// PW = 2: 256-wide p tiles as in the bf16 kernel (two staged halves, eight MFMA waves).
+// Scale area per stage: [P half 0 | Q | P half 1 | unused], 512 bytes each.
+template <int PW> constexpr int wf8_stage() { return (PW + 1) * WF8_PB + PW * 2 * WG_T * 4; }
+template <int PW> constexpr int wf8_lds() { return WF8_S * wf8_stage<PW>(); }
+template <int PW> constexpr int wf8_nt() { return 64 * (4 * PW + 2); }
 
 __device__ __forceinline__ int wf8_h(int r) { return ((r >> 1) & 3) | (((r >> 5) & 1) << 2); }
 
@@ -842,12 +844,13 @@ __device__ __forceinline__ wf8_v2i lds_tr8(const char *p) {
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) wf8_v2i *)p);
 }
 
-template <int PASS>
-__global__ __launch_bounds__(WF8_NT, 3) void wgrad_fp8_kernel(const WgradArgs a, int64_t nlead, int64_t ntiles) {
+template <int PASS, int PW>
+__global__ __launch_bounds__(wf8_nt<PW>(), 3) void wgrad_fp8_kernel(const WgradArgs a, int64_t nlead, int64_t ntiles) {
     extern __shared__ __align__(1024) char wsm[];
+    constexpr int STAGE = wf8_stage<PW>(), QB = PW * WF8_PB, SB = (PW + 1) * WF8_PB;   // Q codes, scales
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const bool producer = wid >= 4;
-    const int wp = (wid >> 1) & 1, wq = wid & 1;
+    const bool producer = wid >= 4 * PW;
+    const int wp = (wid >> 1) & (2 * PW - 1), wq = wid & 1;
     WgTile T;
     if (!wg_decode(a, nlead, ntiles, blockIdx.x, T)) return;
     const WgradProblem &Pr = T.pi ? a.p[1] : a.p[0];
@@ -870,28 +873,32 @@ __global__ __launch_bounds__(WF8_NT, 3) void wgrad_fp8_kernel(const WgradArgs a,
         // instruction n (0..15) of an operand covers rows 8n .. 8n+7 of the step; producer k
         // issues n = 2m + k.  This lane: row 8n + lane/8, slot lane%8 holding data chunk
         // (lane%8) ^ h(row).  The run's scales: lanes 0-31 take P's 128, lanes 32-63 Q's.
-        const int k = wid - 4, drow = lane >> 3, pchunk = lane & 7;
+        const int k = wid - 4 * PW, drow = lane >> 3, pchunk = lane & 7;
         const int64_t prb = p_local ? 0 : rb, qrb = q_local ? 0 : rb;
         int yq = 0, ys = 0;
         auto issue = [&](int y) {
-            char *slot = wsm + (y % WF8_S) * WF8_STAGE;
+            char *slot = wsm + (y % WF8_S) * STAGE;
             const int q0 = (qt0 + yq) * WG_T, r0 = ys * WF8_R;
 #pragma unroll
             for (int m = 0; m < 8; ++m) {
                 const int n = 2 * m + k, kr = 8 * n + drow;
                 const int r = min(r0 + kr, M - 1);   // rows past the expert repeat its last (masked)
                 const int cofs = 16 * (pchunk ^ wf8_h(kr));
-                dma16(Pp + (prb + r) * P_ld + p0 + cofs, slot + n * 1024);
-                dma16(Qp + (qrb + r) * Q_ld + q0 + cofs, slot + WF8_PB + n * 1024);
+#pragma unroll
+                for (int h = 0; h < PW; ++h) dma16(Pp + (prb + r) * P_ld + p0 + h * WG_T + cofs, slot + h * WF8_PB + n * 1024);
+                dma16(Qp + (qrb + r) * Q_ld + q0 + cofs, slot + QB + n * 1024);
             }
             if (k == 0) {
                 const float *src = lane < 32 ? Ps + (pbb + ys) * Pdim + p0 + 4 * lane
                                              : Qs + (qbb + ys) * Qdim + q0 + 4 * (lane - 32);
-                dma16(src, slot + 2 * WF8_PB);
+                dma16(src, slot + SB);
+            } else if (PW == 2) {
+                // P half 1's scales (the upper lanes repeat them into the unused quarter)
+                dma16(Ps + (pbb + ys) * Pdim + p0 + WG_T + 4 * (lane & 31), slot + SB + 2 * WG_T * 4);
             }
             if (++ys == nsteps) { ys = 0; ++yq; }
         };
-        const int nops = 16 + (k == 0 ? 1 : 0);
+        const int nops = 8 * (PW + 1) + ((k == 0 || PW == 2) ? 1 : 0);
         for (int y = 0; y < WF8_S - 1 && y < total; ++y) issue(y);
         for (int x = 0; x < total; ++x) {
             wait_vmcnt_dyn(nops * (min(x + WF8_S - 2, total - 1) - x));
@@ -933,8 +940,9 @@ __global__ __launch_bounds__(WF8_NT, 3) void wgrad_fp8_kernel(const WgradArgs a,
     int ofs[8];
 #pragma unroll
     for (int f = 0; f < 8; ++f) {
-        const int col0 = f < 4 ? wq * 64 + f * 16 : wp * 64 + (f - 4) * 16;
-        const int base = f < 4 ? WF8_PB : 0;
+        // P values of this wave: half wp / 2 of the staged p tile, columns (wp % 2) * 64 ..
+        const int col0 = f < 4 ? wq * 64 + f * 16 : (wp & 1) * 64 + (f - 4) * 16;
+        const int base = f < 4 ? QB : (wp >> 1) * WF8_PB;
         const int r = 32 * g + jj;
         ofs[f] = base + r * WG_T + (((col0 >> 4) ^ wf8_h(r)) << 4) + 8 * aa;
     }
@@ -942,7 +950,7 @@ __global__ __launch_bounds__(WF8_NT, 3) void wgrad_fp8_kernel(const WgradArgs a,
     int qt = 0, st = 0, slot = 0;
     for (int x = 0; x < total; ++x) {
         cta_barrier();
-        const char *sb = wsm + slot * WF8_STAGE;
+        const char *sb = wsm + slot * STAGE;
         auto frag = [&](int f) {
             wf8_v2i v[4];
 #pragma unroll
@@ -967,10 +975,11 @@ __global__ __launch_bounds__(WF8_NT, 3) void wgrad_fp8_kernel(const WgradArgs a,
                     fp[j][w] &= (int)m;
                 }
         }
-        const float *scp = (const float *)(sb + 2 * WF8_PB), *scq = scp + WG_T;
+        // scales: [P half 0 | Q | P half 1 | unused], 128 floats each
+        const float *scq = (const float *)(sb + SB) + WG_T, *scp = (const float *)(sb + SB) + 2 * WG_T * (wp >> 1);
         float sp[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sp[j] = scp[wp * 64 + j * 16 + (lane & 15)];
+        for (int j = 0; j < 4; ++j) sp[j] = scp[(wp & 1) * 64 + j * 16 + (lane & 15)];
         // one row of four products at a time, then its scaling: four partial sums live
         // instead of sixteen, which keeps the kernel at three waves per SIMD
 #pragma unroll
@@ -1093,18 +1102,33 @@ hipError_t launch_wgrad(int dt, int pass, const WgradArgs &args, hipStream_t s) 
         if (pass) wgrad_kernel<DT_F32, 1><<<(unsigned)grid, BW_NT, 0, s>>>(a, nlead, tiles);
         else wgrad_kernel<DT_F32, 0><<<(unsigned)grid, BW_NT, 0, s>>>(a, nlead, tiles);
     } else if (dt == DT_E4M3) {
+        // the 256-wide p tile needs every p dimension and split of the launch on 256-value boundaries
+        bool wide = true;
+        for (int i = 0; i < a.nprob; ++i) wide = wide && a.p[i].Pdim % 256 == 0 && a.p[i].split % 256 == 0;
+        if (wide) {
+            for (int i = 0; i < a.nprob; ++i) a.p[i].p_tile = 256;
+            tiles = 0;
+            for (int i = 0; i < a.nprob; ++i) tiles += wg_tiles(a.p[i]);
+            nlead = (a.nprob > 1 && !a.p[0].offsets) ? wg_tiles(a.p[0]) : 0;
+            grid = (nlead + 7) / 8 * 8 + (tiles - nlead + 7) / 8 * 8;
+        }
         static std::once_flag once8;
         static hipError_t attr8 = hipSuccess;
         std::call_once(once8, [] {
-            attr8 = hipFuncSetAttribute((const void *)wgrad_fp8_kernel<0>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                        WF8_LDS);
-            if (attr8 == hipSuccess)
-                attr8 = hipFuncSetAttribute((const void *)wgrad_fp8_kernel<1>,
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, WF8_LDS);
+            const void *k[4] = {(const void *)wgrad_fp8_kernel<0, 1>, (const void *)wgrad_fp8_kernel<1, 1>,
+                                (const void *)wgrad_fp8_kernel<0, 2>, (const void *)wgrad_fp8_kernel<1, 2>};
+            const int lds[4] = {wf8_lds<1>(), wf8_lds<1>(), wf8_lds<2>(), wf8_lds<2>()};
+            for (int i = 0; i < 4 && attr8 == hipSuccess; ++i)
+                attr8 = hipFuncSetAttribute(k[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds[i]);
         });
         if (attr8 != hipSuccess) return attr8;
-        if (pass) wgrad_fp8_kernel<1><<<(unsigned)grid, WF8_NT, WF8_LDS, s>>>(a, nlead, tiles);
-        else wgrad_fp8_kernel<0><<<(unsigned)grid, WF8_NT, WF8_LDS, s>>>(a, nlead, tiles);
+        if (wide) {
+            if (pass) wgrad_fp8_kernel<1, 2><<<(unsigned)grid, wf8_nt<2>(), wf8_lds<2>(), s>>>(a, nlead, tiles);
+            else wgrad_fp8_kernel<0, 2><<<(unsigned)grid, wf8_nt<2>(), wf8_lds<2>(), s>>>(a, nlead, tiles);
+        } else {
+            if (pass) wgrad_fp8_kernel<1, 1><<<(unsigned)grid, wf8_nt<1>(), wf8_lds<1>(), s>>>(a, nlead, tiles);
+            else wgrad_fp8_kernel<0, 1><<<(unsigned)grid, wf8_nt<1>(), wf8_lds<1>(), s>>>(a, nlead, tiles);
+        }
     } else {
         // the 256-wide p tile needs every p dimension and split of the launch on 256-value boundaries
         bool wide = true;
