@@ -486,11 +486,12 @@ __global__ __launch_bounds__(BW_NT) void wgrad_kernel(const WgradArgs a, int64_t
 // PW = 2: the p tile is 256 wide (two 128-value halves staged side by side, eight MFMA
 // waves), which cuts the operand rows each output value costs by a quarter; it is used
 // when every p dimension and split of the launch is a multiple of 256.
-constexpr int WGB_S = 4;                                  // ring stages
+// ring stages (five for the 256-wide tile measured slower than four)
+template <int PW> constexpr int wgb_s() { return 4; }
 constexpr int WGB_PB = WG_R * WG_T * 2;                   // one operand half's rows of a step (8 KB)
 constexpr int WGB_IDX = 256;                              // gather indices of a later step
 template <int PW> constexpr int wgb_stage() { return (PW + 1) * WGB_PB + WGB_IDX; }
-template <int PW> constexpr int wgb_lds() { return WGB_S * wgb_stage<PW>(); }
+template <int PW> constexpr int wgb_lds() { return wgb_s<PW>() * wgb_stage<PW>(); }
 template <int PW> constexpr int wgb_nt() { return 64 * (4 * PW + 2); }
 
 // slot permutation of a staged row's 16 chunks (an even XOR keeps chunk pairs together)
@@ -521,6 +522,7 @@ template <int PASS, int PW>
 __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArgs a, int64_t nlead, int64_t ntiles) {
     extern __shared__ __align__(1024) char wsm[];
     constexpr int STAGE = wgb_stage<PW>(), QB = PW * WGB_PB;   // Q rows follow the PW halves of P
+    constexpr int WGB_S = wgb_s<PW>();
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const bool producer = wid >= 4 * PW;
     const int wp = (wid >> 1) & (2 * PW - 1), wq = wid & 1;
@@ -827,13 +829,14 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const void *__restrict_
 // 8-byte pieces addressed by lanes 2j+a (j = 0..7); four reads give a lane the 32
 // consecutive rows of its operand.  Staged rows are 128 bytes; their 16-byte chunks sit
 // in slots XOR-permuted by wf8_h so the 32 rows of one read spread over all banks.
-constexpr int WF8_S = 2;                                   // ring stages (two workgroups per CU)
+// ring stages: two (two workgroups per CU), three for the 256-wide tile (one per CU)
+template <int PW> constexpr int wf8_s() { return PW == 2 ? 3 : 2; }
 constexpr int WF8_R = 128;                                 // rows per step (one quantisation run)
 constexpr int WF8_PB = WF8_R * WG_T;                       // one operand's codes of a step (16 KB)
 // PW = 2: 256-wide p tiles as in the bf16 kernel (two staged halves, eight MFMA waves).
 // Scale area per stage: [P half 0 | Q | P half 1 | unused], 512 bytes each.
 template <int PW> constexpr int wf8_stage() { return (PW + 1) * WF8_PB + PW * 2 * WG_T * 4; }
-template <int PW> constexpr int wf8_lds() { return WF8_S * wf8_stage<PW>(); }
+template <int PW> constexpr int wf8_lds() { return wf8_s<PW>() * wf8_stage<PW>(); }
 template <int PW> constexpr int wf8_nt() { return 64 * (4 * PW + 2); }
 
 __device__ __forceinline__ int wf8_h(int r) { return ((r >> 1) & 3) | (((r >> 5) & 1) << 2); }
@@ -848,6 +851,7 @@ template <int PASS, int PW>
 __global__ __launch_bounds__(wf8_nt<PW>(), 3) void wgrad_fp8_kernel(const WgradArgs a, int64_t nlead, int64_t ntiles) {
     extern __shared__ __align__(1024) char wsm[];
     constexpr int STAGE = wf8_stage<PW>(), QB = PW * WF8_PB, SB = (PW + 1) * WF8_PB;   // Q codes, scales
+    constexpr int WF8_S = wf8_s<PW>();
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const bool producer = wid >= 4 * PW;
     const int wp = (wid >> 1) & (2 * PW - 1), wq = wid & 1;
