@@ -143,6 +143,24 @@ def traffic_from_profile(cfg, kernel, backward=False):
     return float(t.group(1))
 
 
+def mfma_util_from_profile(cfg, kernel, backward=False):
+    """MfmaUtil (% of MFMA-busy cycles over GPU-active cycles x SIMDs) of
+    `kernel` from the committed rocprofv3 MFMA-counter summary, or None when
+    there is none for this workload or the kernel sources changed since."""
+    if kernel is None:
+        return None
+    from mixture_experts_layer_35_amd.profsum import source_hash
+    path = profile_path(cfg, backward).replace("_pmc.md", "_mfma.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"source_sha256_16:\s*([0-9a-f]+)", text)
+    t = re.search(r"mfma_util\[%s\]:\s*([0-9.eE+]+)" % re.escape(kernel), text)
+    if not m or not t or m.group(1) != source_hash():
+        return None
+    return float(t.group(1))
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -376,6 +394,8 @@ def main():
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     tr = traffic_from_profile(cfg, dom) if bw is None else traffic_from_profile(cfg, BWD_KERNELS[dom], True)
     roof["traffic"] = tr
+    roof["mfma_util_pct"] = (mfma_util_from_profile(cfg, dom) if bw is None
+                             else mfma_util_from_profile(cfg, BWD_KERNELS[dom], True))
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
