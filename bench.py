@@ -37,10 +37,11 @@ def esz(dtype):
     return {"fp32": 4, "bf16": 2, "fp8": 1}[dtype]
 
 
-def algorithmic(cfg, n_touched):
+def algorithmic(cfg, n_touched, saved=False):
     """Algorithmic FLOPs and HBM bytes per launch of the two expert kernels:
     every weight of a touched expert read once, activations in and H / y out
-    once (no padding rows, no re-reads)."""
+    once (no padding rows, no re-reads); saved: gate/up also writes the fp32
+    SwiGLU inputs a | b of every row for the backward."""
     T, d, I, K, Ns = cfg.T, cfg.d, cfg.I, cfg.K, cfg.Ns
     rows = T * K + T * Ns
     wsz = esz(cfg.dtype)
@@ -51,6 +52,8 @@ def algorithmic(cfg, n_touched):
     xin = T * d * (1 + asc) if cfg.dtype == "fp8" else T * d * act   # u (or its e4m3 copy) read once
     experts = n_touched + Ns
     gu_bytes = experts * 2 * I * d * (wsz + sc) + xin + rows * I * (hsz + asc)
+    if saved:
+        gu_bytes += rows * 2 * I * 4
     dn_bytes = experts * I * d * (wsz + sc) + rows * I * (hsz + asc) + rows * d * act
     return dict(ffn_gate_up=(rows * 4.0 * I * d, gu_bytes), ffn_down=(rows * 2.0 * I * d, dn_bytes))
 
@@ -77,10 +80,11 @@ BWD_STAGES = ("bwd_combine", "bwd_dh", "bwd_swiglu", "bwd_dx", "bwd_token", "bwd
               "wgrad_down", "wgrad_gate_up")
 
 
-def algorithmic_bwd(cfg, n_touched):
+def algorithmic_bwd(cfg, n_touched, saved=False):
     """Algorithmic (FLOPs, HBM bytes) per launch of each backward stage: every
     operand read or written once (weights of touched experts once, u once,
-    activations per expert row once), no padding rows."""
+    activations per expert row once), no padding rows.  saved: the SwiGLU
+    gradient reads the forward's fp32 (a, b) instead of recomputing them."""
     T, d, I, K, Ns, Nr = cfg.T, cfg.d, cfg.I, cfg.K, cfg.Ns, cfg.Nr
     fp8 = cfg.dtype == "fp8"
     a = 2 if fp8 else esz(cfg.dtype)                  # activations, gradients (bf16 for e4m3 layers)
@@ -95,7 +99,8 @@ def algorithmic_bwd(cfg, n_touched):
     return dict(
         bwd_combine=(2.0 * rr * d, T * d * a + 2 * rr * d * a + rr * 12 + (rr + T) * d * q),
         bwd_dh=(gemm, ex * I * d * wb + (rr + T) * d * o + rows * I * a),
-        bwd_swiglu=(2 * gemm, ex * 2 * I * d * wb + T * d * o + rows * I * a + rows * 2 * I * (a + q)),
+        bwd_swiglu=((0.0, rows * I * a + rows * 2 * I * 4 + rows * 2 * I * a) if saved else
+                    (2 * gemm, ex * 2 * I * d * wb + T * d * o + rows * I * a + rows * 2 * I * (a + q))),
         bwd_dx=(2 * gemm, ex * 2 * I * d * wb + rows * 2 * I * o + rows * d * a),
         bwd_token=(2.0 * rows * d, rows * d * a + Nr * d * a + T * d * a + rr * 16),
         bwd_dgate=(2.0 * rr * d, T * d * a + Nr * d * 4 + rr * 8),
@@ -261,6 +266,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=640, help="tokens in the CPU-oracle sample (0: skip)")
     ap.add_argument("--backward", action="store_true",
                     help="time forward + backward (input, centroid and expert-weight gradients) per step")
+    ap.add_argument("--recompute-swiglu", action="store_true",
+                    help="with --backward: recompute the SwiGLU inputs in the backward instead of keeping them "
+                         "from the forward (MOE_SAVE_SWIGLU_INPUTS, the default for --backward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a 1 GiB device copy (reference kernel for HBM counter scaling)")
     args = ap.parse_args()
@@ -286,7 +294,11 @@ def main():
     inp = syn.layer_inputs(cfg)
     t_gen = time.perf_counter() - t_gen
     print("# inputs generated in %.1f s" % t_gen, file=sys.stderr, flush=True)
-    shape = moe.make_shape(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.G, cfg.Mg, cfg.K, cfg.I, cfg.dtype)
+    # a training step keeps the SwiGLU inputs for the backward (fp32 a | b per expert row)
+    saved = args.backward and not args.recompute_swiglu
+    bwd_kernels = dict(BWD_KERNELS, bwd_swiglu="swiglu_grad_kernel") if saved else BWD_KERNELS
+    shape = moe.make_shape(cfg.T, cfg.d, cfg.Nr, cfg.Ns, cfg.G, cfg.Mg, cfg.K, cfg.I, cfg.dtype,
+                           flags=moe.MOE_SAVE_SWIGLU_INPUTS if saved else 0)
     layer = MoeLayer.from_host(shape, inp["gate_w"], inp["bias"], inp["wg"], inp["wu"], inp["wd"], inp["swg"],
                                inp["swu"], inp["swd"])
     T = cfg.T
@@ -377,11 +389,11 @@ def main():
                 "step_ms": [round(float(evs[k][0].elapsed_time(evs[k][5])), 4) for k in range(args.steps)],
                 "bias_range_after": [round(float(layer.bias.min()), 4), round(float(layer.bias.max()), 4)]}
     if bw is None:
-        alg = algorithmic(cfg, n_touched)
+        alg = algorithmic(cfg, n_touched, saved)
         dom = max(("ffn_gate_up", "ffn_down"), key=lambda k: stage_ms[k])
         t_dom = stage_ms[dom] / 1000.0
     else:
-        alg = algorithmic_bwd(cfg, n_touched)
+        alg = algorithmic_bwd(cfg, n_touched, saved)
         dom = max(BWD_STAGES, key=lambda k: bstage_ms[k])
         t_dom = bstage_ms[dom] / 1000.0
     flops, nbytes = alg[dom]
@@ -392,10 +404,10 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(flops / t_dom / 1e12, 1), "peak": peak_f, "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    tr = traffic_from_profile(cfg, dom) if bw is None else traffic_from_profile(cfg, BWD_KERNELS[dom], True)
+    tr = traffic_from_profile(cfg, dom) if bw is None else traffic_from_profile(cfg, bwd_kernels[dom], True)
     roof["traffic"] = tr
     roof["mfma_util_pct"] = (mfma_util_from_profile(cfg, dom) if bw is None
-                             else mfma_util_from_profile(cfg, BWD_KERNELS[dom], True))
+                             else mfma_util_from_profile(cfg, bwd_kernels[dom], True))
     roof["kernel"] = dom
     roof["algorithmic_bytes"] = nbytes
     roof["algorithmic_flops"] = flops
@@ -410,7 +422,7 @@ def main():
                                 "algorithmic_flops": f,
                                 "GB/s": round(nb / t / 1e9, 1) if t > 0 else None,
                                 "TFLOP/s": round(f / t / 1e12, 1) if t > 0 else None,
-                                "traffic": traffic_from_profile(cfg, BWD_KERNELS[name], True)}
+                                "traffic": traffic_from_profile(cfg, bwd_kernels[name], True)}
 
     hbm_stages = {}
     for name, nb in stage_bytes(cfg).items():
@@ -420,7 +432,7 @@ def main():
                             "traffic": traffic_from_profile(cfg, STAGE_KERNELS[name])}
     # "% attainable": the layer's algorithmic flops against min(MFMA peak, AI x HBM peak),
     # with AI over the algorithmic bytes of every stage of the step
-    fwd_alg = algorithmic(cfg, n_touched)
+    fwd_alg = algorithmic(cfg, n_touched, saved)
     layer_bytes = sum(stage_bytes(cfg).values()) + sum(b for _, b in fwd_alg.values())
     layer_flops = T * cfg.flops_per_token
     if bw is not None:
@@ -467,7 +479,8 @@ def main():
         "dtype": {"bf16": "bf16", "fp8": "fp8e4m3", "fp32": "f32"}[cfg.dtype],
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights; no trained weights)",
         "config": {"workload": wl, "T": T, "d": cfg.d, "n_routed": cfg.Nr, "n_shared": cfg.Ns, "topk": cfg.K,
-                   "n_groups": cfg.G, "topk_groups": cfg.Mg, "inter": cfg.I, "parallelism": "single GPU"},
+                   "n_groups": cfg.G, "topk_groups": cfg.Mg, "inter": cfg.I, "parallelism": "single GPU",
+                   **({"swiglu_inputs": "saved by the forward" if saved else "recomputed"} if args.backward else {})},
         "tflops": round(tflops, 2),
         "mfma_peak_frac": round(tflops / peak_f, 4),
         "attainable_tflops": round(attainable, 1),

@@ -66,6 +66,13 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_E4M3 = 2 } moe_dtype;
 
 /* flags */
 #define MOE_ADD_RESIDUAL 1u   /* moe_forward / moe_combine add u_t to the output */
+/* moe_forward keeps the SwiGLU inputs a = W_gate x and b = W_up x of every
+ * routed and shared row (fp32, the gate/up accumulators as they are) in its
+ * workspace, which grows by (T*topk + T*n_shared) * 2 * inter * 4 bytes;
+ * moe_backward with the same flag then forms the SwiGLU gradient from them
+ * instead of recomputing the gate/up product: the same bits, without a second
+ * pass over W_gate and W_up.  Forward and backward must agree on this flag. */
+#define MOE_SAVE_SWIGLU_INPUTS 2u
 
 /*
  * Shape and numerics of one layer (§2.1.2, §4.2).  Supported combinations
@@ -95,7 +102,7 @@ typedef struct moe_shape {
     int32_t out_dtype;      /* y_perm, y_shared, out: equal to act_dtype */
     int32_t quant_block;    /* N_c = 128 */
     float routed_scale;     /* factor on every gating value (1.0) */
-    uint32_t flags;         /* MOE_ADD_RESIDUAL or 0 */
+    uint32_t flags;         /* MOE_ADD_RESIDUAL | MOE_SAVE_SWIGLU_INPUTS, or 0 */
 } moe_shape;
 
 /* ------------------------------------------------------------------------ */
@@ -265,7 +272,8 @@ int moe_transpose_expert_weights(const moe_shape *shape, int32_t n, const void *
  * shared_* likewise (NULL when N_s == 0); *_s and *_wt_s are NULL for
  * fp32 / bf16 layers.  fwd_ws/fwd_ws_bytes: the forward workspace of the
  * moe_forward call whose output dout refers to, untouched since (it holds the
- * scores, selection, dispatch, H and Y, which are the saved activations).
+ * scores, selection, dispatch, H and Y, which are the saved activations,
+ * and with MOE_SAVE_SWIGLU_INPUTS the SwiGLU inputs a and b).
  * Storage: dout, du and the weight gradients in act_dtype (bf16 for E4M3
  * layers).  Outputs: du [T][d]; optional (NULL to skip): dgate_w [N_r][d]
  * fp32, d_routed_w = {dW_gate, dW_up, dW_down} (layout of the forward weights,

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(PKG, "libmoe.so")
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_ADD_RESIDUAL = 1
+MOE_SAVE_SWIGLU_INPUTS = 2   # moe_forward keeps the SwiGLU inputs for moe_backward
 MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_FORWARD = 0, 1, 2
 
 EXPORTED = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_timed",

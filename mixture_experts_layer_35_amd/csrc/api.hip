@@ -99,7 +99,8 @@ int check_shape(const moe_shape *s, const char *fn) {
         return fail(MOE_ERR_UNSUPPORTED, "%s: quant_block = %d (only 128 is supported)", fn, s->quant_block);
     if (s->T * (int64_t)s->topk >= (1ll << 31) || s->T * (int64_t)(s->n_shared ? s->n_shared : 1) >= (1ll << 31))
         return fail(MOE_ERR_UNSUPPORTED, "%s: T * topk and T * n_shared must be below 2^31", fn);
-    if (s->flags & ~MOE_ADD_RESIDUAL) return fail(MOE_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, s->flags);
+    if (s->flags & ~(MOE_ADD_RESIDUAL | MOE_SAVE_SWIGLU_INPUTS))
+        return fail(MOE_ERR_INVALID_ARG, "%s: unknown flags 0x%x", fn, s->flags);
     return MOE_OK;
 }
 
@@ -116,7 +117,7 @@ int dt_of(int d) { return d == MOE_F32 ? DT_F32 : d == MOE_BF16 ? DT_BF16 : DT_E
 // ---- workspace layouts --------------------------------------------------------
 
 struct FwdLayout {
-    size_t scores, idx, w, counts, offsets, bc, perm, inv, uq, us, h, hs, hsh, hshs, yperm, ysh, fq, total;
+    size_t scores, idx, w, counts, offsets, bc, perm, inv, uq, us, h, hs, hsh, hshs, yperm, ysh, fq, ab, total;
 };
 
 FwdLayout fwd_layout(const moe_shape *s) {
@@ -144,6 +145,8 @@ FwdLayout fwd_layout(const moe_shape *s) {
     L.yperm = take((size_t)TK * s->d * osz);
     L.ysh = take((size_t)TS * s->d * osz);
     L.fq = take(FFN_QUEUE_INTS * 4);
+    // SwiGLU inputs a | b of the routed rows, then of the shared rows (MOE_SAVE_SWIGLU_INPUTS)
+    L.ab = take((s->flags & MOE_SAVE_SWIGLU_INPUTS) ? (size_t)(TK + TS) * 2 * s->inter * 4 : 0);
     L.total = o;
     return L;
 }
@@ -450,6 +453,10 @@ int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, con
         dn[1].s0 = fp8 ? shared_s[2] : nullptr;
         dn[1].out = W + L.ysh;
     }
+    if (s->flags & MOE_SAVE_SWIGLU_INPUTS) {
+        gu[0].ab = (float *)(W + L.ab);
+        gu[1].ab = s->n_shared > 0 ? (float *)(W + L.ab) + (size_t)TK * 2 * s->inter : nullptr;
+    }
     {
         FfnArgs a{};
         a.nprob = nprob;
@@ -701,8 +708,14 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
         q[1].out = dab_s;
         q[1].out_ld = 2 * I;
     }
-    for (int i = 0; i < fa.nprob; ++i) fa.p[i] = q[fa.nprob - 1 - i];
-    HIPCHK(launch_ffn(wdt, FFN_GATEUP_BWD, fa, st));
+    if (s->flags & MOE_SAVE_SWIGLU_INPUTS) {
+        // the forward kept a | b for the routed rows and then the shared rows, as dh and dab lie
+        HIPCHK(launch_swiglu_grad(wdt == DT_F32 ? DT_F32 : DT_BF16, dh, (const float *)(Fw + F.ab), dab,
+                                  TK + T * Ns, I, st));
+    } else {
+        for (int i = 0; i < fa.nprob; ++i) fa.p[i] = q[fa.nprob - 1 - i];
+        HIPCHK(launch_ffn(wdt, FFN_GATEUP_BWD, fa, st));
+    }
     if (fp8) HIPCHK(launch_quant_rows(dt, dab, nullptr, TK + T * Ns, 2 * I, U8(L.abq), F32(L.abs_), st));
     HIPCHK(mark(3));
     // 4. dX = [dA | dB] . [W_gate ; W_up] (transposed copies [n][d][2I])

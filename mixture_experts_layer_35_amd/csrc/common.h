@@ -57,6 +57,16 @@ __device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float
     return v;
 }
 
+// SwiGLU gradient at one feature: h = SiLU(a) * b, SiLU(a) = a * s, s = sigmoid(a);
+// da = dh * b * SiLU'(a) with SiLU'(a) = s (1 + a (1 - s)), db = dh * SiLU(a).  One
+// definition for the expert kernel's recomputing epilogue and the kernel that reads
+// saved (a, b), so both give the same bits.
+__device__ __forceinline__ void swiglu_grad(float dh, float a, float b, float &da, float &db) {
+    const float sg = 1.0f / (1.0f + __expf(-a));
+    da = dh * b * sg * (1.0f + a * (1.0f - sg));
+    db = dh * a * sg;
+}
+
 __device__ __forceinline__ float clamp448(float x) { return fminf(fmaxf(x, -448.0f), 448.0f); }
 
 // Activation / weight quantisation scale for a group with absolute max amax.

@@ -637,12 +637,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                         dh[3] = __uint_as_float(v[1] & 0xFFFF0000u);
                     }
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const float av = acc[i][j][q], bv = acc[i + RB / 2][j][q];
-                        const float sg = 1.0f / (1.0f + __expf(-av));
-                        da[q] = dh[q] * bv * sg * (1.0f + av * (1.0f - sg));
-                        db[q] = dh[q] * av * sg;
-                    }
+                    for (int q = 0; q < 4; ++q) swiglu_grad(dh[q], acc[i][j][q], acc[i + RB / 2][j][q], da[q], db[q]);
                     if (DT == DT_F32) {
                         *(f32x4 *)((float *)P.out + R * ld + f) = f32x4{da[0], da[1], da[2], da[3]};
                         *(f32x4 *)((float *)P.out + R * ld + F + f) = f32x4{db[0], db[1], db[2], db[3]};
@@ -654,6 +649,21 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                 }
             }
         } else if (GATEUP) {
+            if (P.ab) {
+                // the SwiGLU inputs for a backward that reads them instead of recomputing
+#pragma unroll
+                for (int j = 0; j < TB; ++j) {
+                    const int tok = (j * WM + wm) * 16 + (lane & 15);
+                    if (tok >= valid) continue;
+                    float *abrow = P.ab + (rbase + tok) * (2 * (int64_t)F);
+#pragma unroll
+                    for (int i = 0; i < RB / 2; ++i) {
+                        const int f = n0 + wf * (BF / WF) + i * 16 + 4 * (lane >> 4);
+                        *(f32x4 *)(abrow + f) = acc[i][j];
+                        *(f32x4 *)(abrow + F + f) = acc[i + RB / 2][j];
+                    }
+                }
+            }
             if (FP8) {
                 // 1 x 128 groups of H along features: the tile's 128 features of a token live in
                 // 4 lanes x (RB/2) blocks x 4 values in each of the WF waves of its token column
@@ -742,6 +752,41 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
     }
 }
 
+// SwiGLU gradient from the forward's saved fp32 (a, b): one thread per four
+// consecutive features of a row, the epilogue's arithmetic (swiglu_grad).
+template <int DT>
+__global__ __launch_bounds__(256) void swiglu_grad_kernel(const void *__restrict__ dh, const float *__restrict__ ab,
+                                                          void *__restrict__ dab, int64_t quads, int F) {
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= quads) return;
+    const int fq = F / 4;
+    const int64_t r = q / fq;
+    const int f = (int)(q - r * fq) * 4;
+    float dv[4], da[4], db[4];
+    if (DT == DT_F32) {
+        const f32x4 v = *(const f32x4 *)((const float *)dh + r * F + f);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) dv[k] = v[k];
+    } else {
+        const u32x2 v = *(const u32x2 *)((const uint16_t *)dh + r * F + f);
+        dv[0] = __uint_as_float(v[0] << 16);
+        dv[1] = __uint_as_float(v[0] & 0xFFFF0000u);
+        dv[2] = __uint_as_float(v[1] << 16);
+        dv[3] = __uint_as_float(v[1] & 0xFFFF0000u);
+    }
+    const f32x4 av = __builtin_nontemporal_load((const f32x4 *)(ab + r * 2 * F + f));
+    const f32x4 bv = __builtin_nontemporal_load((const f32x4 *)(ab + r * 2 * F + F + f));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) swiglu_grad(dv[k], av[k], bv[k], da[k], db[k]);
+    if (DT == DT_F32) {
+        *(f32x4 *)((float *)dab + r * 2 * F + f) = f32x4{da[0], da[1], da[2], da[3]};
+        *(f32x4 *)((float *)dab + r * 2 * F + F + f) = f32x4{db[0], db[1], db[2], db[3]};
+    } else {
+        *(u32x2 *)((uint16_t *)dab + r * 2 * F + f) = u32x2{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
+        *(u32x2 *)((uint16_t *)dab + r * 2 * F + F + f) = u32x2{pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3])};
+    }
+}
+
 // The tile-queue counters start at zero in every launch.
 __global__ void zero_queues_kernel(int *ctr) {
     if (threadIdx.x < NQ) ctr[threadIdx.x] = 0;
@@ -786,6 +831,15 @@ hipError_t launch_ffn(int dt, int mode, const FfnArgs &a, hipStream_t s) {
     if (dt == DT_F32) return gateup ? run<DT_F32, FFN_GATEUP>(a, s) : run<DT_F32, FFN_DOWN>(a, s);
     if (dt == DT_BF16) return gateup ? run<DT_BF16, FFN_GATEUP>(a, s) : run<DT_BF16, FFN_DOWN>(a, s);
     return gateup ? run<DT_E4M3, FFN_GATEUP>(a, s) : run<DT_E4M3, FFN_DOWN>(a, s);
+}
+
+hipError_t launch_swiglu_grad(int dt, const void *dh, const float *ab, void *dab, int64_t rows, int F, hipStream_t s) {
+    const int64_t quads = rows * (F / 4);
+    if (quads <= 0) return hipSuccess;
+    const unsigned grid = (unsigned)((quads + 255) / 256);
+    if (dt == DT_F32) swiglu_grad_kernel<DT_F32><<<grid, 256, 0, s>>>(dh, ab, dab, quads, F);
+    else swiglu_grad_kernel<DT_BF16><<<grid, 256, 0, s>>>(dh, ab, dab, quads, F);
+    return hipGetLastError();
 }
 
 }  // namespace moe

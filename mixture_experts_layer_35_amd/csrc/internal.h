@@ -58,6 +58,7 @@ struct FfnProblem {
     float *out_s;           // E4M3 gate/up: H scales [rows][F/128]
     int64_t out_ld;         // elements between output rows (0: F)
     const void *dh;         // gate/up gradient pass: dH [rows][F] (act dtype)
+    float *ab;              // gate/up pass, optional: the SwiGLU inputs a | b as fp32 [rows][2F]
 };
 struct FfnArgs {
     FfnProblem p[2];
@@ -75,6 +76,10 @@ constexpr int kMaxExperts = 1024;
 // dX = [dA | dB] [W_gate ; W_up] passes, instantiated apart so that profiles tell the passes apart.
 enum { FFN_DOWN = 0, FFN_GATEUP = 1, FFN_GATEUP_BWD = 2, FFN_BWD_DH = 3, FFN_BWD_DX = 4 };
 hipError_t launch_ffn(int dt, int mode, const FfnArgs &a, hipStream_t s);
+// SwiGLU gradient from saved inputs: for rows x F features, dab[r][f] = da and
+// dab[r][F + f] = db from dh [rows][F] and ab [rows][2F] (fp32); dh and dab are fp32
+// for dt = DT_F32 and bf16 otherwise, as in the FFN_GATEUP_BWD epilogue.
+hipError_t launch_swiglu_grad(int dt, const void *dh, const float *ab, void *dab, int64_t rows, int F, hipStream_t s);
 
 // ---- backward ----------------------------------------------------------------
 // Weight-gradient problem: for each expert e with rows r (offsets, or rows_fixed

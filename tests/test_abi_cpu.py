@@ -157,6 +157,19 @@ def test_workspace_grows_with_tokens(lib):
     assert a > 4096 * 8 * 7168 * 2
 
 
+def test_saved_swiglu_inputs_grow_the_forward_workspace(lib):
+    # MOE_SAVE_SWIGLU_INPUTS adds the fp32 a | b of every routed and shared row
+    for T, Ns in ((4096, 1), (1000, 2), (77, 0)):
+        plain = moe.make_shape(T, 7168, 256, Ns, 8, 4, 8, 2048, "bf16")
+        saved = moe.make_shape(T, 7168, 256, Ns, 8, 4, 8, 2048, "bf16", flags=moe.MOE_SAVE_SWIGLU_INPUTS)
+        a = lib.moe_workspace_bytes(ctypes.byref(plain), moe.MOE_WS_FORWARD)
+        b = lib.moe_workspace_bytes(ctypes.byref(saved), moe.MOE_WS_FORWARD)
+        need = (T * 8 + T * Ns) * 2 * 2048 * 4
+        assert b - a == (need + 255) // 256 * 256
+        assert lib.moe_workspace_bytes(ctypes.byref(saved), moe.MOE_WS_ROUTE) == \
+            lib.moe_workspace_bytes(ctypes.byref(plain), moe.MOE_WS_ROUTE)
+
+
 def test_binding_raises_with_message(lib):
     s = tiny(d=200)
     with pytest.raises(moe.MoeError) as e:

@@ -160,6 +160,8 @@ def run_case(moe, orc, cfg, seed, flags=0, bias=None, skip=(), rs=1.0):
     ("fp8", 700, 512, 32, 4, 2, 4, 1, 256, 0, 2.5),         # several runs per expert, ragged last runs
     ("fp8", 129, 384, 32, 8, 3, 6, 2, 128, 1, 1.0),         # two shared experts, residual flag
     ("fp8", 300, 256, 64, 8, 4, 8, 0, 384, 0, 1.0),         # no shared expert
+    ("bf16", 700, 512, 32, 4, 2, 4, 1, 256, 2, 1.0),        # SwiGLU inputs saved by the forward
+    ("fp8", 129, 384, 32, 8, 3, 6, 2, 128, 3, 1.0),         # saved inputs, two shared experts, residual flag
 ])
 def test_backward_matches_oracle(moe, orc, dtype, T, d, Nr, G, Mg, K, Ns, I, flags, rs):
     cfg = cfg_of(dtype, T, d, Nr, G, Mg, K, Ns, I)
@@ -340,3 +342,33 @@ def test_backward_timed_is_backward(moe, dtype):
         assert (host(a) == host(b)).all()
     ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(9)]
     assert all(x >= 0 for x in ms), ms
+
+
+@pytest.mark.parametrize("dtype,T,d,Nr,G,Mg,K,Ns,I", [
+    ("fp32", 256, 256, 16, 4, 2, 2, 1, 384),
+    ("fp32", 1, 256, 16, 4, 2, 2, 2, 128),
+    ("bf16", 700, 512, 32, 4, 2, 4, 1, 256),
+    ("bf16", 129, 384, 32, 8, 3, 6, 2, 128),
+    ("bf16", 300, 256, 64, 8, 4, 8, 0, 256),
+    ("fp8", 700, 512, 32, 4, 2, 4, 1, 256),
+    ("fp8", 129, 384, 32, 8, 3, 6, 2, 128),
+    ("fp8", 300, 256, 64, 8, 4, 8, 0, 384),
+])
+def test_saved_swiglu_inputs_give_the_same_bits(moe, dtype, T, d, Nr, G, Mg, K, Ns, I):
+    # MOE_SAVE_SWIGLU_INPUTS: the forward keeps the gate/up accumulators and the
+    # backward forms the SwiGLU gradient from them with the recomputing epilogue's
+    # arithmetic, so every gradient must equal the recomputing path's bit for bit
+    import mixture_experts_layer_35_amd as m
+    cfg = cfg_of(dtype, T, d, Nr, G, Mg, K, Ns, I)
+    inp = syn.layer_inputs(cfg, seed=T + 7)
+    dout = syn.grad_output(cfg, seed=T + 7)
+    print("saved SwiGLU inputs", dtype, T, d, Nr, K, Ns, I, flush=True)
+    for extra in (0, m.MOE_ADD_RESIDUAL):
+        a = gpu_forward_backward(cfg, inp, dout, flags=extra)
+        b = gpu_forward_backward(cfg, inp, dout, flags=extra | m.MOE_SAVE_SWIGLU_INPUTS)
+        assert (a["idx"] == b["idx"]).all()
+        assert (a["du"].view(np.uint8) == b["du"].view(np.uint8)).all()
+        assert (a["dgate"].view(np.uint32) == b["dgate"].view(np.uint32)).all()
+        assert (a["dtopk"].view(np.uint32) == b["dtopk"].view(np.uint32)).all()
+        for x, y in zip(a["drouted"] + (a["dshared"] or ()), b["drouted"] + (b["dshared"] or ())):
+            assert (x.view(np.uint8) == y.view(np.uint8)).all()
