@@ -466,7 +466,8 @@ int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, con
         // the shared experts' tiles go first: their row blocks of one weight block are list
         // neighbours, taken together by the workgroups of one XCD
         for (int i = 0; i < nprob; ++i) a.p[i] = gu[nprob - 1 - i];
-        HIPCHK(launch_ffn(dt_of(s->w_dtype), FFN_GATEUP, a, st));
+        HIPCHK(launch_ffn(dt_of(s->w_dtype), (s->flags & MOE_SAVE_SWIGLU_INPUTS) ? FFN_GATEUP_SAVE : FFN_GATEUP, a,
+                          st));
         HIPCHK(mark(3));
         a.K = s->inter;
         a.F = s->d;

@@ -310,12 +310,15 @@ __device__ __forceinline__ void compute_step(const char *st, const float *sc, f3
 // LDS bytes of the fp8 H-quantisation scratch (per-wave row maxima), kept
 // apart from the ring so the next tile's loads can land during the epilogue.
 template <int DT, int MODE>
-__host__ __device__ constexpr int red_bytes() { return (DT == DT_E4M3 && MODE == FFN_GATEUP) ? WF * BM * 4 : 0; }
+__host__ __device__ constexpr int red_bytes() {
+    return (DT == DT_E4M3 && (MODE == FFN_GATEUP || MODE == FFN_GATEUP_SAVE)) ? WF * BM * 4 : 0;
+}
 
 
 template <int DT, int MODE>
 __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_bytes) {
-    constexpr bool GATEUP = MODE == FFN_GATEUP || MODE == FFN_GATEUP_BWD;   // two weight matrices, SwiGLU epilogue
+    constexpr bool GATEUP = MODE == FFN_GATEUP || MODE == FFN_GATEUP_SAVE || MODE == FFN_GATEUP_BWD;   // two weight matrices
+    constexpr bool SAVEAB = MODE == FFN_GATEUP_SAVE;    // epilogue also stores the SwiGLU inputs to P.ab
     constexpr bool SWBWD = MODE == FFN_GATEUP_BWD;      // epilogue: SwiGLU gradient from dH
     constexpr int esz = FTraits<DT>::esz;
     constexpr int CB = Frag<DT>::CB;              // staged bytes per row per reduction step
@@ -649,7 +652,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                 }
             }
         } else if (GATEUP) {
-            if (P.ab) {
+            if (SAVEAB) {
                 // the SwiGLU inputs for a backward that reads them instead of recomputing
 #pragma unroll
                 for (int j = 0; j < TB; ++j) {
@@ -827,6 +830,9 @@ hipError_t launch_ffn(int dt, int mode, const FfnArgs &a, hipStream_t s) {
         return dt == DT_F32 ? run<DT_F32, FFN_BWD_DX>(a, s)
                             : dt == DT_BF16 ? run<DT_BF16, FFN_BWD_DX>(a, s) : run<DT_E4M3, FFN_BWD_DX>(a, s);
     }
+    if (mode == FFN_GATEUP_SAVE)
+        return dt == DT_F32 ? run<DT_F32, FFN_GATEUP_SAVE>(a, s)
+                            : dt == DT_BF16 ? run<DT_BF16, FFN_GATEUP_SAVE>(a, s) : run<DT_E4M3, FFN_GATEUP_SAVE>(a, s);
     const bool gateup = mode == FFN_GATEUP;
     if (dt == DT_F32) return gateup ? run<DT_F32, FFN_GATEUP>(a, s) : run<DT_F32, FFN_DOWN>(a, s);
     if (dt == DT_BF16) return gateup ? run<DT_BF16, FFN_GATEUP>(a, s) : run<DT_BF16, FFN_DOWN>(a, s);

@@ -58,7 +58,7 @@ struct FfnProblem {
     float *out_s;           // E4M3 gate/up: H scales [rows][F/128]
     int64_t out_ld;         // elements between output rows (0: F)
     const void *dh;         // gate/up gradient pass: dH [rows][F] (act dtype)
-    float *ab;              // gate/up pass, optional: the SwiGLU inputs a | b as fp32 [rows][2F]
+    float *ab;              // FFN_GATEUP_SAVE: the SwiGLU inputs a | b as fp32 [rows][2F]
 };
 struct FfnArgs {
     FfnProblem p[2];
@@ -74,7 +74,9 @@ constexpr int kMaxExperts = 1024;
 // out[:, 0:F] = dh * b * SiLU'(a) and out[:, F:2F] = dh * SiLU(a); out_ld = 2F).
 // FFN_BWD_DH / FFN_BWD_DX: the plain product of FFN_DOWN for the backward's dH = dY W_down and
 // dX = [dA | dB] [W_gate ; W_up] passes, instantiated apart so that profiles tell the passes apart.
-enum { FFN_DOWN = 0, FFN_GATEUP = 1, FFN_GATEUP_BWD = 2, FFN_BWD_DH = 3, FFN_BWD_DX = 4 };
+// FFN_GATEUP_SAVE: FFN_GATEUP that also stores a | b to P.ab, a mode of its own so that the
+// plain forward kernel carries no extra registers for it.
+enum { FFN_DOWN = 0, FFN_GATEUP = 1, FFN_GATEUP_BWD = 2, FFN_BWD_DH = 3, FFN_BWD_DX = 4, FFN_GATEUP_SAVE = 5 };
 hipError_t launch_ffn(int dt, int mode, const FfnArgs &a, hipStream_t s);
 // SwiGLU gradient from saved inputs: for rows x F features, dab[r][f] = da and
 // dab[r][F + f] = db from dh [rows][F] and ab [rows][2F] (fp32); dh and dab are fp32

@@ -32,7 +32,8 @@ def short_name(full: str) -> str:
     by their function name."""
     m = re.search(r"ffn_kernel<(\d+), (\d+)>", full)
     if m:
-        return {0: "ffn_down", 1: "ffn_gate_up", 2: "bwd_swiglu", 3: "bwd_dh", 4: "bwd_dx"}[int(m.group(2))]
+        return {0: "ffn_down", 1: "ffn_gate_up", 2: "bwd_swiglu", 3: "bwd_dh", 4: "bwd_dx",
+                5: "ffn_gate_up"}[int(m.group(2))]
     # the pass (0: dW_down, 1: dW_gate / dW_up) is the first template argument of the bf16
     # and e4m3 kernels and the second of the fp32 one
     m = re.search(r"wgrad_(?:bf16|fp8)_kernel<(\d+)", full) or re.search(r"wgrad_kernel<\d+, (\d+)>", full)
