@@ -200,6 +200,11 @@ def test_backward_rejections(lib):
     assert call(ws_bytes=need - 1) == moe.MOE_ERR_WORKSPACE
     assert call(fwd_bytes=fwd - 1) == moe.MOE_ERR_WORKSPACE
     assert "forward workspace" in moe.moe_last_error()
+    # with saved SwiGLU inputs the backward expects the forward's larger workspace
+    sv = tiny(flags=moe.MOE_SAVE_SWIGLU_INPUTS)
+    fwd_sv = lib.moe_workspace_bytes(ctypes.byref(sv), moe.MOE_WS_FORWARD)
+    assert fwd_sv > fwd
+    assert call(shape=ctypes.byref(sv), fwd_bytes=fwd) == moe.MOE_ERR_WORKSPACE
     assert call(du=None) == moe.MOE_ERR_INVALID_ARG
     assert call(fwd_ws=FAKE + 16) == moe.MOE_ERR_INVALID_ARG
     bad_t, bad_ta = _parr(FAKE, None, None)

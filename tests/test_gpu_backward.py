@@ -306,14 +306,15 @@ def test_quantize_128x1_matches_oracle(moe, orc, x_dtype, gather):
     assert (s_r[:, 7] == 1.0).all()
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_backward_timed_is_backward(moe, dtype):
-    """moe_backward_timed (ten stage events) writes exactly what moe_backward writes."""
+@pytest.mark.parametrize("dtype,flags", [("bf16", 0), ("fp8", 0), ("bf16", 2), ("fp8", 2)])
+def test_backward_timed_is_backward(moe, dtype, flags):
+    """moe_backward_timed (ten stage events) writes exactly what moe_backward writes
+    (flags 2: the SwiGLU inputs saved by the forward)."""
     import mixture_experts_layer_35_amd as m
     from mixture_experts_layer_35_amd.layer import MoeLayer
     cfg = cfg_of(dtype, 300, 256, 16, 4, 2, 2, 1, 256)
     inp = syn.layer_inputs(cfg, seed=51)
-    layer = MoeLayer.from_host(shape_of(cfg), inp["gate_w"], inp["bias"], inp["wg"], inp["wu"], inp["wd"],
+    layer = MoeLayer.from_host(shape_of(cfg, flags=flags), inp["gate_w"], inp["bias"], inp["wg"], inp["wu"], inp["wd"],
                                inp["swg"], inp["swu"], inp["swd"])
     u = dev(inp["u"])
     layer.forward(u)
@@ -322,7 +323,7 @@ def test_backward_timed_is_backward(moe, dtype):
                      tuple(torch.empty(w.shape, dtype=torch.bfloat16, device="cuda") for w in layer.routed_w),
                      tuple(torch.empty(w.shape, dtype=torch.bfloat16, device="cuda") for w in layer.shared_w))
     g0, r0, s0 = grads()
-    print("backward timed", dtype, flush=True)
+    print("backward timed", dtype, flags, flush=True)
     du0 = layer.backward(u, dout, dgate_w=g0, d_routed_w=r0, d_shared_w=s0)
     (rt, rts), (st, sts) = layer.transposed_weights()
     g1, r1, s1 = grads()
