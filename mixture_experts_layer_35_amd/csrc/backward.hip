@@ -735,9 +735,9 @@ __global__ void block_base_kernel(const int32_t *__restrict__ offsets, int n, in
 // e*ceil(seg_rows/128)).  List row r reads source row gather[r] (or r), bf16, or
 // e4m3 with 1 x 128 scales (decoded to fp32 first).  Scale = amax / 448 (1 for an
 // all-zero column), codes = e4m3(clamp(v / scale)), nearest even.  The run is read
-// twice (amax, then codes); the second pass finds it in L2.
+// once: a workgroup keeps its 128 rows x 128 columns in registers.
 constexpr int QC_COLS = 8;                  // columns per thread
-constexpr int QC_CHUNK = 256 * QC_COLS;     // columns per workgroup
+constexpr int QC_CHUNK = 16 * QC_COLS;      // columns per workgroup (16 threads per row, 16 row groups)
 template <int IN>
 __global__ __launch_bounds__(256) void quant_cols_kernel(const void *__restrict__ src, const float *__restrict__ src_s,
                                                          const int32_t *__restrict__ gather,
@@ -764,8 +764,12 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const void *__restrict_
         r0 = e * seg_rows + j * 128;
         r1 = min(r0 + 128, (e + 1) * seg_rows);
     }
-    const int c = blockIdx.y * QC_CHUNK + threadIdx.x * QC_COLS;
-    if (c >= cols) return;
+    // one pass: thread (g, t) = (threadIdx.x / 16, threadIdx.x % 16) holds rows r0 + 8g .. r0 + 8g + 7
+    // of columns c .. c + 7 in registers; the run's column maxima are combined across the
+    // 16 row groups (shuffles inside a wave, then LDS across the four waves)
+    __shared__ float red[4][16][QC_COLS];
+    const int t = threadIdx.x & 15, g = threadIdx.x >> 4, wv = threadIdx.x >> 6;
+    const int c = blockIdx.y * QC_CHUNK + t * QC_COLS;
     auto load = [&](int64_t r, float (&v)[QC_COLS]) {
         const int64_t xr = gather ? (int64_t)gather[r] : r;
         if (IN == DT_E4M3) {
@@ -783,38 +787,44 @@ __global__ __launch_bounds__(256) void quant_cols_kernel(const void *__restrict_
             }
         }
     };
+    float v[8][QC_COLS];
     float amax[QC_COLS];
 #pragma unroll
     for (int k = 0; k < QC_COLS; ++k) amax[k] = 0.0f;
-    for (int64_t r = r0; r < r1; r += 4) {
-        float v[4][QC_COLS];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) load(min(r + u, r1 - 1), v[u]);   // rows past the run repeat its last
+    for (int i = 0; i < 8; ++i) {
+        const int64_t r = r0 + 8 * g + i;
+        load(min(r, r1 - 1), v[i]);   // rows past the run repeat its last (no effect on the maxima)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-            for (int k = 0; k < QC_COLS; ++k) amax[k] = fmaxf(amax[k], fabsf(v[u][k]));
+        for (int k = 0; k < QC_COLS; ++k) amax[k] = fmaxf(amax[k], fabsf(v[i][k]));
     }
+#pragma unroll
+    for (int k = 0; k < QC_COLS; ++k) {
+        amax[k] = fmaxf(amax[k], __shfl_xor(amax[k], 16, 64));
+        amax[k] = fmaxf(amax[k], __shfl_xor(amax[k], 32, 64));
+    }
+    if ((threadIdx.x & 63) < 16)
+#pragma unroll
+        for (int k = 0; k < QC_COLS; ++k) red[wv][t][k] = amax[k];
+    __syncthreads();
     float scale[QC_COLS];
 #pragma unroll
-    for (int k = 0; k < QC_COLS; ++k) scale[k] = quant_scale(amax[k]);
-    *(f32x4 *)(sc + b * cols + c) = f32x4{scale[0], scale[1], scale[2], scale[3]};
-    *(f32x4 *)(sc + b * cols + c + 4) = f32x4{scale[4], scale[5], scale[6], scale[7]};
-    for (int64_t r = r0; r < r1; r += 4) {
-        float v[4][QC_COLS];
+    for (int k = 0; k < QC_COLS; ++k)
+        scale[k] = quant_scale(fmaxf(fmaxf(red[0][t][k], red[1][t][k]), fmaxf(red[2][t][k], red[3][t][k])));
+    if (g == 0) {
+        *(f32x4 *)(sc + b * cols + c) = f32x4{scale[0], scale[1], scale[2], scale[3]};
+        *(f32x4 *)(sc + b * cols + c + 4) = f32x4{scale[4], scale[5], scale[6], scale[7]};
+    }
 #pragma unroll
-        for (int u = 0; u < 4; ++u) load(min(r + u, r1 - 1), v[u]);
+    for (int i = 0; i < 8; ++i) {
+        const int64_t r = r0 + 8 * g + i;
+        if (r >= r1) break;
+        u32x2 o;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (r + u >= r1) break;
-            u32x2 o;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                o[h] = pack_e4m3x4(clamp448(v[u][4 * h] / scale[4 * h]), clamp448(v[u][4 * h + 1] / scale[4 * h + 1]),
-                                   clamp448(v[u][4 * h + 2] / scale[4 * h + 2]),
-                                   clamp448(v[u][4 * h + 3] / scale[4 * h + 3]));
-            *(u32x2 *)(q + (r + u) * cols + c) = o;
-        }
+        for (int h = 0; h < 2; ++h)
+            o[h] = pack_e4m3x4(clamp448(v[i][4 * h] / scale[4 * h]), clamp448(v[i][4 * h + 1] / scale[4 * h + 1]),
+                               clamp448(v[i][4 * h + 2] / scale[4 * h + 2]), clamp448(v[i][4 * h + 3] / scale[4 * h + 3]));
+        *(u32x2 *)(q + r * cols + c) = o;
     }
 }
 
