@@ -377,10 +377,12 @@ int moe_quantize_weights_128x128(int64_t nmat, int32_t rows, int32_t cols, int32
 
 /*
  * moe_quantize_128x1 -- Q over 128x1 tiles down the rows of segments, the
- * operands of the FP8 weight-gradient GEMMs (§3.3 fine-grained quantization:
- * its tiles are 1x128 for activations in the forward direction and 128x1
- * where the backward reduces over tokens; the tile origin is not stated,
- * read as runs of 128 list rows from each segment's first row).
+ * operands of the FP8 weight-gradient GEMMs.  §3.3 runs Wgrad in FP8 and
+ * names 1x128 activation tiles and 128x128 weight blocks, but no tile for a
+ * GEMM that reduces over tokens.  Reading (not the page's text): a tile is
+ * 128 consecutive elements along the GEMM's reduction, which for a weight
+ * gradient runs down the token rows, i.e. 128x1; the tile origin is not
+ * stated either, read as runs of 128 list rows from each segment's first row.
  *   n_seg segments; offsets [n_seg+1] (device, int32, offsets[0] >= 0,
  *   nondecreasing, offsets[n_seg] <= max_rows): segment e owns list rows
  *   offsets[e] .. offsets[e+1]-1, cut into runs of 128 rows from its first

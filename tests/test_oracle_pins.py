@@ -10,6 +10,7 @@ import os
 import numpy as np
 import pytest
 import torch
+from hypothesis import given, settings, strategies as st
 
 import moe_synth as syn
 
@@ -165,6 +166,33 @@ def test_route_matches_brute_force_sort(orc, Nr, G, Mg, K):
         for j in range(K):
             den = (den + s[np.arange(T), idx[:, j]]).astype(np.float32)
         assert (w == (s[np.arange(T)[:, None], idx] / den[:, None]).astype(np.float32)).all()
+
+
+@settings(max_examples=150, deadline=None, derandomize=True)
+@given(data=st.data())
+def test_route_property_matches_brute_force_sort(orc, data):
+    """Hypothesis over tiny shapes, value grids (many exact ties) and biases:
+    the oracle's selection equals the full-sort selection, and the gates are
+    the selected un-biased affinities over their sum taken in slot order."""
+    G = data.draw(st.sampled_from([1, 2, 3, 4, 8]), "G")
+    per = data.draw(st.integers(1, 6), "experts per group")
+    Nr = G * per
+    Mg = data.draw(st.integers(1, G), "Mg")
+    K = data.draw(st.integers(1, Mg * per), "K")
+    T = data.draw(st.integers(1, 12), "T")
+    levels = data.draw(st.sampled_from([2, 4, 16, 0]), "levels")   # 0: continuous values
+    seed = data.draw(st.integers(0, 2**31 - 1), "seed")
+    rng = np.random.default_rng(seed)
+    s = rng.random((T, Nr), dtype=np.float32)
+    if levels:
+        s = (np.floor(s * levels) / levels + 1.0 / (2 * levels)).astype(np.float32)
+    b = (rng.uniform(-0.2, 0.2, Nr) if data.draw(st.booleans(), "bias") else np.zeros(Nr)).astype(np.float32)
+    _, idx, w = orc.route(None, None, b, G=G, Mg=Mg, K=K, scores_in=s)
+    assert (idx == brute_route(s, b, G, Mg, K)).all()
+    den = np.zeros(T, np.float32)
+    for j in range(K):
+        den = (den + s[np.arange(T), idx[:, j]]).astype(np.float32)
+    assert (w == (s[np.arange(T)[:, None], idx] / den[:, None]).astype(np.float32)).all()
 
 
 def test_route_single_group_is_plain_topk(orc):
@@ -411,6 +439,85 @@ def test_fp8_ffn_matches_dense_on_dequantised_values(orc):
         ref = dq(qd[e], sd[e]) @ hd
         got = f32_of_bits(y[r]).astype(np.float64)
         assert np.abs(got - ref).max() <= 2.0 ** -8 * np.abs(ref).max() + 1e-30
+
+
+def _fp8_weights(orc, inp, Ns):
+    """128 x 128 e4m3 blocks of the routed and shared weights (§3.3)."""
+    routed = [orc.quant_128x128(inp[k]) for k in ("wg", "wu", "wd")]
+    shared = [orc.quant_128x128(inp[k]) for k in ("swg", "swu", "swd")] if Ns else None
+    return routed, shared
+
+
+def test_layer_equals_its_steps_e4m3(orc):
+    """The E4M3 layer = route -> 1 x 128 tiles of u, gathered by the permutation
+    -> e4m3 grouped FFN of the routed experts and of each shared expert over all
+    tokens -> combine with the residual; bit for bit (§2.1.2 layer, §3.3 tiles
+    and blocks).  Two shared experts with different block scales, so a shared
+    expert reading another's scale grid would fail."""
+    cfg = syn.LayerConfig("t", T=40, d=256, Nr=8, G=2, Mg=1, K=3, Ns=2, I=256, dtype="bf16", bias="uniform")
+    inp = syn.layer_inputs(cfg, seed=21)
+    routed, shared = _fp8_weights(orc, inp, cfg.Ns)
+    assert not (shared[0][1][0] == shared[0][1][1]).all()
+    kw = dict(G=cfg.G, Mg=cfg.Mg, K=cfg.K)
+    out, idx, w, s = orc.moe_forward(inp["u"], inp["gate_w"], inp["bias"], tuple(q for q, _ in routed),
+                                     tuple(q for q, _ in shared), w_code=orc.E4M3, out_code=orc.BF16,
+                                     routed_scales=tuple(sc for _, sc in routed),
+                                     shared_scales=tuple(sc for _, sc in shared), flags=1, **kw)
+    s2, idx2, w2 = orc.route(inp["u"], inp["gate_w"], inp["bias"], **kw)
+    assert (idx == idx2).all() and (w == w2).all() and (s == s2).all()
+    counts, offsets, perm, inv = orc.permute(idx, cfg.Nr)
+    assert len(np.unique(idx)) > 3
+    uq, us = orc.quant_1x128(inp["u"])
+    y = orc.grouped_ffn(offsets, uq[perm], *(q for q, _ in routed), rows=np.arange(cfg.T * cfg.K),
+                        x_scales=us[perm], w_scales=tuple(sc for _, sc in routed))
+    ysh = np.stack([orc.grouped_ffn(np.array([0, cfg.T]), uq, *(q[j:j + 1] for q, _ in shared),
+                                    rows=np.arange(cfg.T), x_scales=us,
+                                    w_scales=tuple(sc[j:j + 1] for _, sc in shared)) for j in range(cfg.Ns)])
+    ref = orc.combine(y, inv, w, T=cfg.T, y_shared=ysh, residual=inp["u"])
+    assert (out == ref).all()
+    # and the routed part alone is what it is without the residual and shared experts
+    no_res, _, _, _ = orc.moe_forward(inp["u"], inp["gate_w"], inp["bias"], tuple(q for q, _ in routed), None,
+                                      w_code=orc.E4M3, out_code=orc.BF16,
+                                      routed_scales=tuple(sc for _, sc in routed), **kw)
+    assert (no_res == orc.combine(y, inv, w, T=cfg.T)).all()
+
+
+def test_single_expert_fp8_reduces_to_dense_swiglu(orc):
+    """N_r = K = 1 in e4m3 with two shared experts: the layer is three dense
+    SwiGLU FFNs (numpy matmuls) on the dequantised 1 x 128 tiles of u and the
+    dequantised 128 x 128 weight blocks, with each H re-tiled 1 x 128 and each
+    expert output stored in bf16, summed once (§3.3; the gate is s/s = 1)."""
+    cfg = syn.LayerConfig("t", T=24, d=384, Nr=1, G=1, Mg=1, K=1, Ns=2, I=256, dtype="bf16")
+    inp = syn.layer_inputs(cfg, seed=22)
+    routed, shared = _fp8_weights(orc, inp, cfg.Ns)
+    out, idx, w, _ = orc.moe_forward(inp["u"], inp["gate_w"], inp["bias"], tuple(q for q, _ in routed),
+                                     tuple(q for q, _ in shared), G=1, Mg=1, K=1, w_code=orc.E4M3,
+                                     out_code=orc.BF16, routed_scales=tuple(sc for _, sc in routed),
+                                     shared_scales=tuple(sc for _, sc in shared))
+    assert (idx == 0).all() and (w == 1.0).all()
+    dec = np.vectorize(orc.decode_e4m3)
+    dq = lambda q, s: dec(q) * np.kron(s, np.ones((128, 128)))
+    uq, us = orc.quant_1x128(inp["u"])
+    x = dec(uq) * np.repeat(us, 128, axis=1)
+    rb = lambda v: f32_of_bits(torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).view(torch.int16)
+                               .numpy().view(np.uint16)).astype(np.float64)
+
+    def tiled(h):
+        hq, hs = orc.quant_1x128(h.astype(np.float32))
+        return dec(hq) * np.repeat(hs, 128, axis=1)
+
+    total = np.zeros((cfg.T, cfg.d))
+    for (qg, sg), (qu, su), (qd, sd), e in [(*routed, 0)] + [(*shared, j) for j in range(cfg.Ns)]:
+        total += swiglu_dense(x, dq(qg[e], sg[e]), dq(qu[e], su[e]), dq(qd[e], sd[e]), tiled, rb)
+    ref = rb(total)
+    got = f32_of_bits(out).astype(np.float64)
+    assert np.abs(got - ref).max() <= 2.0 ** -8 * np.abs(ref).max()
+    # a shared expert that took the other's block scales would be far off
+    wrong = swiglu_dense(x, dq(shared[0][0][1], shared[0][1][0]), dq(shared[1][0][1], shared[1][1][0]),
+                         dq(shared[2][0][1], shared[2][1][0]), tiled, rb)
+    right = swiglu_dense(x, dq(shared[0][0][1], shared[0][1][1]), dq(shared[1][0][1], shared[1][1][1]),
+                         dq(shared[2][0][1], shared[2][1][1]), tiled, rb)
+    assert np.abs(wrong - right).max() > 2.0 ** -8 * np.abs(ref).max()
 
 
 # ---------------------------------------------------------------------------
