@@ -223,6 +223,30 @@ int moe_forward_timed(const moe_shape *shape, const void *u, const void *gate_w,
                       void *out, int32_t *topk_idx_out, float *topk_w_out, int32_t *counts_out,
                       float *scores_out, void *ws, size_t ws_bytes, void *stream, void *const *stage_events);
 
+/*
+ * moe_forward_static -- moe_forward for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  The caller passes inputs and outputs only (arguments,
+ * results and errors as for moe_forward); the workspace is a buffer of
+ * MOE_STATIC_WS_BYTES that the library keeps in device memory, one per GPU it
+ * runs on, for the life of the process.  No call allocates or frees memory.
+ * Limit: shapes whose moe_workspace_bytes(shape, MOE_WS_FORWARD) exceeds
+ * MOE_STATIC_WS_BYTES are rejected with MOE_ERR_WORKSPACE (at the V3 shape,
+ * d = 7168 with 256 + 1 experts of I = 2048 in bf16, that is T above about 400
+ * tokens: decode-size batches fit); MOE_SAVE_SWIGLU_INPUTS is rejected with
+ * MOE_ERR_UNSUPPORTED (the saved activations stay in the library's buffer,
+ * where moe_backward cannot read them).  Every call on one GPU shares that
+ * GPU's buffer, which keeps the last call's intermediate results: calls that
+ * overlap on one GPU (other streams, other host threads) race, so a caller
+ * serialises them.
+ */
+#define MOE_STATIC_WS_BYTES ((size_t)64 << 20)
+int moe_forward_static(const moe_shape *shape, const void *u, const void *gate_w, const float *bias,
+                       const void *const *routed_w, const float *const *routed_s,
+                       const void *const *shared_w, const float *const *shared_s,
+                       void *out, int32_t *topk_idx_out, float *topk_w_out, int32_t *counts_out,
+                       float *scores_out, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* backward                                                                 */
 

@@ -24,8 +24,10 @@ MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2
 MOE_ADD_RESIDUAL = 1
 MOE_SAVE_SWIGLU_INPUTS = 2   # moe_forward keeps the SwiGLU inputs for moe_backward
 MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_FORWARD = 0, 1, 2
+MOE_STATIC_WS_BYTES = 64 << 20   # the library's own forward workspace per GPU (moe_forward_static)
 
 EXPORTED = ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_timed",
+            "moe_forward_static",
             "moe_workspace_bytes",
             "moe_ffn_workspace_bytes", "moe_bias_update", "moe_seq_balance", "moe_seq_balance_workspace_bytes",
             "moe_transpose_expert_weights", "moe_backward", "moe_backward_timed", "moe_backward_workspace_bytes",
@@ -80,6 +82,7 @@ def lib():
                 "moe_combine": [S, P, P, P, P, P, P, P],
                 "moe_forward": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P],
                 "moe_forward_timed": [S, P, P, P, P, P, P, P, P, P, P, P, P, P, sz, P, P],
+                "moe_forward_static": [S, P, P, P, P, P, P, P, P, P, P, P, P, P],
                 "moe_bias_update": [S, P, P, ctypes.c_float, P],
                 "moe_seq_balance": [S, P, P, i64, ctypes.c_float, P, P, P, P, sz, P],
                 "moe_transpose_expert_weights": [S, i32, P, P, P, P, P],
@@ -208,6 +211,16 @@ def moe_forward(shape, u, gate_w, bias, routed_w, routed_s, shared_w, shared_s, 
                                     rs[0] if rs else None, sw[0] if sw else None, ss[0] if ss else None, _ptr(out),
                                     _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(counts_out), _ptr(scores_out),
                                     _ptr(ws), _nbytes(ws), _stream(stream)))
+
+
+def moe_forward_static(shape, u, gate_w, bias, routed_w, routed_s, shared_w, shared_s, out, topk_idx_out=None,
+                       topk_w_out=None, counts_out=None, scores_out=None, stream=None):
+    """moe_forward with the library's own per-GPU workspace (no caller workspace)."""
+    rw, rs, sw, ss = (_ptr_array(x) for x in (routed_w, routed_s, shared_w, shared_s))
+    return _check(lib().moe_forward_static(ctypes.byref(shape), _ptr(u), _ptr(gate_w), _ptr(bias),
+                                           rw[0] if rw else None, rs[0] if rs else None, sw[0] if sw else None,
+                                           ss[0] if ss else None, _ptr(out), _ptr(topk_idx_out), _ptr(topk_w_out),
+                                           _ptr(counts_out), _ptr(scores_out), _stream(stream)))
 
 
 def moe_forward_timed(shape, u, gate_w, bias, routed_w, routed_s, shared_w, shared_s, out, topk_idx_out=None,

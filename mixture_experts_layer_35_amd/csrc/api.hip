@@ -173,6 +173,45 @@ int run_ffn_pair(const moe_shape *s, const FfnProblem *gu, const FfnProblem *dn,
     return MOE_OK;
 }
 
+// ---- the library's own forward workspace (moe_forward_static) -------------------
+//
+// A file-scope device array: each GPU the library runs on holds its own copy for
+// the life of the process.  In host code `scratch` only names the symbol; its
+// device address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is ever handed to kernels or copies.
+constexpr size_t kStaticWsBytes = MOE_STATIC_WS_BYTES;
+static __device__ __align__(256) char scratch[kStaticWsBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_static_mu;
+void *g_static_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (nullptr and a message on failure).
+void *static_workspace(int *rc, const char *fn) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *rc = fail(MOE_ERR_HIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        *rc = fail(MOE_ERR_UNSUPPORTED, "%s: device %d is beyond the library's %d devices", fn, dev, kMaxDevices);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    if (!g_static_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            *rc = fail(MOE_ERR_HIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+            return nullptr;
+        }
+        g_static_ptr[dev] = p;
+    }
+    *rc = MOE_OK;
+    return g_static_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -337,12 +376,14 @@ int moe_forward(const moe_shape *s, const void *u, const void *gate_w, const flo
                              topk_w_out, counts_out, scores_out, ws, ws_bytes, stream, nullptr);
 }
 
-int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, const float *bias,
-                      const void *const *routed_w, const float *const *routed_s, const void *const *shared_w,
-                      const float *const *shared_s, void *out, int32_t *topk_idx_out, float *topk_w_out,
-                      int32_t *counts_out, float *scores_out, void *ws, size_t ws_bytes, void *stream,
-                      void *const *ev) {
-    const char *fn = "moe_forward";
+}  // extern "C"
+
+namespace {
+
+// Every argument check of the forward that needs no workspace (shape, pointers).
+int check_forward_args(const char *fn, const moe_shape *s, const void *u, const void *gate_w, const float *bias,
+                       const void *const *routed_w, const float *const *routed_s, const void *const *shared_w,
+                       const float *const *shared_s, void *out) {
     int rc = check_shape(s, fn);
     if (rc) return rc;
     NEED(u);
@@ -368,6 +409,16 @@ int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, con
                 return fail(MOE_ERR_INVALID_ARG, "%s: shared_s entries must not be NULL", fn);
         }
     }
+    return MOE_OK;
+}
+
+int forward_impl(const char *fn, const moe_shape *s, const void *u, const void *gate_w, const float *bias,
+                 const void *const *routed_w, const float *const *routed_s, const void *const *shared_w,
+                 const float *const *shared_s, void *out, int32_t *topk_idx_out, float *topk_w_out,
+                 int32_t *counts_out, float *scores_out, void *ws, size_t ws_bytes, void *stream, void *const *ev) {
+    int rc = check_forward_args(fn, s, u, gate_w, bias, routed_w, routed_s, shared_w, shared_s, out);
+    if (rc) return rc;
+    const bool fp8 = s->w_dtype == MOE_E4M3;
     const FwdLayout L = fwd_layout(s);
     rc = ws_check(ws, ws_bytes, L.total, fn);
     if (rc) return rc;
@@ -481,6 +532,38 @@ int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, con
                           (s->flags & MOE_ADD_RESIDUAL) ? u : nullptr, out, T, s->d, s->topk, st));
     HIPCHK(mark(5));
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_timed(const moe_shape *s, const void *u, const void *gate_w, const float *bias,
+                      const void *const *routed_w, const float *const *routed_s, const void *const *shared_w,
+                      const float *const *shared_s, void *out, int32_t *topk_idx_out, float *topk_w_out,
+                      int32_t *counts_out, float *scores_out, void *ws, size_t ws_bytes, void *stream,
+                      void *const *ev) {
+    return forward_impl("moe_forward", s, u, gate_w, bias, routed_w, routed_s, shared_w, shared_s, out, topk_idx_out,
+                        topk_w_out, counts_out, scores_out, ws, ws_bytes, stream, ev);
+}
+
+int moe_forward_static(const moe_shape *s, const void *u, const void *gate_w, const float *bias,
+                       const void *const *routed_w, const float *const *routed_s, const void *const *shared_w,
+                       const float *const *shared_s, void *out, int32_t *topk_idx_out, float *topk_w_out,
+                       int32_t *counts_out, float *scores_out, void *stream) {
+    const char *fn = "moe_forward_static";
+    int rc = check_forward_args(fn, s, u, gate_w, bias, routed_w, routed_s, shared_w, shared_s, out);
+    if (rc) return rc;
+    if (s->flags & MOE_SAVE_SWIGLU_INPUTS)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: MOE_SAVE_SWIGLU_INPUTS needs a caller workspace (moe_forward)", fn);
+    const size_t need = fwd_layout(s).total;
+    if (need > kStaticWsBytes)
+        return fail(MOE_ERR_WORKSPACE, "%s: the forward needs %zu workspace bytes, above the library's %zu", fn, need,
+                    kStaticWsBytes);
+    void *ws = static_workspace(&rc, fn);
+    if (!ws) return rc;
+    return forward_impl(fn, s, u, gate_w, bias, routed_w, routed_s, shared_w, shared_s, out, topk_idx_out,
+                        topk_w_out, counts_out, scores_out, ws, kStaticWsBytes, stream, nullptr);
 }
 
 // backward workspace: dy [TK][d], dg [TK], dz [TK], dh [R][I], dab [R][2I], dx [R][d] (R = TK + T*Ns);

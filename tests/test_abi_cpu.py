@@ -228,3 +228,25 @@ def test_backward_rejections(lib):
     s0 = tiny(T=0)
     assert lib.moe_backward(ctypes.byref(s0), None, None, None, None, None, None, None, None, None, None, None, 0,
                             None, None, None, None, None, None, None, 0, None) == moe.MOE_OK
+
+
+def test_static_forward_rejections_make_no_hip_call(lib):
+    """moe_forward_static (the forward on the library's own buffer) checks its
+    arguments on the host first: shapes, pointers, the saved-inputs flag and the
+    size limit of that buffer."""
+    w, wa = _parr(FAKE, FAKE, FAKE)
+    S = lambda s: ctypes.byref(s)
+    call = lambda s, u=FAKE: lib.moe_forward_static(S(s), u, FAKE, FAKE, w, None, w, None, FAKE, None, None, None,
+                                                    None, None)
+    assert call(tiny(d=200)) == moe.MOE_ERR_UNSUPPORTED
+    assert call(tiny(), u=None) == moe.MOE_ERR_INVALID_ARG
+    assert "moe_forward_static" in moe.moe_last_error()
+    assert call(tiny(flags=moe.MOE_SAVE_SWIGLU_INPUTS)) == moe.MOE_ERR_UNSUPPORTED
+    v3 = moe.make_shape(4096, 7168, 256, 1, 8, 4, 8, 2048, "bf16")
+    assert lib.moe_workspace_bytes(S(v3), moe.MOE_WS_FORWARD) > moe.MOE_STATIC_WS_BYTES
+    assert call(v3) == moe.MOE_ERR_WORKSPACE
+    # the limit admits decode-size batches of the V3 shape
+    dec = moe.make_shape(128, 7168, 256, 1, 8, 4, 8, 2048, "bf16")
+    assert lib.moe_workspace_bytes(S(dec), moe.MOE_WS_FORWARD) <= moe.MOE_STATIC_WS_BYTES
+    fp8 = moe.make_shape(256, 256, 16, 1, 4, 2, 2, 128, "fp8")
+    assert call(fp8) == moe.MOE_ERR_INVALID_ARG          # e4m3 weights need their block scales
