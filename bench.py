@@ -31,6 +31,16 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0                          # MI355X HBM3E
 PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp32": 157.3}
 STAGES = ("router", "dispatch", "ffn_gate_up", "ffn_down", "combine")
+ROTATE_SEED = 2000          # u of rotated batch k > 0 is drawn with seed 2000 + k
+FLUSH_BYTES = 512 << 20     # written between cold-stage launches: twice the 256 MB Infinity Cache
+
+
+def rotation_batches(cfg):
+    """Resident input batches the timed steps cycle through, so that a step's
+    router does not find its u in the 256 MB memory-side cache: at least four,
+    and together at least 512 MiB (at most 16)."""
+    act = 4 if cfg.dtype == "fp32" else 2
+    return int(min(16, max(4, -(-FLUSH_BYTES // (cfg.T * cfg.d * act)))))
 
 
 def esz(dtype):
@@ -167,17 +177,38 @@ def mfma_util_from_profile(cfg, kernel, backward=False):
 
 
 def cpu_model():
+    """The host CPU as /proc/cpuinfo names it (model name, family / model /
+    stepping of the first processor entry) and how many logical CPUs this
+    process may run on."""
+    fields = {}
     try:
         with open("/proc/cpuinfo") as f:
             for line in f:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if not line.strip():
+                    break                                   # first processor entry only
+                k, _, v = line.partition(":")
+                fields[k.strip()] = v.strip()
     except OSError:
-        pass
-    return None
+        return None
+    ids = ", ".join("%s %s" % (k, fields[k]) for k in ("cpu family", "model", "stepping") if k in fields)
+    return "%s (%s); %d logical CPUs in this process's affinity of %d online" % (
+        fields.get("model name", "?"), ids, len(os.sched_getaffinity(0)), os.cpu_count() or 0)
 
 
 def cpu_baseline(cfg, inp, n_tokens):
+    """The oracle on the first n/2 and the first n tokens of the batch: tokens/s
+    of the larger sample, and both per-token times (the oracle's work is per
+    token, so they agree when the sample rate stands for the whole batch)."""
+    half = _cpu_forward(cfg, inp, max(1, n_tokens // 2))
+    full = _cpu_forward(cfg, inp, n_tokens)
+    full["per_token_s"] = [half.pop("_per_token"), full.pop("_per_token")]
+    full["per_token_ratio"] = round(full["per_token_s"][1] / full["per_token_s"][0], 4)
+    full["sample"] += "; also timed on the first %d tokens: per-token time ratio %.3f" % (
+        max(1, n_tokens // 2), full["per_token_ratio"])
+    return full
+
+
+def _cpu_forward(cfg, inp, n_tokens):
     import numpy as np
     import oracle
     wcode = {"fp32": oracle.F32, "bf16": oracle.BF16, "fp8": oracle.E4M3}[cfg.dtype]
@@ -207,7 +238,7 @@ def cpu_baseline(cfg, inp, n_tokens):
                        w_code=wcode, out_code=ocode, tokens=tokens, routed_scales=rs, shared_scales=ss)
     dt = time.perf_counter() - t0
     return {"value": round(len(tokens) / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "cpu_model": cpu_model(),
+            "cpu_model": cpu_model(), "_per_token": dt / len(tokens),
             "sample": "first %d tokens of the same %d-token batch: routing, %d routed + %d shared SwiGLU experts "
                       "each, combine (fp64 sums)%s; %.1f s" % (len(tokens), cfg.T, cfg.K, cfg.Ns,
                                                                ", activation and H quantisation (weights "
@@ -254,6 +285,49 @@ def cpu_baseline_backward(cfg, inp, n_tokens):
                       "and centroid gradients not in the sample; %.1f s" % (
                           cfg.K, cfg.Ns, ", Dgrad operands in e4m3 tiles" if cfg.dtype == "fp8" else "", n, cfg.T,
                           dt)}
+
+
+def cold_stage_ms(moe, shape, cfg, layer, us, stream, n):
+    """Median time of the router (moe_route) and of the combine (moe_combine)
+    launched alone, each after a 512 MiB write that evicts L2 and the 256 MB
+    Infinity Cache, so that every operand comes from HBM.  The router cycles
+    through the resident batches; the combine reads the real routing of batch 0
+    (its inverse permutation and gates) and seeded expert-output rows."""
+    import numpy as np
+    import torch
+    T, K, Nr, d = cfg.T, cfg.K, cfg.Nr, cfg.d
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    scores = torch.empty((T, Nr), dtype=torch.float32, device="cuda")
+    idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    for k in range(n):
+        flush.fill_(k & 255)
+        ev[2 * k].record(stream)
+        moe.moe_route(shape, us[k % len(us)], layer.gate_w, layer.bias, None, scores, idx, w, None, stream)
+        ev[2 * k + 1].record(stream)
+    torch.cuda.synchronize()
+    router = float(np.median([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(n)]))
+    moe.moe_route(shape, us[0], layer.gate_w, layer.bias, None, scores, idx, w, None, stream)
+    counts, offsets = (torch.empty(m, dtype=torch.int32, device="cuda") for m in (Nr, Nr + 1))
+    perm, inv = (torch.empty(T * K, dtype=torch.int32, device="cuda") for _ in range(2))
+    pws = torch.empty(max(moe.moe_workspace_bytes(shape, moe.MOE_WS_PERMUTE), 256), dtype=torch.uint8, device="cuda")
+    moe.moe_permute(shape, idx, None, counts, offsets, perm, inv, None, None, pws, stream)
+    dt = us[0].dtype
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    y = torch.randn((T * K, d), generator=gen, device="cuda").to(dt)
+    ysh = torch.randn((cfg.Ns, T, d), generator=gen, device="cuda").to(dt) if cfg.Ns else None
+    out = torch.empty((T, d), dtype=dt, device="cuda")
+    for k in range(n):
+        flush.fill_(k & 255)
+        ev[2 * k].record(stream)
+        moe.moe_combine(shape, y, inv, w, ysh, None, out, stream)
+        ev[2 * k + 1].record(stream)
+    torch.cuda.synchronize()
+    combine = float(np.median([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(n)]))
+    del flush, y, ysh
+    torch.cuda.empty_cache()
+    return {"router": router, "combine": combine}
 
 
 def main():
@@ -309,7 +383,9 @@ def main():
         inp["u"] = batches[0]
         us = [to_device(b) for b in batches]
     else:
-        us = [to_device(inp["u"])]
+        # several resident batches (batch 0 is the recipe's u), cycled through by the steps
+        us = [to_device(inp["u"])] + [to_device(syn.hidden(cfg, seed=ROTATE_SEED + k))
+                                      for k in range(1, rotation_batches(cfg))]
     out = torch.empty((T, cfg.d), dtype=us[0].dtype, device="cuda")
     counts = torch.zeros((max(args.steps, 1), cfg.Nr), dtype=torch.int32, device="cuda")
     ws = layer.workspace(T)
@@ -378,6 +454,7 @@ def main():
         bstage_ms = {name: float(np.mean([bevs[k][i].elapsed_time(bevs[k][i + 1]) for k in range(args.steps)]))
                      for i, name in enumerate(BWD_STAGES)}
 
+    cold = cold_stage_ms(moe, shape, cfg, layer, us, stream, n=max(5, min(args.steps, 20))) if bw is None else None
     cnt = counts.cpu().numpy()
     n_touched = int(np.mean([(c > 0).sum() for c in cnt]))
     skew = None
@@ -430,6 +507,11 @@ def main():
         hbm_stages[name] = {"algorithmic_bytes": int(nb), "ms": round(stage_ms[name], 4), "GB/s": round(gbs, 1),
                             "frac": round(gbs / PEAK_HBM_GBS, 4),
                             "traffic": traffic_from_profile(cfg, STAGE_KERNELS[name])}
+        if cold and name in cold:
+            # the same call launched alone after a 512 MiB write (no operand in any cache)
+            cg = nb / (cold[name] / 1000.0) / 1e9
+            hbm_stages[name]["cold"] = {"ms": round(cold[name], 4), "GB/s": round(cg, 1),
+                                        "frac": round(cg / PEAK_HBM_GBS, 4)}
     # "% attainable": the layer's algorithmic flops against min(MFMA peak, AI x HBM peak),
     # with AI over the algorithmic bytes of every stage of the step
     fwd_alg = algorithmic(cfg, n_touched, saved)

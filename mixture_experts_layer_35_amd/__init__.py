@@ -17,7 +17,9 @@ import os
 import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libmoe.so")
+# MOE_LIB_PATH names another build of the same sources (the sanitizer tier's
+# host-instrumented library); the default is the in-tree libmoe.so
+LIB_PATH = os.environ.get("MOE_LIB_PATH") or os.path.join(PKG, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, -1, -2, -3, -4
 MOE_F32, MOE_BF16, MOE_E4M3 = 0, 1, 2

@@ -28,7 +28,9 @@ NC = 128
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# MOE_ORACLE_LIB names another build of moe_oracle.c to load (the sanitizer
+# tier's AddressSanitizer / UndefinedBehaviorSanitizer build)
+_LIB = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -42,6 +44,17 @@ def build(force: bool = True) -> str:
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB)
     return _LIB
+
+
+def build_sanitized(out: str) -> str:
+    """Compile moe_oracle.c with AddressSanitizer and UndefinedBehaviorSanitizer
+    (gcc; any report aborts) into ``out``; load it by running a process with
+    MOE_ORACLE_LIB=out and gcc's libasan preloaded."""
+    cmd = ["gcc", "-std=c11", "-O1", "-g", "-fno-omit-frame-pointer", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-shared", "-fPIC", _SRC,
+           "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
 
 
 def _load():

@@ -66,6 +66,41 @@ def run(layer, cfg, u_host):
     return dict(out=to_host(out), idx=to_host(idx), w=to_host(w), counts=to_host(counts), scores=to_host(scores))
 
 
+def row_blocks(m, bm=256):
+    """First row of each row block when an expert's m rows are split evenly over
+    ceil(m / bm) blocks (the expert kernel's tiles), plus m."""
+    mt = -(-m // bm)
+    mq, mr = divmod(m, mt)
+    return [b * mq + min(b, mr) for b in range(mt)] + [m]
+
+
+def covering_sample(idx_all, n, rng, experts):
+    """n random tokens, plus for every row block of every listed expert (rows in
+    token order, as the dispatch lays them out) one of its tokens if the random
+    draw missed the block.  Returns the sorted tokens and the number of blocks."""
+    T, _ = idx_all.shape
+    tokens = set(rng.choice(T, n, replace=False).tolist())
+    nblocks = 0
+    for e in experts:
+        rows = np.nonzero((idx_all == e).any(1))[0]           # the expert's tokens, increasing
+        b = row_blocks(len(rows))
+        for lo, hi in zip(b[:-1], b[1:]):
+            nblocks += 1
+            if not tokens.intersection(rows[lo:hi].tolist()):
+                tokens.add(int(rng.choice(rows[lo:hi])))
+    return np.array(sorted(tokens)), nblocks
+
+
+def assert_covers(idx_all, tokens, experts):
+    """Every row block of every listed expert holds a sampled token."""
+    sample = set(tokens.tolist())
+    for e in experts:
+        rows = np.nonzero((idx_all == e).any(1))[0]
+        b = row_blocks(len(rows))
+        for lo, hi in zip(b[:-1], b[1:]):
+            assert sample.intersection(rows[lo:hi].tolist()), (e, lo, hi)
+
+
 def check(cfg, T, got, ref, tokens, bias, tol):
     out_r, idx_r, _, s_r = ref
     same = np.array([(got["idx"][t] == idx_r[n]).all() for n, t in enumerate(tokens)])
@@ -90,14 +125,18 @@ def test_v3_prefill_bf16(moe, orc, v3, v3_routing):
     cfg, inp, layer = v3
     print("forward V3 bf16 T=%d" % cfg.T, flush=True)
     got = run(layer, cfg, inp["u"])
-    tokens = np.sort(np.random.default_rng(1).choice(cfg.T, 40, replace=False))
+    s_all, i_all, _ = v3_routing
+    # 512 random tokens, completed so that every expert's row block holds one of them
+    used = np.unique(i_all)
+    tokens, nb = covering_sample(i_all, 512, np.random.default_rng(1), used)
+    assert_covers(i_all, tokens, used)
+    print("sample: %d tokens covering %d row blocks of %d experts" % (len(tokens), nb, len(used)), flush=True)
     wcode, ocode = oracle_codes(cfg)
     ref = orc.moe_forward(inp["u"], inp["gate_w"], inp["bias"], (inp["wg"], inp["wu"], inp["wd"]),
                           (inp["swg"], inp["swu"], inp["swd"]), G=cfg.G, Mg=cfg.Mg, K=cfg.K, w_code=wcode,
                           out_code=ocode, tokens=tokens)
     check(cfg, cfg.T, got, ref, tokens, inp["bias"], 2e-2)
     # the whole batch routes as the oracle does, up to near ties of the fp32 affinities
-    s_all, i_all, _ = v3_routing
     same = (got["idx"] == i_all).all(1)
     for t in np.nonzero(~same)[0]:
         assert routing_disagreement_is_near_tie(s_all[t], inp["bias"], i_all[t], got["idx"][t], cfg.G, 4e-6), t
@@ -144,7 +183,7 @@ def test_v3_decode_bf16(moe, orc, v3):
     assert (u == inp["u"][: cfg.T]).all()
     print("forward V3 bf16 T=%d" % cfg.T, flush=True)
     got = run(layer, cfg, u)
-    tokens = np.arange(0, cfg.T, 2)
+    tokens = np.arange(cfg.T)                                 # every token of the decode batch
     wcode, ocode = oracle_codes(cfg)
     ref = orc.moe_forward(u, inp["gate_w"], inp["bias"], (inp["wg"], inp["wu"], inp["wd"]),
                           (inp["swg"], inp["swu"], inp["swd"]), G=cfg.G, Mg=cfg.Mg, K=cfg.K, w_code=wcode,
@@ -199,9 +238,17 @@ def test_v3_fp8(moe, orc, v3, v3_fp8):
     u = syn.hidden(cfg)
     print("forward V3 fp8 T=%d" % cfg.T, flush=True)
     got = run(layer, cfg, u)
-    tokens = np.sort(np.random.default_rng(2).choice(cfg.T, 16, replace=False))
-    _, idx_o, _ = orc.route(u, inp["gate_w"], inp["bias"], G=cfg.G, Mg=cfg.Mg, K=cfg.K, tokens=tokens)
-    routed_q, routed_s, shared_q, shared_s = quantise_for_oracle(orc, inp, np.unique(idx_o))
+    print("oracle routing of all %d tokens" % cfg.T, flush=True)
+    _, i_all, _ = orc.route(u, inp["gate_w"], inp["bias"], G=cfg.G, Mg=cfg.Mg, K=cfg.K)
+    # 512 random tokens, completed so that both row blocks of every expert (about 512
+    # rows each at T = 16384) hold one of them
+    used = np.unique(i_all)
+    tokens, nb = covering_sample(i_all, 512, np.random.default_rng(2), used)
+    assert_covers(i_all, tokens, used)
+    assert nb > len(used)
+    print("sample: %d tokens covering %d row blocks of %d experts" % (len(tokens), nb, len(used)), flush=True)
+    print("oracle: 128 x 128 blocks of the touched experts", flush=True)
+    routed_q, routed_s, shared_q, shared_s = quantise_for_oracle(orc, inp, np.unique(i_all[tokens]))
     ref = orc.moe_forward(u, inp["gate_w"], inp["bias"], tuple(routed_q), tuple(shared_q), G=cfg.G,
                           Mg=cfg.Mg, K=cfg.K, w_code=orc.E4M3, out_code=orc.BF16, tokens=tokens,
                           routed_scales=tuple(routed_s), shared_scales=tuple(shared_s))
@@ -256,7 +303,13 @@ def test_v3_skew_bias_steps(moe, orc, v3):
         if step == 0:
             # the recipe's skew: hottest expert near 8x the mean load
             assert 6.5 <= ratios[0] <= 9.5, ratios[0]
-            tokens = np.sort(np.random.default_rng(5).choice(T, 12, replace=False))
+            # 256 random tokens, completed so that every row block of the five hottest
+            # experts (up to 8 blocks each, split over the XCD queues) holds one of them
+            hot = np.argsort(-cr, kind="stable")[:5]
+            tokens, nb = covering_sample(ir, 256, np.random.default_rng(5), hot)
+            assert_covers(ir, tokens, hot)
+            print("  sample: %d tokens covering %d row blocks of the hottest experts %s (rows %s)"
+                  % (len(tokens), nb, hot.tolist(), cr[hot].tolist()), flush=True)
             wcode, ocode = oracle_codes(cfg)
             ref = orc.moe_forward(u, gate_w, bias_before, (inp["wg"], inp["wu"], inp["wd"]),
                                   (inp["swg"], inp["swu"], inp["swd"]), G=cfg.G, Mg=cfg.Mg, K=K, w_code=wcode,
