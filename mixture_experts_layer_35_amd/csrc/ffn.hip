@@ -362,33 +362,72 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
     // RPI*i + l/(CB/16) and stores into chunk slot l%(CB/16), which holds the
     // row's chunk slot ^ swz(row).
     const bool producer = wid < NP;
+    // a scalar copy of the wave id for load addresses (LDS destinations, row offsets); the
+    // divergent one keeps the compiler's loop structure around the producer branches
+    const int uwid = __builtin_amdgcn_readfirstlane(wid);
     const int csub = lane / (CB / 16), cslot = lane % (CB / 16);
     const int wrow0 = RPI * wid + csub;
+    // Loads go through buffer descriptors: a lane's byte offset within the tile
+    // stays fixed for the whole tile (a vector register), and the step's offset
+    // is a scalar, so issuing a load costs no vector instruction.
+    // (e4m3 tiles keep 64-bit per-lane addresses: their kernel has no scalar registers to spare)
+    constexpr bool BUFDMA = DT != DT_E4M3;
     const int wchunk = (cslot ^ swz<CB>(wrow0)) << 4;
+    const uint32_t woff = (uint32_t)(wrow0 * rowbytes) + wchunk;
 
-    // Everything one tile's loads and stores need.
+    // Everything one tile's loads and stores need (wave-uniform except the
+    // per-lane offsets).
     struct Tile {
         int p, valid, r0, n0, ntb, S, stage_bytes, srows, qmax, nextra;
         int nx;                       // token instructions of this producer per step
         bool spread;                  // double-buffered: loads spread over the products
+        bool xfar;                    // this producer's token rows span 4 GiB or more: 64-bit addresses
         int64_t base;                 // first row of the tile's expert
-        const char *wbase0, *wbase1;  // this producer's first weight row (gate and up, or down)
+        __amdgpu_buffer_rsrc_t rw0, rw1;   // buffer loads: the tile's weight rows (gate and up, or down)
+        __amdgpu_buffer_rsrc_t rx;         // buffer loads: token rows from this producer's lowest one
+        const char *wbase0, *wbase1;       // 64-bit loads: this producer's first weight row
+        int xrow[QX];                      // 64-bit loads: token rows of this producer's token instructions
         const float *xssrc, *wssrc;   // fp8 scale sources
         bool xs_live;
-        int xrow[QX];                 // token rows of this producer's token instructions
+        uint32_t xoff[QX];            // byte offsets of this producer's token rows in rx (row index if xfar)
+    };
+    auto wave_min = [](uint32_t v) {
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, m, 64));
+        return (uint32_t)__builtin_amdgcn_readfirstlane(v);
+    };
+    auto wave_max = [](uint32_t v) {
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, m, 64));
+        return (uint32_t)__builtin_amdgcn_readfirstlane(v);
+    };
+    constexpr int RSRC_FLAGS = 0x00020000;
+    auto rsrc = [](const void *p, uint64_t bytes) {
+        return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0,
+                                                 (int)(bytes > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)bytes),
+                                                 RSRC_FLAGS);
     };
     auto setup = [&](int t, Tile &T) {
+        t = __builtin_amdgcn_readfirstlane(t);
         T.p = t < total0 ? 0 : 1;
         const FfnProblem P = pick(a, T.p);
         const int *ppre = T.p ? pre1 : pre;
         const int lt = t - (T.p ? total0 : 0);
-        const int e = find_expert(ppre, P.n_exp, lt);
-        T.base = P.offsets ? (int64_t)P.offsets[e] : (int64_t)e * P.rows_fixed;
-        const int Me = P.offsets ? P.offsets[e + 1] - P.offsets[e] : (int)P.rows_fixed;
+        const int e = __builtin_amdgcn_readfirstlane(find_expert(ppre, P.n_exp, lt));
+        const int pe = __builtin_amdgcn_readfirstlane(ppre[e]);
+        int Me;
+        if (P.offsets) {
+            const int o0 = __builtin_amdgcn_readfirstlane(P.offsets[e]);
+            Me = __builtin_amdgcn_readfirstlane(P.offsets[e + 1]) - o0;
+            T.base = o0;
+        } else {
+            Me = (int)P.rows_fixed;
+            T.base = (int64_t)e * P.rows_fixed;
+        }
         // the expert's rows are split evenly over its row blocks, so row blocks that share
         // a weight block take equally long and stay close enough to share it through L2
         const int mt = (Me + BM - 1) / BM;
-        const int ln = lt - ppre[e];
+        const int ln = lt - pe;
         const int nt = ln / mt, mi = ln - nt * mt;
         const int mq = Me / mt, mr = Me - mq * mt;
         T.r0 = mi * mq + min(mi, mr);
@@ -416,28 +455,61 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
 #pragma unroll
             for (int q = 0; q < QX; ++q) T.nx += RPI * (q * NP + wid) < trows ? 1 : 0;
         }
-        // weight rows: instruction q < QW of this producer covers row RPI*(q*NP+wid) + csub.  The
-        // chunk permutation does not depend on q (RPI*NP rows apart), so one base pointer per
-        // weight matrix plus a per-instruction row stride addresses them all; in a ragged last
-        // tile (F - n0 < WR) the instructions past F re-read the last full instruction's rows.
-        T.wbase0 = (const char *)P.w0 + ((int64_t)e * F + T.n0 + wrow0) * rowbytes + wchunk;
-        T.wbase1 = GATEUP ? (const char *)P.w1 + ((int64_t)e * F + T.n0 + wrow0) * rowbytes + wchunk : T.wbase0;
+        // weight rows: instruction q < QW of this producer covers row RPI*(q*NP+wid) + csub
+        // of the tile; in a ragged last tile (F - n0 < WR) the instructions past F re-read
+        // the last full instruction's rows
+        if (BUFDMA) {
+            const uint64_t wbytes = (uint64_t)(F - T.n0) * rowbytes;
+            T.rw0 = rsrc((const char *)P.w0 + ((int64_t)e * F + T.n0) * rowbytes, wbytes);
+            T.rw1 = GATEUP ? rsrc((const char *)P.w1 + ((int64_t)e * F + T.n0) * rowbytes, wbytes) : T.rw0;
+        } else {
+            T.wbase0 = (const char *)P.w0 + ((int64_t)e * F + T.n0 + wrow0) * rowbytes + wchunk;
+            T.wbase1 = GATEUP ? (const char *)P.w1 + ((int64_t)e * F + T.n0 + wrow0) * rowbytes + wchunk : T.wbase0;
+        }
         T.qmax = GATEUP ? QW / 2 - 1 : min(QW, (F - T.n0) / (RPI * NP)) - 1;
+        T.nextra = 0;
+        T.xfar = false;
+        T.xs_live = false;
+        T.xssrc = T.wssrc = nullptr;
+        if (uwid >= NP) return;   // producers only (tested on the scalar wave id: the rest stays uniform)
         // token rows: instruction q of this producer covers token RPI*(q*NP+wid) + csub
+        if (!BUFDMA) {
+#pragma unroll
+            for (int q = 0; q < QX; ++q) {
+                const int r = min(RPI * (q * NP + wid) + csub, T.valid - 1);
+                const int64_t R = T.base + T.r0 + r;
+                T.xrow[q] = P.gather ? P.gather[R] : (int)(P.x_local ? (int64_t)(T.r0 + r) : R);
+            }
+        } else {
+        uint32_t xr[QX];
 #pragma unroll
         for (int q = 0; q < QX; ++q) {
             const int r = min(RPI * (q * NP + wid) + csub, T.valid - 1);
             const int64_t R = T.base + T.r0 + r;
-            T.xrow[q] = P.gather ? P.gather[R] : (int)(P.x_local ? (int64_t)(T.r0 + r) : R);
+            xr[q] = (uint32_t)(P.gather ? P.gather[R] : (P.x_local ? (int64_t)(T.r0 + r) : R));
         }
-        // fp8 scales, 4-byte DMAs into the stage's scale area: producer w stages
-        // the activation scales of tokens 64w .. 64w+63 (while any is valid);
-        // producer 0 also stages the two weight block scales at slots BM, BM+1
-        // (gate/up: gate and up block; down: first and second 128-row block).
-        T.nextra = 0;
-        T.xssrc = T.wssrc = nullptr;
-        T.xs_live = false;
-        if (FP8 && producer) {
+        uint32_t lo = xr[0], hi = xr[0];
+#pragma unroll
+        for (int q = 1; q < QX; ++q) {
+            lo = min(lo, xr[q]);
+            hi = max(hi, xr[q]);
+        }
+        lo = wave_min(lo);
+        hi = wave_max(hi);
+        const uint64_t span = (uint64_t)(hi - lo + 1) * (uint64_t)rowbytes;
+        T.xfar = span > 0xFFFFFFFFull;
+        T.rx = rsrc((const char *)P.x + (int64_t)lo * rowbytes, span);
+#pragma unroll
+        for (int q = 0; q < QX; ++q) {
+            const int row = WR + RPI * (q * NP + wid) + csub;
+            T.xoff[q] = T.xfar ? xr[q] : (uint32_t)((xr[q] - lo) * (uint64_t)rowbytes) + ((cslot ^ swz<CB>(row)) << 4);
+        }
+        }
+        // fp8 scales, 4-byte loads into the stage's scale area: producer w stages the
+        // activation scales of tokens 64w .. 64w+63 (while any is valid); producer 0 also
+        // stages the two weight block scales at slots BM, BM+1 (gate/up: gate and up
+        // block; down: first and second 128-row block)
+        if (FP8) {
             const int r = min(wid * 64 + lane, T.valid - 1);
             const int64_t R = T.base + T.r0 + r;
             const int64_t xr = P.gather ? (int64_t)P.gather[R] : (P.x_local ? (int64_t)(T.r0 + r) : R);
@@ -457,29 +529,49 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
     // Load q of one step by this producer: q < QW are weight instructions, the
     // rest token instructions (NTB of them cover 32*NTB token rows).
     auto dma_one = [&](const Tile &T, int q, int ks, char *st) {
-        // an opaque copy of the row stride keeps the per-instruction addresses
-        // from being hoisted out of the reduction loop (they would occupy
-        // ~32 VGPRs for the whole tile); recomputing them costs a few SALU/VALU ops
-        int64_t rb = rowbytes;
-        asm volatile("" : "+s"(rb));
+        if (!BUFDMA) {
+            // an opaque copy of the row stride keeps the per-instruction addresses
+            // from being hoisted out of the reduction loop (they would occupy
+            // ~32 VGPRs for the whole tile); recomputing them costs a few SALU/VALU ops
+            int64_t rb = rowbytes;
+            asm volatile("" : "+s"(rb));
+            if (q < QW) {
+                const bool up = GATEUP && q >= QW / 2;
+                const int qq = min(GATEUP ? (up ? q - QW / 2 : q) : q, T.qmax);
+                const char *src = (up ? T.wbase1 : T.wbase0) + (int64_t)qq * (RPI * NP) * rb + (int64_t)ks * CB;
+                dma16(src, st + (q * NP + wid) * 1024);
+            } else {
+                const int qx = q - QW;
+                const int ins = qx * NP + wid;
+                const int row = WR + RPI * ins + csub;
+                const char *src = (const char *)pick(a, T.p).x + (int64_t)T.xrow[qx] * rb + (int64_t)ks * CB +
+                                  ((cslot ^ swz<CB>(row)) << 4);
+                dma16(src, st + (WR / RPI + ins) * 1024);
+            }
+            return;
+        }
         if (q < QW) {
             // gate/up: instructions q < QW/2 read gate rows, the rest the matching up rows
             const bool up = GATEUP && q >= QW / 2;
             const int qq = min(GATEUP ? (up ? q - QW / 2 : q) : q, T.qmax);
-            const char *src = (up ? T.wbase1 : T.wbase0) + (int64_t)qq * (RPI * NP) * rb + (int64_t)ks * CB;
-            dma16(src, st + (q * NP + wid) * 1024);
+            const int soff = qq * (RPI * NP) * (int)rowbytes + ks * CB;
+            buffer_dma16(up ? T.rw1 : T.rw0, woff, soff, st + (q * NP + uwid) * 1024);
         } else {
             const int qx = q - QW;
-            const int ins = qx * NP + wid;
-            const int row = WR + RPI * ins + csub;
-            const char *src = (const char *)pick(a, T.p).x + (int64_t)T.xrow[qx] * rb + (int64_t)ks * CB +
-                              ((cslot ^ swz<CB>(row)) << 4);
-            dma16(src, st + (WR / RPI + ins) * 1024);
+            const int ins = qx * NP + uwid;
+            char *dst = st + (WR / RPI + ins) * 1024;
+            if (!T.xfar) {
+                buffer_dma16(T.rx, T.xoff[qx], ks * CB, dst);
+            } else {
+                const int row = WR + RPI * ins + csub;
+                dma16((const char *)pick(a, T.p).x + (int64_t)T.xoff[qx] * rowbytes + (int64_t)ks * CB +
+                          ((cslot ^ swz<CB>(row)) << 4), dst);
+            }
         }
     };
     auto dma_scales = [&](const Tile &T, int ks, char *st) {
         if (FP8) {
-            if (T.xs_live) dma4(T.xssrc + ks, st + T.srows * CB + wid * 256);
+            if (T.xs_live) dma4(T.xssrc + ks, st + T.srows * CB + uwid * 256);
             if (wid == 0) dma4(T.wssrc + ks, st + T.srows * CB + BM * 4);
         }
     };
@@ -508,7 +600,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
         slot[1] = grab_tile(a.ctr, bounds, xcd, slot + 3);
     }
     __syncthreads();
-    const int first = slot[0];
+    const int first = __builtin_amdgcn_readfirstlane(slot[0]);
     Tile cur, nxt;
     if (first >= 0) {
         setup(first, cur);
@@ -589,7 +681,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
         // write this tile's results while they are in flight.
         cta_barrier();
         const int it1 = it == 2 ? 0 : it + 1, it2 = it1 == 2 ? 0 : it1 + 1;
-        const int tn = slot[it1];
+        const int tn = __builtin_amdgcn_readfirstlane(slot[it1]);
         if (grabber && tn >= 0) {
             // slot it2 was last read at the end of the previous iteration, before this
             // tile's barriers; it is read at the end of the next tile, after its barriers

@@ -134,5 +134,15 @@ __device__ __forceinline__ void dma4(const void *g, void *l) {
     __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 4, 0, 0);
 }
 
+// The same loads through a buffer descriptor: address = base + voff (per lane)
+// + soff (wave-uniform), so a step's loads need scalar arithmetic only.  Offsets
+// at or past the descriptor's byte count read as zero.
+__device__ __forceinline__ void buffer_dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, void *l) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)l, 16, (int)voff, soff, 0, 0);
+}
+__device__ __forceinline__ void buffer_dma4(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, void *l) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)l, 4, (int)voff, soff, 0, 0);
+}
+
 }  // namespace
 }  // namespace moe
