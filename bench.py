@@ -301,14 +301,15 @@ def cold_stage_ms(moe, shape, cfg, layer, us, stream, n):
     idx = torch.empty((T, K), dtype=torch.int32, device="cuda")
     w = torch.empty((T, K), dtype=torch.float32, device="cuda")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+    rws = torch.empty(max(moe.moe_workspace_bytes(shape, moe.MOE_WS_ROUTE), 256), dtype=torch.uint8, device="cuda")
     for k in range(n):
         flush.fill_(k & 255)
         ev[2 * k].record(stream)
-        moe.moe_route(shape, us[k % len(us)], layer.gate_w, layer.bias, None, scores, idx, w, None, stream)
+        moe.moe_route(shape, us[k % len(us)], layer.gate_w, layer.bias, None, scores, idx, w, rws, stream)
         ev[2 * k + 1].record(stream)
     torch.cuda.synchronize()
     router = float(np.median([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(n)]))
-    moe.moe_route(shape, us[0], layer.gate_w, layer.bias, None, scores, idx, w, None, stream)
+    moe.moe_route(shape, us[0], layer.gate_w, layer.bias, None, scores, idx, w, rws, stream)
     counts, offsets = (torch.empty(m, dtype=torch.int32, device="cuda") for m in (Nr, Nr + 1))
     perm, inv = (torch.empty(T * K, dtype=torch.int32, device="cuda") for _ in range(2))
     pws = torch.empty(max(moe.moe_workspace_bytes(shape, moe.MOE_WS_PERMUTE), 256), dtype=torch.uint8, device="cuda")

@@ -122,6 +122,13 @@ typedef struct moe_shape {
  * scores_in [T][N_r] fp32 or NULL: when given, u and gate_w are not read and
  * selection runs on these affinities (bit-exact routing checks).
  * scores_out [T][N_r] fp32 or NULL; topk_idx [T][K] int32; topk_w [T][K] fp32.
+ * ws: moe_workspace_bytes(shape, MOE_WS_ROUTE) bytes (256-byte aligned): the
+ * affinities when scores_out is NULL, and for bf16 layers of 256 routed experts
+ * in groups of a multiple of 16 experts with topk <= 16 the chunk partials of
+ * a split-K gate GEMM (fp32 partial dot products over chunks of the hidden
+ * dimension, summed in chunk order).  Given less workspace (at least the
+ * affinities' when scores_out is NULL) the single-pass gate GEMM runs instead:
+ * the affinities agree up to the order of the fp32 additions.
  */
 int moe_route(const moe_shape *shape, const void *u, const void *gate_w, const float *bias,
               const float *scores_in, float *scores_out, int32_t *topk_idx, float *topk_w,

@@ -117,7 +117,7 @@ int dt_of(int d) { return d == MOE_F32 ? DT_F32 : d == MOE_BF16 ? DT_BF16 : DT_E
 // ---- workspace layouts --------------------------------------------------------
 
 struct FwdLayout {
-    size_t scores, idx, w, counts, offsets, bc, perm, inv, uq, us, h, hs, hsh, hshs, yperm, ysh, fq, ab, total;
+    size_t scores, idx, w, counts, offsets, bc, perm, inv, uq, us, h, hs, hsh, hshs, yperm, ysh, fq, ab, rpart, total;
 };
 
 FwdLayout fwd_layout(const moe_shape *s) {
@@ -147,6 +147,9 @@ FwdLayout fwd_layout(const moe_shape *s) {
     L.fq = take(FFN_QUEUE_INTS * 4);
     // SwiGLU inputs a | b of the routed rows, then of the shared rows (MOE_SAVE_SWIGLU_INPUTS)
     L.ab = take((s->flags & MOE_SAVE_SWIGLU_INPUTS) ? (size_t)(TK + TS) * 2 * s->inter * 4 : 0);
+    // the split-K router's chunk partials of the gate products
+    L.rpart = take(router_splitk_ok(dt_of(s->act_dtype), s->n_routed, s->n_groups, s->topk)
+                       ? router_partial_bytes(T, s->d, s->n_routed) : 0);
     L.total = o;
     return L;
 }
@@ -223,7 +226,10 @@ const char *moe_version(void) { return "libmoe 0.1 (gfx950)"; }
 size_t moe_workspace_bytes(const moe_shape *s, int which) {
     if (check_shape(s, "moe_workspace_bytes") != MOE_OK) return 0;
     switch (which) {
-        case MOE_WS_ROUTE: return align256((size_t)s->T * s->n_routed * 4);
+        case MOE_WS_ROUTE:
+            return align256((size_t)s->T * s->n_routed * 4) +
+                   (router_splitk_ok(dt_of(s->act_dtype), s->n_routed, s->n_groups, s->topk)
+                        ? align256(router_partial_bytes(s->T, s->d, s->n_routed)) : 0);
         case MOE_WS_PERMUTE: return align256((size_t)perm_blocks(s->T) * s->n_routed * 4);
         case MOE_WS_FORWARD: return fwd_layout(s).total;
         default: fail(MOE_ERR_INVALID_ARG, "moe_workspace_bytes: unknown workspace kind %d", which); return 0;
@@ -249,13 +255,26 @@ int moe_route(const moe_shape *s, const void *u, const void *gate_w, const float
         NEED(gate_w);
     }
     float *scores = scores_out;
+    const size_t sbytes = align256((size_t)s->T * s->n_routed * 4);
     if (!scores_in && !scores) {
-        rc = ws_check(ws, ws_bytes, align256((size_t)s->T * s->n_routed * 4), fn);
+        rc = ws_check(ws, ws_bytes, sbytes, fn);
         if (rc) return rc;
         scores = (float *)ws;
     }
+    // the split-K gate GEMM when the workspace also holds its chunk partials
+    float *part = nullptr;
+    if (!scores_in && router_splitk_ok(dt_of(s->act_dtype), s->n_routed, s->n_groups, s->topk) && ws &&
+        !((uintptr_t)ws & 255)) {
+        const size_t off = scores_out ? 0 : sbytes;
+        if (ws_bytes >= off + align256(router_partial_bytes(s->T, s->d, s->n_routed))) part = (float *)((char *)ws + off);
+    }
     if (s->T == 0) return MOE_OK;
     hipStream_t st = (hipStream_t)stream;
+    if (part) {
+        HIPCHK(launch_router_splitk(u, gate_w, part, scores, bias, s->T, s->d, s->n_groups, s->topk_groups, s->topk,
+                                    s->routed_scale, topk_idx, topk_w, st));
+        return MOE_OK;
+    }
     if (scores_in) {
         if (scores_out)
             HIPCHK(hipMemcpyAsync(scores_out, scores_in, (size_t)s->T * s->n_routed * 4, hipMemcpyDeviceToDevice, st));
@@ -443,9 +462,14 @@ int forward_impl(const char *fn, const moe_shape *s, const void *u, const void *
     };
     // 1. affinities and selection
     HIPCHK(mark(0));
-    HIPCHK(launch_router_gemm(dt_of(s->act_dtype), u, gate_w, scores, T, s->d, s->n_routed, st));
-    HIPCHK(launch_router_select(scores, bias, T, s->n_routed, s->n_groups, s->topk_groups, s->topk, s->routed_scale,
-                                idx, tw, st));
+    if (router_splitk_ok(dt_of(s->act_dtype), s->n_routed, s->n_groups, s->topk)) {
+        HIPCHK(launch_router_splitk(u, gate_w, (float *)(W + L.rpart), scores, bias, T, s->d, s->n_groups,
+                                    s->topk_groups, s->topk, s->routed_scale, idx, tw, st));
+    } else {
+        HIPCHK(launch_router_gemm(dt_of(s->act_dtype), u, gate_w, scores, T, s->d, s->n_routed, st));
+        HIPCHK(launch_router_select(scores, bias, T, s->n_routed, s->n_groups, s->topk_groups, s->topk,
+                                    s->routed_scale, idx, tw, st));
+    }
     if (scores_out)
         HIPCHK(hipMemcpyAsync(scores_out, scores, (size_t)T * s->n_routed * 4, hipMemcpyDeviceToDevice, st));
     if (topk_idx_out) HIPCHK(hipMemcpyAsync(topk_idx_out, idx, (size_t)TK * 4, hipMemcpyDeviceToDevice, st));

@@ -370,7 +370,8 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
     // Loads go through buffer descriptors: a lane's byte offset within the tile
     // stays fixed for the whole tile (a vector register), and the step's offset
     // is a scalar, so issuing a load costs no vector instruction.
-    // (e4m3 tiles keep 64-bit per-lane addresses: their kernel has no scalar registers to spare)
+    // (e4m3 tiles use 64-bit addresses from a wave-uniform base instead: their kernel has no
+    // scalar registers to spare for descriptors)
     constexpr bool BUFDMA = DT != DT_E4M3;
     const int wchunk = (cslot ^ swz<CB>(wrow0)) << 4;
     const uint32_t woff = (uint32_t)(wrow0 * rowbytes) + wchunk;
@@ -386,7 +387,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
         __amdgpu_buffer_rsrc_t rw0, rw1;   // buffer loads: the tile's weight rows (gate and up, or down)
         __amdgpu_buffer_rsrc_t rx;         // buffer loads: token rows from this producer's lowest one
         const char *wbase0, *wbase1;       // 64-bit loads: this producer's first weight row
-        int xrow[QX];                      // 64-bit loads: token rows of this producer's token instructions
+        const char *xb;                    // 64-bit loads: this producer's lowest token row (wave-uniform)
         const float *xssrc, *wssrc;   // fp8 scale sources
         bool xs_live;
         uint32_t xoff[QX];            // byte offsets of this producer's token rows in rx (row index if xfar)
@@ -473,14 +474,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
         T.xssrc = T.wssrc = nullptr;
         if (uwid >= NP) return;   // producers only (tested on the scalar wave id: the rest stays uniform)
         // token rows: instruction q of this producer covers token RPI*(q*NP+wid) + csub
-        if (!BUFDMA) {
-#pragma unroll
-            for (int q = 0; q < QX; ++q) {
-                const int r = min(RPI * (q * NP + wid) + csub, T.valid - 1);
-                const int64_t R = T.base + T.r0 + r;
-                T.xrow[q] = P.gather ? P.gather[R] : (int)(P.x_local ? (int64_t)(T.r0 + r) : R);
-            }
-        } else {
+        {
         uint32_t xr[QX];
 #pragma unroll
         for (int q = 0; q < QX; ++q) {
@@ -498,7 +492,8 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
         hi = wave_max(hi);
         const uint64_t span = (uint64_t)(hi - lo + 1) * (uint64_t)rowbytes;
         T.xfar = span > 0xFFFFFFFFull;
-        T.rx = rsrc((const char *)P.x + (int64_t)lo * rowbytes, span);
+        if (BUFDMA) T.rx = rsrc((const char *)P.x + (int64_t)lo * rowbytes, span);
+        else T.xb = (const char *)P.x + (T.xfar ? 0 : (int64_t)lo * rowbytes);
 #pragma unroll
         for (int q = 0; q < QX; ++q) {
             const int row = WR + RPI * (q * NP + wid) + csub;
@@ -528,11 +523,13 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
     };
     // Load q of one step by this producer: q < QW are weight instructions, the
     // rest token instructions (NTB of them cover 32*NTB token rows).
-    auto dma_one = [&](const Tile &T, int q, int ks, char *st) {
+    auto dma_one = [&](const Tile &T, int q, int ks, char *st, auto farc) {
+        constexpr bool FAR = decltype(farc)::value;
         if (!BUFDMA) {
-            // an opaque copy of the row stride keeps the per-instruction addresses
-            // from being hoisted out of the reduction loop (they would occupy
-            // ~32 VGPRs for the whole tile); recomputing them costs a few SALU/VALU ops
+            // a wave-uniform base plus the step's offset (scalar), plus the lane's fixed
+            // 32-bit offset: one 64-bit vector add per load
+            // an opaque copy of the row stride keeps the per-instruction offsets from being
+            // hoisted out of the reduction loop into registers held for the whole tile
             int64_t rb = rowbytes;
             asm volatile("" : "+s"(rb));
             if (q < QW) {
@@ -542,11 +539,13 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                 dma16(src, st + (q * NP + wid) * 1024);
             } else {
                 const int qx = q - QW;
-                const int ins = qx * NP + wid;
-                const int row = WR + RPI * ins + csub;
-                const char *src = (const char *)pick(a, T.p).x + (int64_t)T.xrow[qx] * rb + (int64_t)ks * CB +
-                                  ((cslot ^ swz<CB>(row)) << 4);
-                dma16(src, st + (WR / RPI + ins) * 1024);
+                const int ins = qx * NP + uwid;
+                char *dst = st + (WR / RPI + ins) * 1024;
+                // far rows (a loop of their own): xoff holds the row itself; the chunk slot of
+                // every token row this lane fills equals that of its weight rows (the swizzle
+                // sees row bits 0-3 only)
+                if (FAR) dma16(T.xb + (int64_t)T.xoff[qx] * rb + (int64_t)ks * CB + wchunk, dst);
+                else dma16(T.xb + (int64_t)(ks * CB) + T.xoff[qx], dst);
             }
             return;
         }
@@ -560,13 +559,8 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
             const int qx = q - QW;
             const int ins = qx * NP + uwid;
             char *dst = st + (WR / RPI + ins) * 1024;
-            if (!T.xfar) {
-                buffer_dma16(T.rx, T.xoff[qx], ks * CB, dst);
-            } else {
-                const int row = WR + RPI * ins + csub;
-                dma16((const char *)pick(a, T.p).x + (int64_t)T.xoff[qx] * rowbytes + (int64_t)ks * CB +
-                          ((cslot ^ swz<CB>(row)) << 4), dst);
-            }
+            if (!T.xfar) buffer_dma16(T.rx, T.xoff[qx], ks * CB, dst);
+            else dma16((const char *)pick(a, T.p).x + (int64_t)T.xoff[qx] * rowbytes + (int64_t)ks * CB + wchunk, dst);
         }
     };
     auto dma_scales = [&](const Tile &T, int ks, char *st) {
@@ -584,7 +578,10 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
             dma_scales(T, ks, st);
 #pragma unroll
             for (int q = 0; q < QW + QX; ++q)
-                if (q < ndma) dma_one(T, q, ks, st);
+                if (q < ndma) {
+                    if (!BUFDMA && T.xfar) dma_one(T, q, ks, st, std::true_type{});
+                    else dma_one(T, q, ks, st, std::false_type{});
+                }
         }
     };
 
@@ -624,7 +621,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
         // stores are younger than them in this wave's memory counter: waiting
         // for at most (S-2) steps outstanding covers them conservatively.
         const int S = cur.S, stage_bytes = cur.stage_bytes, srows = cur.srows;
-        auto kloop = [&](auto ntb, auto spread) {
+        auto kloop = [&](auto ntb, auto spread, auto farc) {
             constexpr int NTB = decltype(ntb)::value;
             constexpr bool SPREAD = decltype(spread)::value;
             constexpr int NDMA = QW + NTB * 16 * WM / RPI / NP;   // loads per producer per step, at most
@@ -648,13 +645,13 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                         // a deeper ring has room to load ahead: issue the whole step first
 #pragma unroll
                         for (int q = 0; q < NDMA; ++q)
-                            if (q < QW + cur.nx) dma_one(cur, q, ks, dst);
+                            if (q < QW + cur.nx) dma_one(cur, q, ks, dst, farc);
                         compute_step<DT, GATEUP, NTB, false, NDMA>(st, sc, acc, wm, wf, lane, [](int) {});
                     } else {
                         // double buffering: spread the loads over the products so this
                         // wave's share of the products is not held up behind them
                         compute_step<DT, GATEUP, NTB, true, NDMA>(st, sc, acc, wm, wf, lane,
-                                                                  [&](int q) { dma_one(cur, q, ks, dst); });
+                                                                  [&](int q) { dma_one(cur, q, ks, dst, farc); });
                     }
                 } else {
                     compute_step<DT, GATEUP, NTB, false, NDMA>(st, sc, acc, wm, wf, lane, [](int) {});
@@ -663,8 +660,14 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
             }
         };
         auto kloop_s = [&](auto ntb) {
-            if (cur.spread) kloop(ntb, std::true_type{});
-            else kloop(ntb, std::false_type{});
+            if (!BUFDMA && cur.xfar) {
+                // e4m3 tiles whose token rows span 4 GiB or more: 64-bit row addresses
+                if (cur.spread) kloop(ntb, std::true_type{}, std::true_type{});
+                else kloop(ntb, std::false_type{}, std::true_type{});
+            } else {
+                if (cur.spread) kloop(ntb, std::true_type{}, std::false_type{});
+                else kloop(ntb, std::false_type{}, std::false_type{});
+            }
         };
         switch (cur.ntb) {
             case 1: kloop_s(std::integral_constant<int, 1>{}); break;

@@ -16,6 +16,14 @@ int device_cus();
 // scores[T][Nr] = sigmoid(u[T][d] . gate_w[Nr][d]^T), fp32 accumulation.
 hipError_t launch_router_gemm(int dt, const void *u, const void *gate_w, float *scores, int64_t T, int d, int Nr,
                               hipStream_t s);
+// Split-K gate GEMM over all experts (bf16, Nr == 256, groups of a multiple of 16
+// experts, K <= 16): chunk partials to part (router_partial_bytes), then affinities
+// (to scores, when not null), selection and gates in one finishing kernel.
+bool router_splitk_ok(int dt, int Nr, int G, int K);
+size_t router_partial_bytes(int64_t T, int d, int Nr);
+hipError_t launch_router_splitk(const void *u, const void *gate_w, float *part, float *scores, const float *bias,
+                                int64_t T, int d, int G, int Mg, int K, float routed_scale, int32_t *topk_idx,
+                                float *topk_w, hipStream_t s);
 // Group-limited biased top-K selection and normalised gates from fp32 scores.
 hipError_t launch_router_select(const float *scores, const float *bias, int64_t T, int Nr, int G, int Mg, int K,
                                 float routed_scale, int32_t *topk_idx, float *topk_w, hipStream_t s);

@@ -94,7 +94,10 @@ def test_quantize_128x128_bitexact(moe, orc):
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("T,Nr,G,Mg,K", [(256, 16, 4, 2, 2), (1000, 256, 8, 4, 8), (67, 64, 1, 1, 6),
-                                         (129, 32, 8, 8, 5), (300, 1024, 64, 3, 32), (5, 8, 8, 2, 1)])
+                                         (129, 32, 8, 8, 5), (300, 1024, 64, 3, 32), (5, 8, 8, 2, 1),
+                                         # 256 experts: the 16-lane selection, groups of 16 .. 256 experts
+                                         (333, 256, 16, 5, 16), (70, 256, 2, 1, 7), (61, 256, 1, 1, 3),
+                                         (17, 256, 4, 2, 8)])
 @pytest.mark.parametrize("ties", [False, True])
 def test_route_selection_bitexact(moe, orc, T, Nr, G, Mg, K, ties):
     s = syn.random_scores(T, Nr, seed=T + Nr)
@@ -115,9 +118,13 @@ def test_route_selection_bitexact(moe, orc, T, Nr, G, Mg, K, ties):
 
 def test_route_affinities_close_and_selection_consistent(moe, orc):
     # the last two shapes have enough 128-token tiles to take the wide gate-GEMM tiles
+    # 256 bf16 experts take the split-K gate GEMM: 64-token tiles below 2048 tokens, 128 above
     for cfg in (syn.CONFIGS["tiny"], small_cfg("bf16", 200, d=1024, Nr=64, G=8, Mg=4, K=8),
                 small_cfg("bf16", 4200, d=256, Nr=1024, G=16, Mg=4, K=8),
-                small_cfg("fp32", 4100, d=128, Nr=1024, G=8, Mg=2, K=6)):
+                small_cfg("fp32", 4100, d=128, Nr=1024, G=8, Mg=2, K=6),
+                small_cfg("bf16", 777, d=1024, Nr=256, G=8, Mg=4, K=8),
+                small_cfg("bf16", 2500, d=768, Nr=256, G=2, Mg=1, K=6),
+                small_cfg("bf16", 33, d=2048, Nr=256, G=16, Mg=3, K=16)):
         u = syn.hidden(cfg)
         g, b = syn.router_params(cfg)
         shape = shape_of(cfg)
@@ -134,6 +141,16 @@ def test_route_affinities_close_and_selection_consistent(moe, orc):
         for t in range(cfg.T):
             if not (ig[t] == ir[t]).all():
                 assert routing_disagreement_is_near_tie(sr[t], b, ir[t], ig[t], cfg.G, 4e-6), t
+        if cfg.Nr == 256 and cfg.dtype == "bf16":
+            # without room for the chunk partials the single-pass gate GEMM runs: the same
+            # affinities up to fp32 rounding, and the same selection up to near ties
+            so1 = empty((cfg.T, cfg.Nr), torch.float32)
+            idx1 = empty((cfg.T, cfg.K), torch.int32)
+            moe.moe_route(shape, dev(u), dev(g), dev(b), None, so1, idx1, w, None)
+            assert np.abs(host(so1).astype(np.float64) - sg).max() <= 2e-6
+            i1 = host(idx1)
+            for t in np.nonzero(~(i1 == ig).all(1))[0]:
+                assert routing_disagreement_is_near_tie(sr[t], b, ir[t], i1[t], cfg.G, 4e-6), t
 
 
 # ---------------------------------------------------------------------------
