@@ -493,6 +493,14 @@ constexpr int WGB_IDX = 256;                              // gather indices of a
 template <int PW> constexpr int wgb_stage() { return (PW + 1) * WGB_PB + WGB_IDX; }
 template <int PW> constexpr int wgb_lds() { return wgb_s<PW>() * wgb_stage<PW>(); }
 template <int PW> constexpr int wgb_nt() { return 64 * (4 * PW + 2); }
+// P-resident tiles (256-wide p tile only): an expert of at most WGB_NSR steps keeps its
+// whole P operand in LDS, loaded once per workgroup, and only Q (plus gather indices)
+// passes through the ring; a q tile then stages a third of the bytes.  (A ring as deep
+// as the rest of LDS allows, up to 11 stages, measured slower than four.)
+constexpr int WGB_NSR = 7;
+constexpr int WGB_QSTAGE = WGB_PB + WGB_IDX;
+template <int PW> constexpr int wgb_res_lds() { return PW == 2 ? WGB_NSR * PW * WGB_PB + wgb_s<PW>() * WGB_QSTAGE : 0; }
+template <int PW> constexpr int wgb_lds_all() { return wgb_lds<PW>() > wgb_res_lds<PW>() ? wgb_lds<PW>() : wgb_res_lds<PW>(); }
 
 // slot permutation of a staged row's 16 chunks (an even XOR keeps chunk pairs together)
 __device__ __forceinline__ int wgb_h(int k) { return 2 * ((k & 3) | (((k >> 3) & 1) << 2)); }
@@ -522,7 +530,6 @@ template <int PASS, int PW>
 __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArgs a, int64_t nlead, int64_t ntiles) {
     extern __shared__ __align__(1024) char wsm[];
     constexpr int STAGE = wgb_stage<PW>(), QB = PW * WGB_PB;   // Q rows follow the PW halves of P
-    constexpr int WGB_S = wgb_s<PW>();
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const bool producer = wid >= 4 * PW;
     const int wp = (wid >> 1) & (2 * PW - 1), wq = wid & 1;
@@ -542,6 +549,12 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
     const int M = (int)(Pr.offsets ? (int64_t)Pr.offsets[e + 1] - rb : Pr.rows_fixed);
     const int nsteps = (M + WG_R - 1) / WG_R;
     const int total = nq * nsteps;
+    // LDS: P-resident, [P of steps 0 .. nsteps-1, PW halves each] then S stages of
+    // [Q | gather indices]; otherwise S stages of [P halves | Q | gather indices]
+    const bool res = PW == 2 && nsteps <= WGB_NSR;
+    constexpr int ring_s = wgb_s<PW>();                 // ring stages
+    const int qa0 = res ? WGB_NSR * PW * WGB_PB : QB;   // Q of stage 0
+    const int qss = res ? WGB_QSTAGE : STAGE;           // Q stage stride
 
     if (producer) {
         if (total == 0) return;
@@ -563,11 +576,12 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
             plast[m] = Pp + (prb + M - 1) * P_ld + p0 + cofs[m];   // rows past the expert repeat its last
             qlast[m] = Qp + (qrb + M - 1) * Q_ld + cofs[m];
         }
-        auto nops = [&](int y) { return 4 * (PW + 1) + ((k == 0 && gather && y + WGB_S - 1 < total) ? 1 : 0); };
+        auto nops = [&](int y) { return 4 * (res ? 1 : PW + 1) + ((k == 0 && gather && y + ring_s - 1 < total) ? 1 : 0); };
         int yq = 0, ys = 0;   // q tile and step of the next step to issue
         // step y into ring slot y % S; qrow: gathered Q rows of this lane's 4 rows (if gather)
         auto issue = [&](int y, const int (&qrow)[4]) {
-            char *slot = wsm + (y % WGB_S) * STAGE;
+            char *slot = wsm + (y % ring_s) * STAGE;
+            char *qslot = wsm + qa0 + (y % ring_s) * qss;
             const int q0 = (qt0 + yq) * WG_T, r0 = ys * WG_R;
             const bool ragged = r0 + WG_R > M;
             const int64_t po = (int64_t)r0 * P_ld, qo = (int64_t)r0 * Q_ld + q0;
@@ -575,23 +589,40 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
             for (int m = 0; m < 4; ++m) {
                 const int n = 2 * m + k;
                 const bool past = ragged && r0 + 4 * n + drow >= M;
+                if (!res)
 #pragma unroll
-                for (int h = 0; h < PW; ++h)
-                    dma16((past ? plast[m] : pbase[m] + po) + h * WG_T, slot + h * WGB_PB + n * 1024);
+                    for (int h = 0; h < PW; ++h)
+                        dma16((past ? plast[m] : pbase[m] + po) + h * WG_T, slot + h * WGB_PB + n * 1024);
                 const uint16_t *qs;
                 if (gather) qs = Qp + (int64_t)qrow[m] * Q_ld + q0 + cofs[m];
                 else qs = past ? qlast[m] + q0 : qbase[m] + qo;
-                dma16(qs, slot + QB + n * 1024);
+                dma16(qs, qslot + n * 1024);
             }
-            if (k == 0 && gather && y + WGB_S - 1 < total) {
+            if (k == 0 && gather && y + ring_s - 1 < total) {
                 // row indices of step y + S - 1 ride along (64 words, the first 32 used)
-                const int ys2 = (ys + WGB_S - 1) % nsteps;
-                dma4(qgb + min(ys2 * WG_R + (lane & 31), M - 1), slot + QB + WGB_PB);
+                const int ys2 = (ys + ring_s - 1) % nsteps;
+                dma4(qgb + min(ys2 * WG_R + (lane & 31), M - 1), qslot + WGB_PB);
             }
             if (++ys == nsteps) { ys = 0; ++yq; }
         };
+        if (res) {
+            // the expert's whole P operand, ahead of every Q step (older in the memory counter)
+            for (int st = 0; st < nsteps; ++st) {
+                const int r0 = st * WG_R;
+                const bool ragged = r0 + WG_R > M;
+                const int64_t po = (int64_t)r0 * P_ld;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int n = 2 * m + k;
+                    const bool past = ragged && r0 + 4 * n + drow >= M;
+#pragma unroll
+                    for (int h = 0; h < PW; ++h)
+                        dma16((past ? plast[m] : pbase[m] + po) + h * WG_T, wsm + (st * PW + h) * WGB_PB + n * 1024);
+                }
+            }
+        }
         int qrow[4] = {0, 0, 0, 0};
-        for (int y = 0; y < WGB_S - 1 && y < total; ++y) {
+        for (int y = 0; y < ring_s - 1 && y < total; ++y) {
             if (gather)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) qrow[m] = qgb[min(ys * WG_R + 4 * (2 * m + k) + drow, M - 1)];
@@ -600,13 +631,13 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
         for (int x = 0; x < total; ++x) {
             // step x has landed once at most the later steps' loads are outstanding
             int after = 0;
-            for (int y = x + 1; y <= min(x + WGB_S - 2, total - 1); ++y) after += nops(y);
+            for (int y = x + 1; y <= min(x + ring_s - 2, total - 1); ++y) after += nops(y);
             wait_vmcnt_dyn(after);
             cta_barrier();                       // step x landed; every MFMA wave is done with slot (x - 1) % S
-            const int y = x + WGB_S - 1;
+            const int y = x + ring_s - 1;
             if (y < total) {
                 if (gather) {
-                    const uint32_t ib = (uint32_t)(uintptr_t)(wsm + (x % WGB_S) * STAGE + QB + WGB_PB);
+                    const uint32_t ib = (uint32_t)(uintptr_t)(wsm + qa0 + (x % ring_s) * qss + WGB_PB);
                     uint32_t v[4];
                     lds_u32_x4(v, ib + 4 * (4 * k + drow), ib + 4 * (4 * (2 + k) + drow), ib + 4 * (4 * (4 + k) + drow),
                                ib + 4 * (4 * (6 + k) + drow));
@@ -657,7 +688,7 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
         const int col0 = f < 4 ? wq * 64 + f * 16 : (wp & 1) * 64 + (f - 4) * 16;
         const int c = (col0 + 4 * aa) >> 3, off = 8 * (aa & 1);
         const int k0 = 8 * g + jj, k1 = k0 + 4;
-        const int base = f < 4 ? QB : (wp >> 1) * WGB_PB;
+        const int base = f < 4 ? 0 : (wp >> 1) * WGB_PB;
         ofs[2 * f] = base + k0 * 256 + ((c ^ wgb_h(k0)) << 4) + off;
         ofs[2 * f + 1] = base + k1 * 256 + ((c ^ wgb_h(k1)) << 4) + off;
     }
@@ -665,10 +696,11 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
     int qt = 0, st = 0, slot = 0;
     for (int x = 0; x < total; ++x) {
         cta_barrier();                           // step x has landed
-        const char *sb = wsm + slot * STAGE;
+        const char *qsb = wsm + qa0 + slot * qss;
+        const char *psb = res ? wsm + st * (PW * WGB_PB) : wsm + slot * STAGE;
         wgb_v4s r[16];
 #pragma unroll
-        for (int f = 0; f < 16; ++f) r[f] = lds_tr16(sb + ofs[f]);
+        for (int f = 0; f < 16; ++f) r[f] = lds_tr16((f < 8 ? qsb : psb) + ofs[f]);
         bf16x8 qa[4], pb[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
@@ -690,7 +722,7 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], pb[j], acc[i][j], 0, 0, 0);
-        slot = slot + 1 == WGB_S ? 0 : slot + 1;
+        slot = slot + 1 == ring_s ? 0 : slot + 1;
         if (++st == nsteps) {
             store_tile((qt0 + qt) * WG_T);
 #pragma unroll
@@ -1159,17 +1191,17 @@ hipError_t launch_wgrad(int dt, int pass, const WgradArgs &args, hipStream_t s) 
         std::call_once(once, [] {
             const void *k[4] = {(const void *)wgrad_bf16_kernel<0, 1>, (const void *)wgrad_bf16_kernel<1, 1>,
                                 (const void *)wgrad_bf16_kernel<0, 2>, (const void *)wgrad_bf16_kernel<1, 2>};
-            const int lds[4] = {wgb_lds<1>(), wgb_lds<1>(), wgb_lds<2>(), wgb_lds<2>()};
+            const int lds[4] = {wgb_lds_all<1>(), wgb_lds_all<1>(), wgb_lds_all<2>(), wgb_lds_all<2>()};
             for (int i = 0; i < 4 && attr == hipSuccess; ++i)
                 attr = hipFuncSetAttribute(k[i], hipFuncAttributeMaxDynamicSharedMemorySize, lds[i]);
         });
         if (attr != hipSuccess) return attr;
         if (wide) {
-            if (pass) wgrad_bf16_kernel<1, 2><<<(unsigned)grid, wgb_nt<2>(), wgb_lds<2>(), s>>>(a, nlead, tiles);
-            else wgrad_bf16_kernel<0, 2><<<(unsigned)grid, wgb_nt<2>(), wgb_lds<2>(), s>>>(a, nlead, tiles);
+            if (pass) wgrad_bf16_kernel<1, 2><<<(unsigned)grid, wgb_nt<2>(), wgb_lds_all<2>(), s>>>(a, nlead, tiles);
+            else wgrad_bf16_kernel<0, 2><<<(unsigned)grid, wgb_nt<2>(), wgb_lds_all<2>(), s>>>(a, nlead, tiles);
         } else {
-            if (pass) wgrad_bf16_kernel<1, 1><<<(unsigned)grid, wgb_nt<1>(), wgb_lds<1>(), s>>>(a, nlead, tiles);
-            else wgrad_bf16_kernel<0, 1><<<(unsigned)grid, wgb_nt<1>(), wgb_lds<1>(), s>>>(a, nlead, tiles);
+            if (pass) wgrad_bf16_kernel<1, 1><<<(unsigned)grid, wgb_nt<1>(), wgb_lds_all<1>(), s>>>(a, nlead, tiles);
+            else wgrad_bf16_kernel<0, 1><<<(unsigned)grid, wgb_nt<1>(), wgb_lds_all<1>(), s>>>(a, nlead, tiles);
         }
     }
     return hipGetLastError();
