@@ -693,6 +693,36 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
         ofs[2 * f + 1] = base + k1 * 256 + ((c ^ wgb_h(k1)) << 4) + off;
     }
     const int vlast = M - (nsteps - 1) * WG_R;   // valid rows of an expert's last step
+    // A q tile's results leave during the next q tile's steps, two 16-byte stores per
+    // lane per step (packed to bf16 when the tile ends), instead of as one burst that
+    // the ring's next loads queue behind: pv holds them, pn counts those already out.
+    u32x4 pv[8];
+    int pq0 = 0, pn = 8;
+    auto pack_tile = [&](int q0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < 4; i += 2) {
+                const float ya[4] = {acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]};
+                const float yb[4] = {acc[i + 1][j][0], acc[i + 1][j][1], acc[i + 1][j][2], acc[i + 1][j][3]};
+                pv[j * 2 + i / 2] = pair_bf16_value(ya, yb, lane);
+            }
+        pq0 = q0;
+        pn = 0;
+    };
+    auto store_one = [&](int n) {
+        const int j = n >> 1, i = (n & 1) * 2;
+        const int prow = prow0 + wp * 64 + j * 16 + (lane & 15);
+        uint16_t *orow = out + ((int64_t)e * split_rows + prow) * Qdim;
+        const int f = pair_bf16_col(pq0 + wq * 64 + i * 16, lane);
+        if (f < Qdim) *(u32x4 *)(orow + f) = pv[n];
+    };
+    auto store_some = [&](int upto) {
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+            if (n >= pn && n < upto) store_one(n);
+        pn = upto > pn ? upto : pn;
+    };
     int qt = 0, st = 0, slot = 0;
     for (int x = 0; x < total; ++x) {
         cta_barrier();                           // step x has landed
@@ -723,8 +753,10 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
             for (int j = 0; j < 4; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[i], pb[j], acc[i][j], 0, 0, 0);
         slot = slot + 1 == ring_s ? 0 : slot + 1;
+        if (pn < 8) store_some(pn + 2 < 8 ? pn + 2 : 8);
         if (++st == nsteps) {
-            store_tile((qt0 + qt) * WG_T);
+            store_some(8);
+            pack_tile((qt0 + qt) * WG_T);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -733,6 +765,7 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
             ++qt;
         }
     }
+    store_some(8);
 }
 
 // ---- FP8 backward helpers ------------------------------------------------------

@@ -40,14 +40,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // same for block i+1.  A token's 32 features then leave as two 32-byte runs
 // instead of four 16-byte ones.  Both partners hold the same token, so they are
 // active together.
-__device__ __forceinline__ void store_pair_bf16(uint16_t *row, int f_block, const float a[4], const float b[4],
-                                                int lane, int F) {
+// pair_bf16_value / pair_bf16_col: the lane's 16 bytes and their first feature, for
+// callers that store them later.
+__device__ __forceinline__ u32x4 pair_bf16_value(const float a[4], const float b[4], int lane) {
     const bool odd = (lane >> 4) & 1;
     const uint32_t a01 = pack_bf16x2(a[0], a[1]), a23 = pack_bf16x2(a[2], a[3]);
     const uint32_t b01 = pack_bf16x2(b[0], b[1]), b23 = pack_bf16x2(b[2], b[3]);
     const uint32_t r0 = __shfl_xor(odd ? a01 : b01, 16, 64), r1 = __shfl_xor(odd ? a23 : b23, 16, 64);
-    const int f = f_block + (odd ? 16 : 0) + 4 * ((lane >> 4) & ~1);
-    if (f < F) *(u32x4 *)(row + f) = odd ? u32x4{r0, r1, b01, b23} : u32x4{a01, a23, r0, r1};
+    return odd ? u32x4{r0, r1, b01, b23} : u32x4{a01, a23, r0, r1};
+}
+__device__ __forceinline__ int pair_bf16_col(int f_block, int lane) {
+    return f_block + (((lane >> 4) & 1) ? 16 : 0) + 4 * ((lane >> 4) & ~1);
+}
+__device__ __forceinline__ void store_pair_bf16(uint16_t *row, int f_block, const float a[4], const float b[4],
+                                                int lane, int F) {
+    const u32x4 v = pair_bf16_value(a, b, lane);
+    const int f = pair_bf16_col(f_block, lane);
+    if (f < F) *(u32x4 *)(row + f) = v;
 }
 
 // Four fp32 values (already in [-448, 448]) -> four E4M3FN codes, nearest even.
