@@ -486,8 +486,13 @@ __global__ __launch_bounds__(BW_NT) void wgrad_kernel(const WgradArgs a, int64_t
 // PW = 2: the p tile is 256 wide (two 128-value halves staged side by side, eight MFMA
 // waves), which cuts the operand rows each output value costs by a quarter; it is used
 // when every p dimension and split of the launch is a multiple of 256.
-// ring stages (five for the 256-wide tile measured slower than four)
-template <int PW> constexpr int wgb_s() { return 4; }
+// Ring stages, and steps consumed per barrier (the rest of the ring is in flight): the
+// 256-wide tile takes two 32-row steps per barrier from six stages, or four from eight
+// when its P is resident and short enough; the 128-wide one a step per barrier from four.
+// Each barrier costs about as much as a step's loads and products, so fewer is faster.
+template <int PW> constexpr int wgb_s() { return PW == 2 ? 6 : 4; }
+template <int PW> constexpr int wgb_sb() { return PW == 2 ? 2 : 1; }
+constexpr int WGB_S4 = 8, WGB_SB4 = 4, WGB_NS4 = 5;   // eight stages, four per barrier: P of <= 5 steps
 constexpr int WGB_PB = WG_R * WG_T * 2;                   // one operand half's rows of a step (8 KB)
 constexpr int WGB_IDX = 256;                              // gather indices of a later step
 template <int PW> constexpr int wgb_stage() { return (PW + 1) * WGB_PB + WGB_IDX; }
@@ -495,11 +500,12 @@ template <int PW> constexpr int wgb_lds() { return wgb_s<PW>() * wgb_stage<PW>()
 template <int PW> constexpr int wgb_nt() { return 64 * (4 * PW + 2); }
 // P-resident tiles (256-wide p tile only): an expert of at most WGB_NSR steps keeps its
 // whole P operand in LDS, loaded once per workgroup, and only Q (plus gather indices)
-// passes through the ring; a q tile then stages a third of the bytes.  (A ring as deep
-// as the rest of LDS allows, up to 11 stages, measured slower than four.)
-constexpr int WGB_NSR = 7;
+// passes through the ring; a q tile then stages a third of the bytes.
+constexpr int WGB_NSR = 6;
 constexpr int WGB_QSTAGE = WGB_PB + WGB_IDX;
-template <int PW> constexpr int wgb_res_lds() { return PW == 2 ? WGB_NSR * PW * WGB_PB + wgb_s<PW>() * WGB_QSTAGE : 0; }
+template <int PW> constexpr int wgb_res_lds() {
+    return PW == 2 ? max(WGB_NSR * PW * WGB_PB + wgb_s<PW>() * WGB_QSTAGE, WGB_NS4 * PW * WGB_PB + WGB_S4 * WGB_QSTAGE) : 0;
+}
 template <int PW> constexpr int wgb_lds_all() { return wgb_lds<PW>() > wgb_res_lds<PW>() ? wgb_lds<PW>() : wgb_res_lds<PW>(); }
 
 // slot permutation of a staged row's 16 chunks (an even XOR keeps chunk pairs together)
@@ -552,8 +558,10 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
     // LDS: P-resident, [P of steps 0 .. nsteps-1, PW halves each] then S stages of
     // [Q | gather indices]; otherwise S stages of [P halves | Q | gather indices]
     const bool res = PW == 2 && nsteps <= WGB_NSR;
-    constexpr int ring_s = wgb_s<PW>();                 // ring stages
-    const int qa0 = res ? WGB_NSR * PW * WGB_PB : QB;   // Q of stage 0
+    const bool four = res && nsteps <= WGB_NS4;
+    const int ring_s = four ? WGB_S4 : wgb_s<PW>(), SB = four ? WGB_SB4 : wgb_sb<PW>();   // stages, steps per barrier
+    const int D = ring_s - SB;                                   // steps in flight past the ones consumed
+    const int qa0 = res ? nsteps * PW * WGB_PB : QB;   // Q of stage 0
     const int qss = res ? WGB_QSTAGE : STAGE;           // Q stage stride
 
     if (producer) {
@@ -576,7 +584,7 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
             plast[m] = Pp + (prb + M - 1) * P_ld + p0 + cofs[m];   // rows past the expert repeat its last
             qlast[m] = Qp + (qrb + M - 1) * Q_ld + cofs[m];
         }
-        auto nops = [&](int y) { return 4 * (res ? 1 : PW + 1) + ((k == 0 && gather && y + ring_s - 1 < total) ? 1 : 0); };
+        auto nops = [&](int y) { return 4 * (res ? 1 : PW + 1) + ((k == 0 && gather && y + D < total) ? 1 : 0); };
         int yq = 0, ys = 0;   // q tile and step of the next step to issue
         // step y into ring slot y % S; qrow: gathered Q rows of this lane's 4 rows (if gather)
         auto issue = [&](int y, const int (&qrow)[4]) {
@@ -598,9 +606,9 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
                 else qs = past ? qlast[m] + q0 : qbase[m] + qo;
                 dma16(qs, qslot + n * 1024);
             }
-            if (k == 0 && gather && y + ring_s - 1 < total) {
-                // row indices of step y + S - 1 ride along (64 words, the first 32 used)
-                const int ys2 = (ys + ring_s - 1) % nsteps;
+            if (k == 0 && gather && y + D < total) {
+                // row indices of step y + D ride along (64 words, the first 32 used)
+                const int ys2 = (ys + D) % nsteps;
                 dma4(qgb + min(ys2 * WG_R + (lane & 31), M - 1), qslot + WGB_PB);
             }
             if (++ys == nsteps) { ys = 0; ++yq; }
@@ -622,29 +630,31 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
             }
         }
         int qrow[4] = {0, 0, 0, 0};
-        for (int y = 0; y < ring_s - 1 && y < total; ++y) {
+        for (int y = 0; y < D && y < total; ++y) {
             if (gather)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) qrow[m] = qgb[min(ys * WG_R + 4 * (2 * m + k) + drow, M - 1)];
             issue(y, qrow);
         }
-        for (int x = 0; x < total; ++x) {
-            // step x has landed once at most the later steps' loads are outstanding
+        for (int x = 0; x < total; x += SB) {
+            // steps x .. x+SB-1 have landed once at most the later steps' loads are outstanding
             int after = 0;
-            for (int y = x + 1; y <= min(x + ring_s - 2, total - 1); ++y) after += nops(y);
+            for (int y = x + SB; y <= min(x + D - 1, total - 1); ++y) after += nops(y);
             wait_vmcnt_dyn(after);
-            cta_barrier();                       // step x landed; every MFMA wave is done with slot (x - 1) % S
-            const int y = x + ring_s - 1;
-            if (y < total) {
-                if (gather) {
-                    const uint32_t ib = (uint32_t)(uintptr_t)(wsm + qa0 + (x % ring_s) * qss + WGB_PB);
-                    uint32_t v[4];
-                    lds_u32_x4(v, ib + 4 * (4 * k + drow), ib + 4 * (4 * (2 + k) + drow), ib + 4 * (4 * (4 + k) + drow),
-                               ib + 4 * (4 * (6 + k) + drow));
+            cta_barrier();   // steps x .. x+SB-1 landed; every MFMA wave is done with the slots of x-SB .. x-1
+            for (int j = 0; j < SB; ++j) {
+                const int y = x + D + j;   // into the slot of step x - SB + j
+                if (y < total) {
+                    if (gather) {
+                        const uint32_t ib = (uint32_t)(uintptr_t)(wsm + qa0 + ((x + j) % ring_s) * qss + WGB_PB);
+                        uint32_t v[4];
+                        lds_u32_x4(v, ib + 4 * (4 * k + drow), ib + 4 * (4 * (2 + k) + drow),
+                                   ib + 4 * (4 * (4 + k) + drow), ib + 4 * (4 * (6 + k) + drow));
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) qrow[m] = (int)v[m];
+                        for (int m = 0; m < 4; ++m) qrow[m] = (int)v[m];
+                    }
+                    issue(y, qrow);
                 }
-                issue(y, qrow);
             }
         }
         return;
@@ -723,9 +733,10 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
             if (n >= pn && n < upto) store_one(n);
         pn = upto > pn ? upto : pn;
     };
-    int qt = 0, st = 0, slot = 0;
+    int qt = 0, st = 0, slot = 0, sbn = 0;
     for (int x = 0; x < total; ++x) {
-        cta_barrier();                           // step x has landed
+        if (sbn == 0) cta_barrier();             // steps x .. x+SB-1 have landed
+        sbn = sbn + 1 == SB ? 0 : sbn + 1;
         const char *qsb = wsm + qa0 + slot * qss;
         const char *psb = res ? wsm + st * (PW * WGB_PB) : wsm + slot * STAGE;
         wgb_v4s r[16];

@@ -156,6 +156,7 @@ def run_case(moe, orc, cfg, seed, flags=0, bias=None, skip=(), rs=1.0):
     ("bf16", 129, 384, 32, 8, 3, 6, 2, 128, 1, 1.0),        # ragged tail, odd group count
     ("bf16", 300, 256, 64, 8, 4, 8, 0, 256, 0, 2.5),        # no shared expert
     ("bf16", 900, 256, 16, 4, 2, 4, 1, 256, 0, 1.0),        # about 225 rows per expert: 6 to 8 steps of 32
+    ("bf16", 640, 384, 16, 4, 2, 2, 1, 256, 0, 1.0),        # three q tiles x 2-4 steps: odd step counts per tile
     ("fp8", 256, 256, 16, 4, 2, 2, 1, 256, 0, 1.0),
     ("fp8", 1, 256, 16, 4, 2, 2, 1, 128, 0, 1.0),           # one token: one-row 128 x 1 runs
     ("fp8", 700, 512, 32, 4, 2, 4, 1, 256, 0, 2.5),         # several runs per expert, ragged last runs
