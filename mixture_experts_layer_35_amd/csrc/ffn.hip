@@ -315,9 +315,14 @@ __host__ __device__ constexpr int red_bytes() {
 }
 
 
-template <int DT, int MODE>
+template <int DT, int MODE, bool WS>
 __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_bytes) {
     constexpr bool GATEUP = MODE == FFN_GATEUP || MODE == FFN_GATEUP_SAVE || MODE == FFN_GATEUP_BWD;   // two weight matrices
+    // Weight rows that one tile alone reads load with the nontemporal policy, so that L2
+    // keeps the token rows the expert's other weight-block tiles read again: always in
+    // gate/up, and in the down projection when no expert has more than one row block
+    // (WS; otherwise the row blocks of a hot expert share its weight rows through L2).
+    constexpr bool WSTREAM = GATEUP || WS;
     constexpr bool SAVEAB = MODE == FFN_GATEUP_SAVE;    // epilogue also stores the SwiGLU inputs to P.ab
     constexpr bool SWBWD = MODE == FFN_GATEUP_BWD;      // epilogue: SwiGLU gradient from dH
     constexpr int esz = FTraits<DT>::esz;
@@ -536,7 +541,8 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                 const bool up = GATEUP && q >= QW / 2;
                 const int qq = min(GATEUP ? (up ? q - QW / 2 : q) : q, T.qmax);
                 const char *src = (up ? T.wbase1 : T.wbase0) + (int64_t)qq * (RPI * NP) * rb + (int64_t)ks * CB;
-                dma16(src, st + (q * NP + wid) * 1024);
+                if (WSTREAM) dma16_stream(src, st + (q * NP + wid) * 1024);
+                else dma16(src, st + (q * NP + wid) * 1024);
             } else {
                 const int qx = q - QW;
                 const int ins = qx * NP + uwid;
@@ -554,7 +560,8 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
             const bool up = GATEUP && q >= QW / 2;
             const int qq = min(GATEUP ? (up ? q - QW / 2 : q) : q, T.qmax);
             const int soff = qq * (RPI * NP) * (int)rowbytes + ks * CB;
-            buffer_dma16(up ? T.rw1 : T.rw0, woff, soff, st + (q * NP + uwid) * 1024);
+            if (WSTREAM) buffer_dma16_stream(up ? T.rw1 : T.rw0, woff, soff, st + (q * NP + uwid) * 1024);
+            else buffer_dma16(up ? T.rw1 : T.rw0, woff, soff, st + (q * NP + uwid) * 1024);
         } else {
             const int qx = q - QW;
             const int ins = qx * NP + uwid;
@@ -893,11 +900,19 @@ __global__ void zero_queues_kernel(int *ctr) {
 template <int DT, int MODE>
 hipError_t run(const FfnArgs &a, hipStream_t s) {
     if (!a.ctr) return hipErrorInvalidValue;
+    // bf16 down projection in which no expert can have more than one row block (every
+    // problem bounds its experts' rows by BM): its weight rows are read by one tile each
+    constexpr bool WS_OK = DT == DT_BF16 && MODE == FFN_DOWN;
+    bool ws = WS_OK;
+    for (int i = 0; i < a.nprob; ++i) ws = ws && a.p[i].rows_max > 0 && a.p[i].rows_max <= BM;
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(once, [&] {
-        attr_err = hipFuncSetAttribute((const void *)ffn_kernel<DT, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       LDS_TOTAL);
+        attr_err = hipFuncSetAttribute((const void *)ffn_kernel<DT, MODE, false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
+        if (WS_OK && attr_err == hipSuccess)
+            attr_err = hipFuncSetAttribute((const void *)ffn_kernel<DT, MODE, WS_OK>,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
     });
     if (attr_err != hipSuccess) return attr_err;
     const int pb = prefix_bytes(a.p[0].n_exp, a.nprob > 1 ? a.p[1].n_exp : 0);
@@ -908,7 +923,8 @@ hipError_t run(const FfnArgs &a, hipStream_t s) {
     int grid = device_cus();
     grid = (grid + 7) / 8 * 8;
     zero_queues_kernel<<<1, 64, 0, s>>>(a.ctr);
-    ffn_kernel<DT, MODE><<<grid, NT, LDS_TOTAL, s>>>(a, ring);
+    if (WS_OK && ws) ffn_kernel<DT, MODE, WS_OK><<<grid, NT, LDS_TOTAL, s>>>(a, ring);
+    else ffn_kernel<DT, MODE, false><<<grid, NT, LDS_TOTAL, s>>>(a, ring);
     return hipGetLastError();
 }
 

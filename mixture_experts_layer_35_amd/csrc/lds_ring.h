@@ -144,5 +144,15 @@ __device__ __forceinline__ void buffer_dma4(__amdgpu_buffer_rsrc_t r, uint32_t v
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)l, 4, (int)voff, soff, 0, 0);
 }
 
+// 16-byte loads with the nontemporal cache policy (the `nt` bit): lines they bring
+// into L2 are the first to go, which leaves L2 to operands that other workgroups
+// read again.  For data one workgroup reads once.
+__device__ __forceinline__ void dma16_stream(const void *g, void *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void *)l, 16, 0, 2);
+}
+__device__ __forceinline__ void buffer_dma16_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff, void *l) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)l, 16, (int)voff, soff, 0, 2);
+}
+
 }  // namespace
 }  // namespace moe

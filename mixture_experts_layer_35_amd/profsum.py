@@ -30,7 +30,7 @@ COPY_BYTES = 1 << 30
 def short_name(full: str) -> str:
     """Readable kernel name: the expert kernels by their projection, others
     by their function name."""
-    m = re.search(r"ffn_kernel<(\d+), (\d+)>", full)
+    m = re.search(r"ffn_kernel<(\d+), (\d+)(?:, (?:true|false))?>", full)
     if m:
         return {0: "ffn_down", 1: "ffn_gate_up", 2: "bwd_swiglu", 3: "bwd_dh", 4: "bwd_dx",
                 5: "ffn_gate_up"}[int(m.group(2))]

@@ -11,8 +11,9 @@ import moe_synth as syn
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-FFN_UP = "void moe::(anonymous namespace)::ffn_kernel<1, 1>(moe::FfnArgs, int)"
-FFN_DOWN = "void moe::(anonymous namespace)::ffn_kernel<2, 0>(moe::FfnArgs, int)"
+FFN_UP = "void moe::(anonymous namespace)::ffn_kernel<1, 1, false>(moe::FfnArgs, int)"
+FFN_DOWN = "void moe::(anonymous namespace)::ffn_kernel<2, 0, false>(moe::FfnArgs, int)"
+FFN_DOWN_WS = "void moe::(anonymous namespace)::ffn_kernel<1, 0, true>(moe::FfnArgs, int)"
 WG_BF16 = "void moe::(anonymous namespace)::wgrad_bf16_kernel<1, 2>(moe::WgradArgs, long, long)"
 WG_F32 = "void moe::(anonymous namespace)::wgrad_kernel<0, 0>(moe::WgradArgs, long, long)"
 COPY = "__amd_rocclr_copyBuffer"
@@ -39,6 +40,8 @@ def _write_counters(path, rows):
 def test_short_names():
     assert profsum.short_name(FFN_UP) == "ffn_gate_up"
     assert profsum.short_name(FFN_DOWN) == "ffn_down"
+    assert profsum.short_name(FFN_DOWN_WS) == "ffn_down"
+    assert profsum.short_name("void moe::(anonymous namespace)::ffn_kernel<1, 3>(moe::FfnArgs, int)") == "bwd_dh"
     assert profsum.short_name(WG_BF16) == "wgrad_gate_up"
     assert profsum.short_name(WG_F32) == "wgrad_down"
     assert profsum.short_name(COPY) == "copy_buffer"
