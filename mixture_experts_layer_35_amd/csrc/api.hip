@@ -507,7 +507,6 @@ int forward_impl(const char *fn, const moe_shape *s, const void *u, const void *
     dn[0].w0 = routed_w[2];
     dn[0].s0 = fp8 ? routed_s[2] : nullptr;
     dn[0].out = W + L.yperm;
-    dn[0].rows_max = T;   // a token selects an expert at most once
     int nprob = 1;
     if (s->n_shared > 0) {
         nprob = 2;
@@ -528,7 +527,6 @@ int forward_impl(const char *fn, const moe_shape *s, const void *u, const void *
         dn[1].w0 = shared_w[2];
         dn[1].s0 = fp8 ? shared_s[2] : nullptr;
         dn[1].out = W + L.ysh;
-        dn[1].rows_max = T;
     }
     if (s->flags & MOE_SAVE_SWIGLU_INPUTS) {
         gu[0].ab = (float *)(W + L.ab);

@@ -315,14 +315,16 @@ __host__ __device__ constexpr int red_bytes() {
 }
 
 
-template <int DT, int MODE, bool WS>
+template <int DT, int MODE>
 __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_bytes) {
     constexpr bool GATEUP = MODE == FFN_GATEUP || MODE == FFN_GATEUP_SAVE || MODE == FFN_GATEUP_BWD;   // two weight matrices
     // Weight rows that one tile alone reads load with the nontemporal policy, so that L2
     // keeps the token rows the expert's other weight-block tiles read again: always in
-    // gate/up, and in the down projection when no expert has more than one row block
-    // (WS; otherwise the row blocks of a hot expert share its weight rows through L2).
-    constexpr bool WSTREAM = GATEUP || WS;
+    // gate/up, and in the other products for the tiles of experts with one row block
+    // (the row blocks of a hot expert share its weight rows through L2).  A tile's
+    // reduction loop is instantiated per policy (bf16 only: the e4m3 and fp32 kernels
+    // spilled with two).
+    constexpr bool WS_TILE = !GATEUP && DT == DT_BF16;
     constexpr bool SAVEAB = MODE == FFN_GATEUP_SAVE;    // epilogue also stores the SwiGLU inputs to P.ab
     constexpr bool SWBWD = MODE == FFN_GATEUP_BWD;      // epilogue: SwiGLU gradient from dH
     constexpr int esz = FTraits<DT>::esz;
@@ -461,6 +463,8 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
 #pragma unroll
             for (int q = 0; q < QX; ++q) T.nx += RPI * (q * NP + wid) < trows ? 1 : 0;
         }
+        // the tile's expert has one row block: its reduction loop streams the weight rows
+        if (WS_TILE && mt == 1) T.ntb += 16;
         // weight rows: instruction q < QW of this producer covers row RPI*(q*NP+wid) + csub
         // of the tile; in a ragged last tile (F - n0 < WR) the instructions past F re-read
         // the last full instruction's rows
@@ -528,8 +532,9 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
     };
     // Load q of one step by this producer: q < QW are weight instructions, the
     // rest token instructions (NTB of them cover 32*NTB token rows).
-    auto dma_one = [&](const Tile &T, int q, int ks, char *st, auto farc) {
+    auto dma_one = [&](const Tile &T, int q, int ks, char *st, auto farc, auto wsc) {
         constexpr bool FAR = decltype(farc)::value;
+        constexpr bool WSTREAM = decltype(wsc)::value;
         if (!BUFDMA) {
             // a wave-uniform base plus the step's offset (scalar), plus the lane's fixed
             // 32-bit offset: one 64-bit vector add per load
@@ -586,8 +591,8 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
 #pragma unroll
             for (int q = 0; q < QW + QX; ++q)
                 if (q < ndma) {
-                    if (!BUFDMA && T.xfar) dma_one(T, q, ks, st, std::true_type{});
-                    else dma_one(T, q, ks, st, std::false_type{});
+                    if (!BUFDMA && T.xfar) dma_one(T, q, ks, st, std::true_type{}, std::integral_constant<bool, GATEUP>{});
+                    else dma_one(T, q, ks, st, std::false_type{}, std::integral_constant<bool, GATEUP>{});
                 }
         }
     };
@@ -628,7 +633,7 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
         // stores are younger than them in this wave's memory counter: waiting
         // for at most (S-2) steps outstanding covers them conservatively.
         const int S = cur.S, stage_bytes = cur.stage_bytes, srows = cur.srows;
-        auto kloop = [&](auto ntb, auto spread, auto farc) {
+        auto kloop = [&](auto ntb, auto spread, auto farc, auto wsc) {
             constexpr int NTB = decltype(ntb)::value;
             constexpr bool SPREAD = decltype(spread)::value;
             constexpr int NDMA = QW + NTB * 16 * WM / RPI / NP;   // loads per producer per step, at most
@@ -652,13 +657,13 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                         // a deeper ring has room to load ahead: issue the whole step first
 #pragma unroll
                         for (int q = 0; q < NDMA; ++q)
-                            if (q < QW + cur.nx) dma_one(cur, q, ks, dst, farc);
+                            if (q < QW + cur.nx) dma_one(cur, q, ks, dst, farc, wsc);
                         compute_step<DT, GATEUP, NTB, false, NDMA>(st, sc, acc, wm, wf, lane, [](int) {});
                     } else {
                         // double buffering: spread the loads over the products so this
                         // wave's share of the products is not held up behind them
                         compute_step<DT, GATEUP, NTB, true, NDMA>(st, sc, acc, wm, wf, lane,
-                                                                  [&](int q) { dma_one(cur, q, ks, dst, farc); });
+                                                                  [&](int q) { dma_one(cur, q, ks, dst, farc, wsc); });
                     }
                 } else {
                     compute_step<DT, GATEUP, NTB, false, NDMA>(st, sc, acc, wm, wf, lane, [](int) {});
@@ -666,17 +671,25 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
                 slot = slot + 1 == S ? 0 : slot + 1;
             }
         };
-        auto kloop_s = [&](auto ntb) {
+        auto kloop_p = [&](auto ntb, auto wsc) {
             if (!BUFDMA && cur.xfar) {
                 // e4m3 tiles whose token rows span 4 GiB or more: 64-bit row addresses
-                if (cur.spread) kloop(ntb, std::true_type{}, std::true_type{});
-                else kloop(ntb, std::false_type{}, std::true_type{});
+                if (cur.spread) kloop(ntb, std::true_type{}, std::true_type{}, wsc);
+                else kloop(ntb, std::false_type{}, std::true_type{}, wsc);
             } else {
-                if (cur.spread) kloop(ntb, std::true_type{}, std::false_type{});
-                else kloop(ntb, std::false_type{}, std::false_type{});
+                if (cur.spread) kloop(ntb, std::true_type{}, std::false_type{}, wsc);
+                else kloop(ntb, std::false_type{}, std::false_type{}, wsc);
             }
         };
-        switch (cur.ntb) {
+        auto kloop_s = [&](auto ntb) {
+            if constexpr (WS_TILE) {
+                if (cur.ntb >= 16) kloop_p(ntb, std::true_type{});
+                else kloop_p(ntb, std::false_type{});
+            } else {
+                kloop_p(ntb, std::integral_constant<bool, GATEUP>{});
+            }
+        };
+        switch (cur.ntb & 15) {
             case 1: kloop_s(std::integral_constant<int, 1>{}); break;
             case 2: kloop_s(std::integral_constant<int, 2>{}); break;
             case 3: kloop_s(std::integral_constant<int, 3>{}); break;
@@ -900,19 +913,11 @@ __global__ void zero_queues_kernel(int *ctr) {
 template <int DT, int MODE>
 hipError_t run(const FfnArgs &a, hipStream_t s) {
     if (!a.ctr) return hipErrorInvalidValue;
-    // bf16 down projection in which no expert can have more than one row block (every
-    // problem bounds its experts' rows by BM): its weight rows are read by one tile each
-    constexpr bool WS_OK = DT == DT_BF16 && MODE == FFN_DOWN;
-    bool ws = WS_OK;
-    for (int i = 0; i < a.nprob; ++i) ws = ws && a.p[i].rows_max > 0 && a.p[i].rows_max <= BM;
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(once, [&] {
-        attr_err = hipFuncSetAttribute((const void *)ffn_kernel<DT, MODE, false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
-        if (WS_OK && attr_err == hipSuccess)
-            attr_err = hipFuncSetAttribute((const void *)ffn_kernel<DT, MODE, WS_OK>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
+        attr_err = hipFuncSetAttribute((const void *)ffn_kernel<DT, MODE>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       LDS_TOTAL);
     });
     if (attr_err != hipSuccess) return attr_err;
     const int pb = prefix_bytes(a.p[0].n_exp, a.nprob > 1 ? a.p[1].n_exp : 0);
@@ -923,8 +928,7 @@ hipError_t run(const FfnArgs &a, hipStream_t s) {
     int grid = device_cus();
     grid = (grid + 7) / 8 * 8;
     zero_queues_kernel<<<1, 64, 0, s>>>(a.ctr);
-    if (WS_OK && ws) ffn_kernel<DT, MODE, WS_OK><<<grid, NT, LDS_TOTAL, s>>>(a, ring);
-    else ffn_kernel<DT, MODE, false><<<grid, NT, LDS_TOTAL, s>>>(a, ring);
+    ffn_kernel<DT, MODE><<<grid, NT, LDS_TOTAL, s>>>(a, ring);
     return hipGetLastError();
 }
 

@@ -56,7 +56,6 @@ struct FfnProblem {
     int x_local;            // x row of local row r is r (shared experts over u)
     const int32_t *offsets; // [n_exp+1] device row offsets, or null: expert e owns rows [e*rows_fixed, +rows_fixed)
     int64_t rows_fixed;
-    int64_t rows_max;       // an upper bound on any expert's rows (0: none known)
     const int32_t *gather;  // x row of problem row R is gather[R] (null: R, or local r when x_local)
     const void *x;          // activations, rows of K elements
     const float *xs;        // E4M3: [rows][K/128] scales
