@@ -277,10 +277,16 @@ __global__ __launch_bounds__(RG_NT) void router_partial_kernel(const char *__res
         const char *p = row < RP_E ? gw + (int64_t)row * rowbytes : u + min(t0 + row - RP_E, T - 1) * rowbytes;
         src[q] = p + (int64_t)k0 * 128 + c * 16;
     }
+    // token rows are read by this workgroup alone: nontemporal, so that L2 keeps the
+    // centroid chunk that every token tile on the XCD reads
+    const int uw = __builtin_amdgcn_readfirstlane(wid);
     auto issue = [&](int k) {
         char *st = ring + (k % S) * STAGE;
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) dma16(src[q] + (int64_t)k * 128, st + (NQ * wid + q) * 1024);
+        for (int q = 0; q < NQ; ++q) {
+            if (8 * (NQ * uw + q) >= RP_E) dma16_stream(src[q] + (int64_t)k * 128, st + (NQ * wid + q) * 1024);
+            else dma16(src[q] + (int64_t)k * 128, st + (NQ * wid + q) * 1024);
+        }
     };
     f32x4 acc[Tl::EBW][Tl::TBW];
 #pragma unroll
