@@ -349,7 +349,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs the layer on a single GPU only (expert-parallel sharding across GPUs is "
+        print("bench.py: the layer runs on a single GPU only (expert-parallel sharding across GPUs is "
               "not built); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
