@@ -319,12 +319,12 @@ template <int DT, int MODE>
 __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_bytes) {
     constexpr bool GATEUP = MODE == FFN_GATEUP || MODE == FFN_GATEUP_SAVE || MODE == FFN_GATEUP_BWD;   // two weight matrices
     // Weight rows that one tile alone reads load with the nontemporal policy, so that L2
-    // keeps the token rows the expert's other weight-block tiles read again: always in
-    // gate/up, and in the other products for the tiles of experts with one row block
-    // (the row blocks of a hot expert share its weight rows through L2).  A tile's
-    // reduction loop is instantiated per policy (bf16 only: the e4m3 and fp32 kernels
-    // spilled with two).
-    constexpr bool WS_TILE = !GATEUP && DT == DT_BF16;
+    // keeps the token rows the expert's other weight-block tiles read again.  That is the
+    // case for the tiles of experts with one row block; the row blocks of a larger expert
+    // share its weight rows through L2.  In bf16 a tile's reduction loop is instantiated
+    // per policy; the e4m3 and fp32 kernels spilled with two, so they keep one policy per
+    // pass (nontemporal in gate/up, cached otherwise).
+    constexpr bool WS_TILE = DT == DT_BF16;
     constexpr bool SAVEAB = MODE == FFN_GATEUP_SAVE;    // epilogue also stores the SwiGLU inputs to P.ab
     constexpr bool SWBWD = MODE == FFN_GATEUP_BWD;      // epilogue: SwiGLU gradient from dH
     constexpr int esz = FTraits<DT>::esz;
