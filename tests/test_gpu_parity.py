@@ -233,6 +233,43 @@ def test_grouped_ffn(moe, orc, dtype, n_exp, rows, d, I):
     assert rel_err(host(y), ref) <= tol_of(cfg)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_grouped_ffn_multi_row_block_experts(moe, orc, dtype):
+    """Experts of one, two and three 256-row blocks (and an empty one) in one
+    launch: row blocks of one expert share its weight block, and bf16 tiles of
+    single-block experts run the reduction loop with streamed weight loads, the
+    others the one with cached loads."""
+    rng = np.random.default_rng(11)
+    sizes = [700, 0, 130, 257, 40]
+    off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    rows = int(off[-1])
+    cfg = small_cfg(dtype, rows, d=256, Nr=len(sizes), G=1, Mg=1, K=1, I=256)
+    x = syn.hidden(cfg)
+    wg, wu, wd = syn.expert_weights(cfg)
+    gather = rng.permutation(rows).astype(np.int32)
+    shape = shape_of(cfg)
+    y = empty((rows, cfg.d), torch.bfloat16)
+    ws = empty(moe.moe_ffn_workspace_bytes(shape, rows), torch.uint8)
+    print("grouped_ffn multi-row-block", dtype, sizes, flush=True)
+    if dtype == "fp8":
+        (qg, sg), (qu, su), (qd, sd) = (orc.quant_128x128(w) for w in (wg, wu, wd))
+        xq, xsr = orc.quant_1x128(x)
+        moe.moe_grouped_ffn(shape, len(sizes), dev(off), rows, dev(gather), dev(xq), dev(xsr), dev(qg), dev(qu),
+                            dev(qd), (dev(sg), dev(su), dev(sd)), y, ws)
+        ref = orc.grouped_ffn(off, xq[gather], qg, qu, qd, rows=np.arange(rows), x_scales=xsr[gather],
+                              w_scales=(sg, su, sd))
+    else:
+        moe.moe_grouped_ffn(shape, len(sizes), dev(off), rows, dev(gather), dev(x), None, dev(wg), dev(wu),
+                            dev(wd), None, y, ws)
+        ref = orc.grouped_ffn(off, x[gather], wg, wu, wd, rows=np.arange(rows))
+    got = host(y)
+    assert rel_err(got, ref) <= tol_of(cfg)
+    for e in range(len(sizes)):                                # every expert, not just the largest values
+        if sizes[e]:
+            sl = slice(off[e], off[e + 1])
+            assert rel_err(got[sl], ref[sl]) <= tol_of(cfg), e
+
+
 def test_grouped_ffn_integer_inputs_bitexact(moe, orc):
     """Integer-valued operands keep every fp32 partial sum exact, so the result
     is independent of summation order and tiling (gate pre-activations >= 24
