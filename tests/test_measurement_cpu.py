@@ -117,3 +117,14 @@ def test_algorithmic_work_of_the_expert_kernels():
     assert b_dn == 257 * cfg.I * cfg.d * 2 + rows * cfg.I * 2 + rows * cfg.d * 2
     # the layer's flops per token: (K + N_s) SwiGLU experts plus the gate GEMM
     assert cfg.flops_per_token == (cfg.K + cfg.Ns) * 6 * cfg.d * cfg.I + 2 * cfg.d * cfg.Nr
+
+
+@pytest.mark.parametrize("argv,env", [(["--gpus", "2"], {}), (["--gpus", "8"], {}), ([], {"WORLD_SIZE": "2"})])
+def test_bench_runs_on_one_gpu_only(argv, env):
+    """More than one GPU is refused with a message before any GPU work."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")] + argv, capture_output=True, text=True,
+                       timeout=120, env=dict(os.environ, **env), cwd=ROOT)
+    assert r.returncode == 2, r.stderr
+    assert "single GPU" in r.stderr and r.stdout == ""
