@@ -314,15 +314,26 @@ __global__ __launch_bounds__(RG_NT) void router_partial_kernel(const char *__res
                 for (int j = 0; j < Tl::TBW; ++j) acc[i][j] = Tr::mma(a[i], b[j], acc[i][j]);
         }
     }
-    // a lane holds experts (we*EBW + i)*16 + 4*(lane>>4) + {0..3} of token (wt*TBW + j)*16 + (lane&15)
-    float *pc = part + (int64_t)chunk * T * RP_E;
+    // a lane holds experts (we*EBW + i)*16 + 4*(lane>>4) + {0..3} of token (wt*TBW + j)*16 + (lane&15).
+    // The tile goes through LDS (rows padded by 16 bytes, so the 16 tokens of a write land in
+    // distinct bank groups) and leaves as whole 1 KB token rows, one 16-byte chunk per lane:
+    // stored straight from the accumulators, each instruction wrote 64-byte pieces of 16 rows.
+    constexpr int PITCH = RP_E * 4 + 16;
+    static_assert(RT * PITCH <= RP_LDS, "the staged partial tile fits the ring");
+    __syncthreads();   // every wave is done with the ring (no load is in flight after the last step)
 #pragma unroll
     for (int j = 0; j < Tl::TBW; ++j) {
-        const int64_t t = t0 + (wt * Tl::TBW + j) * 16 + (lane & 15);
-        if (t >= T) continue;
+        const int tl = (wt * Tl::TBW + j) * 16 + (lane & 15);
 #pragma unroll
         for (int i = 0; i < Tl::EBW; ++i)
-            *(f32x4 *)(pc + t * RP_E + (we * Tl::EBW + i) * 16 + 4 * (lane >> 4)) = acc[i][j];
+            *(f32x4 *)(ring + tl * PITCH + ((we * Tl::EBW + i) * 16 + 4 * (lane >> 4)) * 4) = acc[i][j];
+    }
+    __syncthreads();
+    float *pc = part + (int64_t)chunk * T * RP_E;
+    for (int r = wid; r < RT; r += RG_NT / 64) {
+        const int64_t t = t0 + r;
+        if (t >= T) break;
+        *(f32x4 *)(pc + t * RP_E + 4 * lane) = *(const f32x4 *)(ring + r * PITCH + 16 * lane);
     }
 }
 
