@@ -720,17 +720,29 @@ __global__ __launch_bounds__(wgb_nt<PW>()) void wgrad_bf16_kernel(const WgradArg
         pq0 = q0;
         pn = 0;
     };
-    auto store_one = [&](int n) {
-        const int j = n >> 1, i = (n & 1) * 2;
-        const int prow = prow0 + wp * 64 + j * 16 + (lane & 15);
-        uint16_t *orow = out + ((int64_t)e * split_rows + prow) * Qdim;
-        const int f = pair_bf16_col(pq0 + wq * 64 + i * 16, lane);
-        if (f < Qdim) *(u32x4 *)(orow + f) = pv[n];
+    // pv[2j] and pv[2j+1] hold the wave's 64 columns of row block j for the lane's row; the
+    // lanes of rows r and r ^ 8 swap halves so that each of the two 16-byte stores writes
+    // 128 contiguous bytes of 8 rows (64 bytes of 16 rows before)
+    auto store_pair = [&](int j) {
+        const bool hi = (lane >> 3) & 1;
+        const u32x4 send = hi ? pv[2 * j] : pv[2 * j + 1];
+        u32x4 recv;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) recv[k] = (uint32_t)__shfl_xor((int)send[k], 8, 64);
+        const u32x4 va = hi ? recv : pv[2 * j], vb = hi ? pv[2 * j + 1] : recv;
+        const int rbase = prow0 + wp * 64 + j * 16 + (lane & 7);
+        uint16_t *ra = out + ((int64_t)e * split_rows + rbase) * Qdim;
+        uint16_t *rb = ra + 8 * (int64_t)Qdim;
+        const int f = pair_bf16_col(pq0 + wq * 64 + (hi ? 32 : 0), lane);
+        if (f < Qdim) {
+            *(u32x4 *)(ra + f) = va;
+            *(u32x4 *)(rb + f) = vb;
+        }
     };
     auto store_some = [&](int upto) {
 #pragma unroll
-        for (int n = 0; n < 8; ++n)
-            if (n >= pn && n < upto) store_one(n);
+        for (int j = 0; j < 4; ++j)
+            if (2 * j >= pn && 2 * j < upto) store_pair(j);
         pn = upto > pn ? upto : pn;
     };
     int qt = 0, st = 0, slot = 0, sbn = 0;
