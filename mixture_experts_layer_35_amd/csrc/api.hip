@@ -753,12 +753,11 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
     };
     HIPCHK(mark(0));
     // 1. combine: dY rows and gate gradients
-    HIPCHK(launch_bwd_combine(dt, dout, Fw + F.yperm, inv, tw, T, d, s->topk, dy, dg, st));
-    if (fp8) {
-        // Dgrad inputs in 1 x 128 tiles along their reduction (d)
-        HIPCHK(launch_quant_rows(dt, dy, nullptr, TK, d, U8(L.dyq), F32(L.dys), st));
-        if (Ns) HIPCHK(launch_quant_rows(dt, dout, nullptr, T, d, U8(L.doq), F32(L.dos), st));
-    }
+    // e4m3 layers: the Dgrad inputs dY and dO also in 1 x 128 tiles along their reduction
+    // (d), written by the same kernel from the bf16 values it stores
+    HIPCHK(launch_bwd_combine(dt, dout, Fw + F.yperm, inv, tw, T, d, s->topk, dy, dg, fp8 ? U8(L.dyq) : nullptr,
+                              fp8 ? F32(L.dys) : nullptr, fp8 && Ns ? U8(L.doq) : nullptr,
+                              fp8 && Ns ? F32(L.dos) : nullptr, st));
     HIPCHK(mark(1));
     // 2. dH = dY . W_down (transposed copies [n][I][d])
     FfnProblem p[2] = {}, q[2] = {};

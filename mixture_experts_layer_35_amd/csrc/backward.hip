@@ -78,13 +78,36 @@ __global__ __launch_bounds__(256) void transpose_kernel(const char *__restrict__
     for (int k = 0; k < 16; ++k) d[(size_t)(c0 + ty + 4 * k) * dst_ld + col0 + r0 + tx] = tile[tx][ty + 4 * k];
 }
 
+// 1 x 128 tile of eight stored values per lane (16 lanes of one tile): the scale and
+// the four-byte code pairs, the arithmetic of quant_rows_kernel on the same values
+__device__ __forceinline__ void quant8_tile(const float v[8], uint8_t *q, float *sc, int sub) {
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+#pragma unroll
+    for (int m = 8; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 16));
+    const float scale = quant_scale(amax);
+    *(u32x2 *)q = u32x2{pack_e4m3x4(clamp448(v[0] / scale), clamp448(v[1] / scale), clamp448(v[2] / scale),
+                                    clamp448(v[3] / scale)),
+                        pack_e4m3x4(clamp448(v[4] / scale), clamp448(v[5] / scale), clamp448(v[6] / scale),
+                                    clamp448(v[7] / scale))};
+    if (sub == 0) *sc = scale;
+}
+
 // ---- combine backward: one workgroup per token ----
 // dY[inv(t,j)] = g_{t,j} dO_t (rounded to the act dtype); dg_{t,j} = dO_t . y[inv(t,j)]
-template <int DT, int KMAX>
+// With QUANT (bf16, for e4m3 layers) the kernel also writes the 1 x 128 tiles of dY
+// (dyq, dys) and, when doq is set, of dO: the codes quant_rows_kernel would make from
+// the stored bf16 values, without reading them back.
+template <int DT, int KMAX, bool QUANT>
 __global__ __launch_bounds__(BW_NT) void bwd_combine_kernel(const void *__restrict__ dout, const void *__restrict__ y,
                                                             const int32_t *__restrict__ inv,
                                                             const float *__restrict__ topk_w, int64_t T, int d, int K,
-                                                            void *__restrict__ dy, float *__restrict__ dg) {
+                                                            void *__restrict__ dy, float *__restrict__ dg,
+                                                            uint8_t *__restrict__ dyq, float *__restrict__ dys,
+                                                            uint8_t *__restrict__ doq, float *__restrict__ dos) {
+    static_assert(!QUANT || DT == DT_BF16, "the fused quantisation reads bf16 values");
+    static_assert(BW_NT % 16 == 0, "a 1 x 128 tile is 16 consecutive threads");
     __shared__ float red[BW_NT / 64][KMAX];
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
@@ -94,6 +117,8 @@ __global__ __launch_bounds__(BW_NT) void bwd_combine_kernel(const void *__restri
         for (int c = threadIdx.x * 8; c < d; c += BW_NT * 8) {
             float o[8];
             ld8v<DT>(dout, t * d + c, o);
+            const int sub = threadIdx.x & 15, ntile = d >> 7;
+            if (QUANT && doq) quant8_tile(o, doq + t * d + c, dos + t * ntile + (c >> 7), sub);
 #pragma unroll
             for (int j = 0; j < KMAX; ++j) {
                 if (j >= K) break;
@@ -107,6 +132,16 @@ __global__ __launch_bounds__(BW_NT) void bwd_combine_kernel(const void *__restri
                     w[q] = g * o[q];
                 }
                 st8v<DT>(dy, row * d + c, w);
+                if (QUANT) {
+                    float wb[8];   // the stored bf16 values
+#pragma unroll
+                    for (int q = 0; q < 8; q += 2) {
+                        const uint32_t pk = pack_bf16x2(w[q], w[q + 1]);
+                        wb[q] = __uint_as_float(pk << 16);
+                        wb[q + 1] = __uint_as_float(pk & 0xFFFF0000u);
+                    }
+                    quant8_tile(wb, dyq + row * d + c, dys + row * ntile + (c >> 7), sub);
+                }
             }
         }
 #pragma unroll
@@ -1153,12 +1188,16 @@ hipError_t launch_quant_cols(int in_dt, const void *src, const float *src_s, con
 }
 
 hipError_t launch_bwd_combine(int dt, const void *dout, const void *y, const int32_t *inv, const float *topk_w, int64_t T,
-                              int d, int K, void *dy, float *dg, hipStream_t s) {
+                              int d, int K, void *dy, float *dg, uint8_t *dyq, float *dys, uint8_t *doq, float *dos,
+                              hipStream_t s) {
     if (T <= 0) return hipSuccess;
+    if (dyq && (dt != DT_BF16 || d % 128)) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)(T < (1 << 20) ? T : (1 << 20));
-#define BC(DT, KM) bwd_combine_kernel<DT, KM><<<grid, BW_NT, 0, s>>>(dout, y, inv, topk_w, T, d, K, dy, dg)
-    if (dt == DT_F32) { if (K <= 8) BC(DT_F32, 8); else BC(DT_F32, 32); }
-    else { if (K <= 8) BC(DT_BF16, 8); else BC(DT_BF16, 32); }
+#define BC(DT, KM, Q)                                                                                                \
+    bwd_combine_kernel<DT, KM, Q><<<grid, BW_NT, 0, s>>>(dout, y, inv, topk_w, T, d, K, dy, dg, dyq, dys, doq, dos)
+    if (dt == DT_F32) { if (K <= 8) BC(DT_F32, 8, false); else BC(DT_F32, 32, false); }
+    else if (dyq) { if (K <= 8) BC(DT_BF16, 8, true); else BC(DT_BF16, 32, true); }
+    else { if (K <= 8) BC(DT_BF16, 8, false); else BC(DT_BF16, 32, false); }
 #undef BC
     return hipGetLastError();
 }

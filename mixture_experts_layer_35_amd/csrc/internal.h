@@ -133,7 +133,8 @@ hipError_t launch_quant_cols(int in_dt, const void *src, const float *src_s, con
                              const int32_t *offsets, const int32_t *bbase, int64_t seg_rows, int n_seg, int64_t max_blocks,
                              int cols, uint8_t *q, float *sc, hipStream_t s);
 hipError_t launch_bwd_combine(int dt, const void *dout, const void *y, const int32_t *inv, const float *topk_w, int64_t T,
-                              int d, int K, void *dy, float *dg, hipStream_t s);
+                              int d, int K, void *dy, float *dg, uint8_t *dyq, float *dys, uint8_t *doq, float *dos,
+                              hipStream_t s);
 hipError_t launch_bwd_token(int dt, const void *dxr, const void *dxs, int Ns, const int32_t *inv, const int32_t *idx,
                             const float *scores, const float *dg, const void *gate_w, int64_t T, int d, int Nr, int K,
                             float rs, void *du, float *dz_row, hipStream_t s);
