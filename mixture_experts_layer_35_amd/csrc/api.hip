@@ -817,13 +817,14 @@ static int backward_impl(const moe_shape *s, const void *u, const void *gate_w, 
     }
     if (s->flags & MOE_SAVE_SWIGLU_INPUTS) {
         // the forward kept a | b for the routed rows and then the shared rows, as dh and dab lie
+        // (e4m3 layers: with the 1 x 128 tiles of [dA dB], the Dgrad input of dX)
         HIPCHK(launch_swiglu_grad(wdt == DT_F32 ? DT_F32 : DT_BF16, dh, (const float *)(Fw + F.ab), dab,
-                                  TK + T * Ns, I, st));
+                                  TK + T * Ns, I, fp8 ? U8(L.abq) : nullptr, fp8 ? F32(L.abs_) : nullptr, st));
     } else {
         for (int i = 0; i < fa.nprob; ++i) fa.p[i] = q[fa.nprob - 1 - i];
         HIPCHK(launch_ffn(wdt, FFN_GATEUP_BWD, fa, st));
+        if (fp8) HIPCHK(launch_quant_rows(dt, dab, nullptr, TK + T * Ns, 2 * I, U8(L.abq), F32(L.abs_), st));
     }
-    if (fp8) HIPCHK(launch_quant_rows(dt, dab, nullptr, TK + T * Ns, 2 * I, U8(L.abq), F32(L.abs_), st));
     HIPCHK(mark(3));
     // 4. dX = [dA | dB] . [W_gate ; W_up] (transposed copies [n][d][2I])
     FfnProblem r[2] = {};

@@ -871,11 +871,17 @@ __global__ __launch_bounds__(NT, 1) void ffn_kernel(const FfnArgs a, int ring_by
 }
 
 // SwiGLU gradient from the forward's saved fp32 (a, b): one thread per four
-// consecutive features of a row, the epilogue's arithmetic (swiglu_grad).
-template <int DT>
+// consecutive features of a row, the epilogue's arithmetic (swiglu_grad).  With QUANT
+// (bf16 storage, e4m3 layers) the thread also writes the 1 x 128 tiles of the bf16
+// values it stores (q, qs: codes and scales of [dA dB] rows, 32 threads per tile, the
+// quantiser's arithmetic), so they need not be read back.
+template <int DT, bool QUANT>
 __global__ __launch_bounds__(256) void swiglu_grad_kernel(const void *__restrict__ dh, const float *__restrict__ ab,
-                                                          void *__restrict__ dab, int64_t quads, int F) {
+                                                          void *__restrict__ dab, int64_t quads, int F,
+                                                          uint8_t *__restrict__ q8, float *__restrict__ qs) {
+    static_assert(!QUANT || DT == DT_BF16, "the fused quantisation reads bf16 values");
     const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    // F % 128 == 0 with QUANT, so a 32-thread tile lies in one row and is wholly in range or out
     if (q >= quads) return;
     const int fq = F / 4;
     const int64_t r = q / fq;
@@ -900,8 +906,27 @@ __global__ __launch_bounds__(256) void swiglu_grad_kernel(const void *__restrict
         *(f32x4 *)((float *)dab + r * 2 * F + f) = f32x4{da[0], da[1], da[2], da[3]};
         *(f32x4 *)((float *)dab + r * 2 * F + F + f) = f32x4{db[0], db[1], db[2], db[3]};
     } else {
-        *(u32x2 *)((uint16_t *)dab + r * 2 * F + f) = u32x2{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
-        *(u32x2 *)((uint16_t *)dab + r * 2 * F + F + f) = u32x2{pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3])};
+        const u32x2 pa = u32x2{pack_bf16x2(da[0], da[1]), pack_bf16x2(da[2], da[3])};
+        const u32x2 pb = u32x2{pack_bf16x2(db[0], db[1]), pack_bf16x2(db[2], db[3])};
+        *(u32x2 *)((uint16_t *)dab + r * 2 * F + f) = pa;
+        *(u32x2 *)((uint16_t *)dab + r * 2 * F + F + f) = pb;
+        if (QUANT) {
+            const int sub = threadIdx.x & 31, ntile = 2 * F / 128;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x2 p = h ? pb : pa;
+                const float v[4] = {__uint_as_float(p[0] << 16), __uint_as_float(p[0] & 0xFFFF0000u),
+                                    __uint_as_float(p[1] << 16), __uint_as_float(p[1] & 0xFFFF0000u)};
+                float amax = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+#pragma unroll
+                for (int m = 16; m >= 1; m >>= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 32));
+                const float scale = quant_scale(amax);
+                const int64_t col = (int64_t)h * F + f;
+                *(uint32_t *)(q8 + r * 2 * F + col) = pack_e4m3x4(clamp448(v[0] / scale), clamp448(v[1] / scale),
+                                                                  clamp448(v[2] / scale), clamp448(v[3] / scale));
+                if (sub == 0) qs[r * ntile + col / 128] = scale;
+            }
+        }
     }
 }
 
@@ -954,12 +979,15 @@ hipError_t launch_ffn(int dt, int mode, const FfnArgs &a, hipStream_t s) {
     return gateup ? run<DT_E4M3, FFN_GATEUP>(a, s) : run<DT_E4M3, FFN_DOWN>(a, s);
 }
 
-hipError_t launch_swiglu_grad(int dt, const void *dh, const float *ab, void *dab, int64_t rows, int F, hipStream_t s) {
+hipError_t launch_swiglu_grad(int dt, const void *dh, const float *ab, void *dab, int64_t rows, int F, uint8_t *q8,
+                              float *qs, hipStream_t s) {
     const int64_t quads = rows * (F / 4);
     if (quads <= 0) return hipSuccess;
+    if (q8 && (dt != DT_BF16 || F % 128)) return hipErrorInvalidValue;
     const unsigned grid = (unsigned)((quads + 255) / 256);
-    if (dt == DT_F32) swiglu_grad_kernel<DT_F32><<<grid, 256, 0, s>>>(dh, ab, dab, quads, F);
-    else swiglu_grad_kernel<DT_BF16><<<grid, 256, 0, s>>>(dh, ab, dab, quads, F);
+    if (dt == DT_F32) swiglu_grad_kernel<DT_F32, false><<<grid, 256, 0, s>>>(dh, ab, dab, quads, F, nullptr, nullptr);
+    else if (q8) swiglu_grad_kernel<DT_BF16, true><<<grid, 256, 0, s>>>(dh, ab, dab, quads, F, q8, qs);
+    else swiglu_grad_kernel<DT_BF16, false><<<grid, 256, 0, s>>>(dh, ab, dab, quads, F, nullptr, nullptr);
     return hipGetLastError();
 }
 

@@ -89,7 +89,8 @@ hipError_t launch_ffn(int dt, int mode, const FfnArgs &a, hipStream_t s);
 // SwiGLU gradient from saved inputs: for rows x F features, dab[r][f] = da and
 // dab[r][F + f] = db from dh [rows][F] and ab [rows][2F] (fp32); dh and dab are fp32
 // for dt = DT_F32 and bf16 otherwise, as in the FFN_GATEUP_BWD epilogue.
-hipError_t launch_swiglu_grad(int dt, const void *dh, const float *ab, void *dab, int64_t rows, int F, hipStream_t s);
+hipError_t launch_swiglu_grad(int dt, const void *dh, const float *ab, void *dab, int64_t rows, int F, uint8_t *q8,
+                              float *qs, hipStream_t s);
 
 // ---- backward ----------------------------------------------------------------
 // Weight-gradient problem: for each expert e with rows r (offsets, or rows_fixed
